@@ -1,0 +1,7 @@
+"""fp64 CPU oracle of the Sol-Attn sparse attention forward.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path. It shares no code
+with the HIP implementation.
+"""
+from .oracle import attend, attend_head, block_bounds, block_means, proxy_scores, route, route_head  # noqa: F401

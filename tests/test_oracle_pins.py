@@ -1,0 +1,258 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each test names the passage of the page "Sol-Attn: Accelerating Video
+Generation Inference via On-the-Fly Attention Sparsification" (paperlayer.ai
+summary) or the mathematical fact it relies on. Together they are chosen so
+that a dropped term, a wrong sign, a wrong block index, a transposed operand,
+a sum taken for a mean or a missing token count fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attend, attend_head, block_means, route
+from oracle.brute import brute_head
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def sdpa64(q, k, v):
+    """Dense softmax attention from torch's library routine, fp64 on the CPU."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0, 0].numpy()
+
+
+def rand(rng, *shape, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------------------
+# Hand-derived worked examples (closed forms in e)
+# ---------------------------------------------------------------------------
+
+def _closed(expr):
+    return eval(expr, {"__builtins__": {}}, {"e": math.e})  # noqa: S307 - fixed fixture strings
+
+
+@pytest.mark.parametrize("ex", json.load(open(GOLDEN))["examples"], ids=lambda ex: ex["name"])
+def test_worked_examples(ex):
+    N, d = ex["N"], ex["d"]
+    tau = math.inf if ex["tau"] == "inf" else float(ex["tau"])
+    q = np.array(ex["q"], dtype=np.float64).reshape(N, d)
+    k = np.array(ex["k"], dtype=np.float64).reshape(N, d)
+    v = np.array(ex["v"], dtype=np.float64).reshape(N, d)
+    r = attend_head(q, k, v, ex["Bq"], ex["Bk"], tau)
+    assert r["keep"].tolist() == ex["keep"]
+    np.testing.assert_allclose(r["s"].ravel(), [_closed(x) for x in ex["s"]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r["out"].ravel(), [_closed(x) for x in ex["out"]], rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# tau = +inf is dense softmax attention (§2 "Attention and Online Softmax";
+# §3 "Approximate correction": selected blocks are computed exactly)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,d,Bq,Bk", [(1000, 16, 64, 64), (200, 8, 32, 48), (130, 4, 7, 13), (64, 32, 64, 64)])
+def test_dense_limit_equals_sdpa(N, d, Bq, Bk):
+    rng = np.random.default_rng(N * 7 + d)
+    q, k, v = rand(rng, N, d, scale=2.0), rand(rng, N, d, scale=2.0), rand(rng, N, d)
+    r = attend_head(q, k, v, Bq, Bk, math.inf)
+    assert r["keep"].all()
+    np.testing.assert_allclose(r["out"], sdpa64(q, k, v), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Brute force on tiny grids: proxies, keep mask and outputs term by term
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,d,Bq,Bk", [(5, 3, 2, 2), (16, 4, 4, 4), (37, 3, 8, 5), (40, 8, 16, 8), (23, 2, 23, 4)])
+@pytest.mark.parametrize("tau", [0.0, 0.3, 1.0, 3.0, math.inf])
+def test_brute_force_tiny(N, d, Bq, Bk, tau):
+    rng = np.random.default_rng(1000 * N + 10 * d + Bq)
+    q, k, v = rand(rng, N, d, scale=1.5), rand(rng, N, d, scale=1.5), rand(rng, N, d)
+    r = attend_head(q, k, v, Bq, Bk, tau)
+    out_b, s_b, keep_b = brute_head(q.tolist(), k.tolist(), v.tolist(), Bq, Bk, tau)
+    np.testing.assert_allclose(r["s"], np.array(s_b), rtol=0, atol=1e-12)
+    assert (r["keep"] == np.array(keep_b)).all()
+    np.testing.assert_allclose(r["out"], np.array(out_b), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Constant blocks: the zeroth-order correction is exact (§3 "Approximate
+# correction"; App. B "Approximation error": the error vanishes when the
+# centred score deviations inside a block are zero)
+# ---------------------------------------------------------------------------
+
+def _block_constant(rng, N, d, bsz, scale):
+    x = np.empty((N, d))
+    for s in range(0, N, bsz):
+        x[s:s + bsz] = rng.standard_normal(d) * scale
+    return x
+
+
+@pytest.mark.parametrize("N,Bq,Bk", [(1000, 64, 64), (1000, 48, 64), (777, 64, 100), (129, 64, 64)])
+@pytest.mark.parametrize("v_kind", ["arbitrary", "block_constant"])
+def test_tau0_constant_blocks_equals_dense(N, Bq, Bk, v_kind):
+    d = 16
+    rng = np.random.default_rng(N + Bq + Bk)
+    q = _block_constant(rng, N, d, Bq, 1.5)
+    k = _block_constant(rng, N, d, Bk, 1.5)
+    v = rand(rng, N, d) if v_kind == "arbitrary" else _block_constant(rng, N, d, Bk, 1.0)
+    r = attend_head(q, k, v, Bq, Bk, 0.0)
+    assert (~r["keep"]).sum() > 0  # the correction path is exercised
+    np.testing.assert_allclose(r["out"], sdpa64(q, k, v), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Routing invariants (§3 "Dynamic threshold routing", row-max form)
+# ---------------------------------------------------------------------------
+
+def test_routing_monotone_in_tau_and_argmax_kept():
+    rng = np.random.default_rng(7)
+    N, d = 640, 16
+    q, k = rand(rng, N, d, scale=2.0), rand(rng, N, d, scale=2.0)
+    qbar, _ = block_means(q, 64)
+    kbar, _ = block_means(k, 64)
+    s = qbar @ kbar.T / math.sqrt(d)
+    prev = None
+    for tau in [0.0, 0.1, 0.5, 1.0, 2.0, 4.0, math.inf]:
+        M, keep = route(s, tau)
+        assert keep[np.arange(len(M)), s.argmax(axis=1)].all()
+        assert keep.sum(axis=1).min() >= 1
+        if prev is not None:
+            assert (prev <= keep).all()
+        prev = keep
+    # with distinct scores, tau = 0 keeps exactly the argmax
+    M, keep = route(s, 0.0)
+    assert (keep.sum(axis=1) == 1).all()
+
+
+def test_route_rejects_negative_or_nan_tau():
+    s = np.zeros((2, 2))
+    for bad in (-1e-9, -1.0, float("nan")):
+        with pytest.raises(ValueError):
+            route(s, bad)
+
+
+def test_single_kv_block_is_dense():
+    rng = np.random.default_rng(11)
+    N, d = 50, 8
+    q, k, v = rand(rng, N, d, scale=3.0), rand(rng, N, d, scale=3.0), rand(rng, N, d)
+    r = attend_head(q, k, v, 16, 64, 0.0)
+    assert r["keep"].all()
+    np.testing.assert_allclose(r["out"], sdpa64(q, k, v), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Output algebra: the result is a convex combination of token values and
+# block mean values
+# ---------------------------------------------------------------------------
+
+def test_value_shift_invariance_and_convex_hull():
+    rng = np.random.default_rng(3)
+    N, d = 300, 8
+    q, k, v = rand(rng, N, d, scale=2.0), rand(rng, N, d, scale=2.0), rand(rng, N, d)
+    c = rng.standard_normal(d)
+    for tau in (0.0, 1.0, 3.0):
+        a = attend_head(q, k, v, 32, 32, tau)["out"]
+        b = attend_head(q, k, v + c, 32, 32, tau)["out"]
+        np.testing.assert_allclose(b, a + c, rtol=0, atol=1e-12)
+        assert (a <= v.max(axis=0) + 1e-12).all() and (a >= v.min(axis=0) - 1e-12).all()
+
+
+def test_kv_block_permutation_invariance():
+    rng = np.random.default_rng(5)
+    Bk, nb, d = 16, 9, 8
+    N = Bk * nb
+    q, k, v = rand(rng, N, d, scale=2.0), rand(rng, N, d, scale=2.0), rand(rng, N, d)
+    perm = rng.permutation(nb)
+    idx = np.concatenate([np.arange(j * Bk, (j + 1) * Bk) for j in perm])
+    for tau in (0.0, 0.7, 2.0):
+        a = attend_head(q, k, v, 24, Bk, tau)
+        b = attend_head(q, k[idx], v[idx], 24, Bk, tau)
+        np.testing.assert_allclose(b["out"], a["out"], rtol=0, atol=1e-12)
+        assert (b["keep"] == a["keep"][:, perm]).all()
+
+
+def test_token_permutation_inside_block_invariance():
+    """Inside a block only the block's mean and its tokens as a set matter."""
+    rng = np.random.default_rng(9)
+    N, d, Bk = 160, 8, 32
+    q, k, v = rand(rng, N, d, scale=2.0), rand(rng, N, d, scale=2.0), rand(rng, N, d)
+    idx = np.concatenate([s + rng.permutation(min(Bk, N - s)) for s in range(0, N, Bk)])
+    a = attend_head(q, k, v, 32, Bk, 1.0)["out"]
+    b = attend_head(q, k[idx], v[idx], 32, Bk, 1.0)["out"]
+    np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# App. B "Approximation error": for a skipped block, the denominator error is
+# second order in the centred score spread; the numerator error is first order
+# with a coefficient set by the alignment of the deviations with the values.
+# ---------------------------------------------------------------------------
+
+def _scaling_case(eps, aligned):
+    rng = np.random.default_rng(21)
+    d, Bk = 8, 32
+    qv = rng.standard_normal(d)
+    q = np.tile(qv, (Bk, 1))                            # one query block, constant rows
+    k0 = np.tile(qv * 0.8, (Bk, 1))                     # block 0: strongly aligned, kept
+    kbar1 = -0.1 * qv + 0.05 * rng.standard_normal(d)   # block 1: far below, skipped
+    delta = rng.standard_normal((Bk, d))
+    delta -= delta.mean(axis=0)                         # zero-mean deviations
+    k1 = kbar1 + eps * delta
+    k = np.concatenate([k0, k1])
+    v0 = rng.standard_normal((Bk, d))
+    if aligned:
+        a = delta @ qv / math.sqrt(d)                   # centred score deviations
+        v1 = 0.3 + np.outer(a, np.ones(d))
+    else:
+        v1 = np.full((Bk, d), 0.3)
+    v = np.concatenate([v0, v1])
+    qq = np.concatenate([q, q])
+    r = attend_head(qq, k, v, Bk, Bk, 1.0)
+    assert r["keep"].tolist() == [[True, False], [True, False]]
+    return np.abs(r["out"] - sdpa64(qq, k, v)).max()
+
+
+@pytest.mark.parametrize("aligned,ratio", [(False, 4.0), (True, 2.0)])
+def test_error_order_in_score_spread(aligned, ratio):
+    e1 = _scaling_case(2e-2, aligned)
+    e2 = _scaling_case(1e-2, aligned)
+    assert e1 > 0 and e2 > 0
+    assert abs(e1 / e2 - ratio) < 0.15 * ratio, (e1, e2, e1 / e2)
+
+
+# ---------------------------------------------------------------------------
+# Oracle plumbing: sub-selection and override agree with the full computation
+# ---------------------------------------------------------------------------
+
+def test_query_block_subset_and_override_consistent():
+    rng = np.random.default_rng(13)
+    N, d = 700, 16
+    q, k, v = rand(rng, N, d, scale=2.0), rand(rng, N, d, scale=2.0), rand(rng, N, d)
+    full = attend_head(q, k, v, 64, 64, 2.0)
+    sub = attend_head(q, k, v, 64, 64, 2.0, query_blocks=[0, 5, 10])
+    for i in (0, 5, 10):
+        r0, r1 = i * 64, min(N, i * 64 + 64)
+        np.testing.assert_array_equal(sub["out"][r0:r1], full["out"][r0:r1])
+        np.testing.assert_array_equal(sub["keep"][i], full["keep"][i])
+    assert np.isnan(sub["out"][64:128]).all()
+    over = attend_head(q, k, v, 64, 64, 0.0, keep_override=full["keep"])
+    np.testing.assert_allclose(over["out"], full["out"], rtol=0, atol=1e-13)
+
+
+def test_batched_attend_matches_per_head():
+    rng = np.random.default_rng(17)
+    B, H, N, d = 2, 3, 150, 8
+    q, k, v = (rand(rng, B, H, N, d, scale=2.0) for _ in range(3))
+    r = attend(q, k, v, 32, 32, 1.5)
+    for b in range(B):
+        for h in range(H):
+            one = attend_head(q[b, h], k[b, h], v[b, h], 32, 32, 1.5)
+            np.testing.assert_array_equal(r["out"][b, h], one["out"])
+            np.testing.assert_array_equal(r["keep"][b, h], one["keep"])
