@@ -1,0 +1,32 @@
+"""Sol-Attn sparse attention forward for AMD Instinct MI355X (gfx950).
+
+The work is done by libsolattn.so (HIP kernels behind the C ABI in
+include/sol_attn.h); this package only loads it and marshals torch tensors.
+Importing the package does not load the library; the first call does, and it
+raises if the library has not been built.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    SOL_ATTN_MAX_N,
+    SOL_EHIP,
+    SOL_EINVAL,
+    SOL_EUNSUPPORTED,
+    SOL_EWORKSPACE,
+    SOL_F_EXACT_ONLY,
+    SOL_F_POOLED,
+    SOL_OK,
+    SolAttnError,
+    lib,
+    strerror,
+)
+from .api import (  # noqa: F401
+    SolAttention,
+    bitmap_shape,
+    forward,
+    pool,
+    pooled_shape,
+    read_stats,
+    unpack_bitmap,
+    workspace_bytes,
+)

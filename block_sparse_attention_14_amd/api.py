@@ -1,0 +1,172 @@
+"""Python binding of the Sol-Attn C ABI.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their device pointers and torch's current HIP stream go to
+libsolattn.so, whose kernels do all of the work. torch provides the device
+memory and the stream; nothing here computes any part of the attention.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import SOL_F_EXACT_ONLY, SOL_F_POOLED, check, lib  # noqa: F401
+
+STATS_WORDS = 4  # sol_attn_stats is 32 bytes
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_qkv(name: str, t: torch.Tensor, shape=None) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_f32(name: str, t: torch.Tensor, shape, device) -> None:
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape) or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} on {device}")
+
+
+def workspace_bytes(B: int, H: int, N: int, d: int, Bq: int = 64, Bk: int = 64) -> int:
+    return int(lib().sol_attn_workspace_bytes(B, H, N, d, Bq, Bk))
+
+
+def pooled_shape(B: int, H: int, N: int, d: int, Bk: int = 64) -> Tuple[int, int, int, int]:
+    return (B, H, -(-N // Bk), d)
+
+
+def bitmap_shape(B: int, H: int, N: int, Bq: int = 64, Bk: int = 64) -> Tuple[int, int, int, int]:
+    return (B, H, -(-N // Bq), -(-(-(-N // Bk)) // 32))
+
+
+def new_stats(device) -> torch.Tensor:
+    return torch.zeros(STATS_WORDS, dtype=torch.int64, device=device)
+
+
+def read_stats(t: torch.Tensor) -> Dict[str, int]:
+    """Decode a stats tensor written by forward() (synchronises)."""
+    raw = t.detach().cpu().numpy().tobytes()
+    s = _lib.sol_attn_stats.from_buffer_copy(raw)
+    return {f: int(getattr(s, f)) for f, _ in _lib.sol_attn_stats._fields_}
+
+
+def pool(k: torch.Tensor, v: torch.Tensor, Bk: int = 64,
+         kpool: Optional[torch.Tensor] = None, vmean: Optional[torch.Tensor] = None):
+    """Per-block means of k and v (fp32, [B, H, ceil(N/Bk), d])."""
+    _check_qkv("k", k)
+    _check_qkv("v", v, k.shape)
+    B, H, N, d = k.shape
+    ps = pooled_shape(B, H, N, d, Bk)
+    kpool = torch.empty(ps, dtype=torch.float32, device=k.device) if kpool is None else kpool
+    vmean = torch.empty(ps, dtype=torch.float32, device=k.device) if vmean is None else vmean
+    _check_f32("kpool", kpool, ps, k.device)
+    _check_f32("vmean", vmean, ps, k.device)
+    rc = lib().sol_attn_pool(_ptr(k), _ptr(v), _ptr(kpool), _ptr(vmean), B, H, N, d, Bk, _stream(k.device))
+    check(rc, "sol_attn_pool")
+    return kpool, vmean
+
+
+class SolAttention:
+    """Reusable buffers (pooled k/v, workspace, stats) for one [B, H, N, d] shape.
+
+    Calling the object runs the pooling pre-pass and the fused forward on the
+    current stream and returns the fp32 output.
+    """
+
+    def __init__(self, B: int, H: int, N: int, d: int, device="cuda", Bq: int = 64, Bk: int = 64):
+        self.B, self.H, self.N, self.d, self.Bq, self.Bk = B, H, N, d, Bq, Bk
+        self.device = torch.device(device)
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        nbytes = workspace_bytes(B, H, N, d, Bq, Bk)
+        if nbytes == 0:
+            rc = _lib.SOL_EUNSUPPORTED if d > 0 and N > 0 and B > 0 and H > 0 else _lib.SOL_EINVAL
+            check(rc, "sol_attn_workspace_bytes")
+        ps = pooled_shape(B, H, N, d, Bk)
+        self.kpool = torch.empty(ps, dtype=torch.float32, device=self.device)
+        self.vmean = torch.empty(ps, dtype=torch.float32, device=self.device)
+        self.workspace = torch.zeros(-(-nbytes // 8), dtype=torch.int64, device=self.device)
+        self.stats = new_stats(self.device)
+
+    def __call__(self, q, k, v, tau: float, flags: int = 0, out: Optional[torch.Tensor] = None,
+                 stats: bool = True, bitmap: Optional[torch.Tensor] = None) -> torch.Tensor:
+        shape = (self.B, self.H, self.N, self.d)
+        _check_qkv("q", q, shape)
+        _check_qkv("k", k, shape)
+        _check_qkv("v", v, shape)
+        if q.device != self.device or k.device != self.device or v.device != self.device:
+            raise ValueError(f"q, k, v must be on {self.device}")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        _check_f32("out", out, shape, self.device)
+        args = (
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), self.B, self.H, self.N, self.d, self.Bq, self.Bk,
+            ctypes.c_float(float(tau)), ctypes.c_uint(flags), _ptr(self.stats) if stats else None,
+            _ptr(self.kpool), _ptr(self.vmean), _ptr(self.workspace), self.workspace.numel() * 8,
+            _stream(self.device),
+        )
+        if bitmap is None:
+            rc = lib().sol_attn_forward(*args)
+            check(rc, "sol_attn_forward")
+        else:
+            bs = bitmap_shape(self.B, self.H, self.N, self.Bq, self.Bk)
+            if bitmap.dtype != torch.int32 or tuple(bitmap.shape) != bs or not bitmap.is_contiguous() \
+                    or bitmap.device != self.device:
+                raise ValueError(f"bitmap must be a contiguous int32 tensor of shape {bs} on {self.device}")
+            rc = lib().sol_attn_forward_debug(*args, _ptr(bitmap))
+            check(rc, "sol_attn_forward_debug")
+        return out
+
+    def read_stats(self) -> Dict[str, int]:
+        return read_stats(self.stats)
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, Bq: int = 64, Bk: int = 64,
+            flags: int = 0, return_bitmap: bool = False, return_stats: bool = False):
+    """One-shot sparse attention forward (allocates its buffers).
+
+    Returns out (fp32), plus the kept-block bitmap [B, H, Nq, ceil(Nk/32)]
+    (int32 words) and/or the stats dict when asked.
+    """
+    _check_qkv("q", q)
+    B, H, N, d = q.shape
+    if math.isnan(tau) or tau < 0:
+        check(_lib.SOL_EINVAL, "sol_attn_forward")
+    runner = SolAttention(B, H, N, d, q.device, Bq, Bk)
+    bm = None
+    if return_bitmap:
+        bm = torch.zeros(bitmap_shape(B, H, N, Bq, Bk), dtype=torch.int32, device=q.device)
+    out = runner(q, k, v, tau, flags=flags, bitmap=bm)
+    res = [out]
+    if return_bitmap:
+        res.append(bm)
+    if return_stats:
+        res.append(runner.read_stats())
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def unpack_bitmap(words: torch.Tensor, Nk: int):
+    """[..., nwords] int32 words -> [..., Nk] bool numpy array (host)."""
+    import numpy as np
+
+    w = words.detach().cpu().numpy().view(np.uint32)
+    bits = (w[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1
+    return bits.reshape(*w.shape[:-1], -1)[..., :Nk].astype(bool)

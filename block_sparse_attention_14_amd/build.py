@@ -1,0 +1,76 @@
+"""Build libsolattn.so in-tree with hipcc for gfx950.
+
+    python -m block_sparse_attention_14_amd.build [-v]
+
+Every HIP source is compiled with packed-fp32 code generation disabled; the
+library links only the HIP runtime.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libsolattn.so")
+SOURCES = ["pool.hip", "fwd.hip", "api.hip"]
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; a ROCm toolchain is required to build libsolattn.so")
+    return path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object, link the shared library, return its path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="solattn_build_") as tmp:
+        objs = []
+        procs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+        failed = []
+        for src, cmd, pr in procs:
+            out, _ = pr.communicate()
+            lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+            if pr.returncode != 0:
+                failed.append((src, "\n".join(lines)))
+            elif verbose and lines:
+                print("\n".join(lines))
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n\n".join(f"[{s}]\n{o}" for s, o in failed))
+        tmp_lib = LIB + ".tmp"
+        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        if verbose:
+            print(" ".join(link), flush=True)
+        r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout)
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

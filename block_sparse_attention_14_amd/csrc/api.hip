@@ -1,0 +1,129 @@
+// C ABI entry points: argument validation (entirely on the host, before any
+// launch), then kernel launches on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "sol_attn.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return SOL_EINVAL;
+  if (d != 64 && d != 128) return SOL_EUNSUPPORTED;
+  if (Bq != 64 || Bk != 64) return SOL_EUNSUPPORTED;
+  if (N > SOL_ATTN_MAX_N) return SOL_EUNSUPPORTED;
+  const long long nq = (N + 63) / 64;
+  if ((long long)B * H * nq > (1ll << 30)) return SOL_EUNSUPPORTED;  // ticket space
+  return SOL_OK;
+}
+
+int check_forward(const void* q, const void* k, const void* v, const float* out, int B, int H, int N,
+                  int d, int Bq, int Bk, float tau, unsigned flags, const sol_attn_stats* stats,
+                  const float* kpool, const float* vmean, const void* ws, size_t ws_bytes) {
+  if (!q || !k || !v || !out || !kpool || !vmean || !ws) return SOL_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(kpool, 16) || !aligned(vmean, 16) || !aligned(ws, 8) || !aligned(stats, 8))
+    return SOL_EINVAL;
+  if (isnan(tau) || tau < 0.f) return SOL_EINVAL;
+  if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY)) return SOL_EINVAL;
+  const int rc = check_sizes(B, H, N, d, Bq, Bk);
+  if (rc != SOL_OK) return rc;
+  if (ws_bytes < sol_attn_workspace_bytes(B, H, N, d, Bq, Bk)) return SOL_EWORKSPACE;
+  return SOL_OK;
+}
+
+int forward_impl(const void* q, const void* k, const void* v, float* out, int B, int H, int N, int d,
+                 int Bq, int Bk, float tau, unsigned flags, sol_attn_stats* stats, float* kpool,
+                 float* vmean, void* ws, size_t ws_bytes, void* stream, uint32_t* bitmap) {
+  const int rc = check_forward(q, k, v, out, B, H, N, d, Bq, Bk, tau, flags, stats, kpool, vmean, ws, ws_bytes);
+  if (rc != SOL_OK) return rc;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  const int Nq = (N + Bq - 1) / Bq, Nk = (N + Bk - 1) / Bk;
+  unsigned* queue = static_cast<unsigned*>(ws);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+
+  hipError_t e;
+  if (flags & SOL_F_POOLED)
+    e = sol::launch_reset(queue, stats, s);
+  else
+    e = sol::launch_pool(k16, v16, kpool, vmean, BH, N, Nk, d, queue, stats, s);
+  if (e != hipSuccess) return SOL_EHIP;
+
+  sol::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = k16;
+  p.v = v16;
+  p.out = out;
+  p.kpool = kpool;
+  p.vmean = vmean;
+  p.queue = queue;
+  p.stats = stats;
+  p.bitmap = bitmap;
+  p.N = N;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.nitems = BH * Nq;
+  p.nwords = (Nk + 31) / 32;
+  p.tau = tau;
+  p.proxy_scale = (float)(1.0 / sqrt((double)d));
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+  p.exact_only = (flags & SOL_F_EXACT_ONLY) ? 1 : 0;
+  e = sol::launch_forward(p, d, s);
+  return e == hipSuccess ? SOL_OK : SOL_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk) {
+  if (check_sizes(B, H, N, d, Bq, Bk) != SOL_OK) return 0;
+  return 256;  // queue counter words, padded
+}
+
+int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean, int B, int H, int N, int d,
+                  int Bk, void* stream) {
+  if (!k || !v || !kpool || !vmean) return SOL_EINVAL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kpool, 16) || !aligned(vmean, 16)) return SOL_EINVAL;
+  const int rc = check_sizes(B, H, N, d, 64, Bk);
+  if (rc != SOL_OK) return rc;
+  const int Nk = (N + Bk - 1) / Bk;
+  const hipError_t e = sol::launch_pool(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                        kpool, vmean, B * H, N, Nk, d, nullptr, nullptr,
+                                        reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SOL_OK : SOL_EHIP;
+}
+
+int sol_attn_forward(const void* q, const void* k, const void* v, float* out, int B, int H, int N, int d,
+                     int Bq, int Bk, float tau, unsigned flags, sol_attn_stats* stats, float* kpool,
+                     float* vmean, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(q, k, v, out, B, H, N, d, Bq, Bk, tau, flags, stats, kpool, vmean, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+int sol_attn_forward_debug(const void* q, const void* k, const void* v, float* out, int B, int H, int N,
+                           int d, int Bq, int Bk, float tau, unsigned flags, sol_attn_stats* stats,
+                           float* kpool, float* vmean, void* workspace, size_t workspace_bytes,
+                           void* stream, uint32_t* kept_bitmap) {
+  if (!kept_bitmap || !aligned(kept_bitmap, 4)) return SOL_EINVAL;
+  return forward_impl(q, k, v, out, B, H, N, d, Bq, Bk, tau, flags, stats, kpool, vmean, workspace,
+                      workspace_bytes, stream, kept_bitmap);
+}
+
+const char* sol_attn_strerror(int code) {
+  switch (code) {
+    case SOL_OK: return "success";
+    case SOL_EINVAL: return "invalid argument (null/misaligned pointer, size <= 0, tau NaN or negative, unknown flag)";
+    case SOL_EUNSUPPORTED: return "unsupported configuration (d must be 64 or 128, Bq = Bk = 64, N <= SOL_ATTN_MAX_N)";
+    case SOL_EWORKSPACE: return "workspace smaller than sol_attn_workspace_bytes()";
+    case SOL_EHIP: return "HIP runtime error during launch";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

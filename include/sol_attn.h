@@ -1,0 +1,144 @@
+/*
+ * sol_attn.h - C ABI of the Sol-Attn sparse attention forward on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What is computed. Page "Sol-Attn: Accelerating Video Generation Inference
+ * via On-the-Fly Attention Sparsification" (paperlayer.ai summary of arXiv
+ * 2607.24027):
+ *   - §2 "Block-Sparse Attention": q and k are cut into blocks of Bq and Bk
+ *     consecutive tokens; each (query block i, key block j) pair gets a proxy
+ *     score from the block means,  s_ij = mean(q_i) . mean(k_j) / sqrt(d).
+ *   - §3 "Dynamic threshold routing" / "On-the-fly sparsification": a
+ *     query-dependent threshold selects blocks on chip, without a proxy map or
+ *     routing indices in device memory. Here the threshold is the row maximum
+ *     minus tau: block j is kept for query block i iff s_ij >= max_j' s_ij' - tau
+ *     (ties kept, so the best block is always kept; tau = +inf is dense).
+ *   - §3 "Approximate correction": kept blocks get exact attention; every
+ *     skipped block j adds exp(s_ij - m) * n_j * mean(v_j) to the softmax
+ *     numerator and exp(s_ij - m) * n_j to the denominator of every row of
+ *     query block i, n_j being the number of tokens in block j.
+ *   - §3 "Unified execution": exact and corrected terms share one
+ *     online-softmax state, so for row r of query block i
+ *       out_r = (sum_kept_t e^{x_rt} v_t + sum_skip_j n_j e^{s_ij} vbar_j)
+ *             / (sum_kept_t e^{x_rt}     + sum_skip_j n_j e^{s_ij}),
+ *     x_rt = q_r . k_t / sqrt(d) (stabilised by a common maximum).
+ *   - §2 "Attention and Online Softmax", App. B: forward only, bidirectional,
+ *     no masks; a ragged last block pools only its valid tokens.
+ *
+ * Layouts. q, k, v: bf16, contiguous [B][H][N][d], d fastest. out: fp32, same
+ * shape. kpool, vmean: fp32 [B][H][Nk][d] with Nk = ceil(N/Bk). Pointers are
+ * device pointers and must be 16-byte aligned.
+ *
+ * Ownership. The caller allocates and frees every buffer. The library never
+ * allocates device memory, never copies between host and device and never
+ * synchronises: each call validates its arguments on the host and enqueues
+ * kernels on `stream` (a hipStream_t; NULL = the default stream), then
+ * returns. Device-side faults surface at the caller's next synchronisation.
+ *
+ * Errors. Every entry point returns SOL_OK or a negative code, and validates
+ * all arguments before any launch; on an error nothing has been enqueued.
+ *
+ * Re-entrancy. Calls are stateless apart from the caller's workspace: two
+ * forwards that overlap in time (different streams) need separate workspaces.
+ */
+#ifndef SOL_ATTN_H
+#define SOL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+  SOL_OK = 0,
+  SOL_EINVAL = -1,       /* null or misaligned pointer, size <= 0, tau NaN or < 0, bad flag */
+  SOL_EUNSUPPORTED = -2, /* d not in {64, 128}, Bq != 64, Bk != 64, or N too large */
+  SOL_EWORKSPACE = -3,   /* workspace smaller than sol_attn_workspace_bytes() */
+  SOL_EHIP = -4          /* the HIP runtime refused a launch or a query */
+};
+
+/* Flags of sol_attn_forward. */
+enum {
+  /* kpool/vmean already hold sol_attn_pool() of these k and v: skip the pre-pass. */
+  SOL_F_POOLED = 1u << 0,
+  /* Ablation: drop skipped blocks instead of correcting them (keep-or-drop). */
+  SOL_F_EXACT_ONLY = 1u << 1
+};
+
+/* Largest supported sequence length (the per-query-block routing row of
+ * Nk = N/64 scores is held on chip). */
+#define SOL_ATTN_MAX_N (8192 * 64)
+
+/* Per-call counters, written by sol_attn_forward into DEVICE memory. All
+ * fields are reset at the start of every forward that receives the pointer. */
+typedef struct sol_attn_stats {
+  unsigned long long kept_blocks;  /* number of kept (i, j) block pairs */
+  unsigned long long total_blocks; /* B * H * Nq * Nk */
+  unsigned long long kept_pairs;   /* sum over kept (i, j) of n_i * n_j: exact query-key pairs */
+  unsigned int min_kept;           /* fewest kept blocks of any query block */
+  unsigned int max_kept;           /* most kept blocks of any query block */
+} sol_attn_stats;
+
+/* Bytes of device workspace sol_attn_forward needs (work-queue counters).
+ * Returns 0 for unsupported sizes. */
+size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
+
+/*
+ * Pooling pre-pass (§2 "Block-Sparse Attention" mean pooling; §3 "Approximate
+ * correction": pooled keys and summed values = n_j * mean).
+ *   kpool[b][h][j][:] = mean of k[b][h][t][:] over the valid tokens t of block j
+ *   vmean[b][h][j][:] = mean of v[b][h][t][:] over the same tokens
+ * k, v: bf16 [B][H][N][d]; kpool, vmean: fp32 [B][H][ceil(N/Bk)][d], written.
+ * Means are accumulated in fp32.
+ */
+int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean,
+                  int B, int H, int N, int d, int Bk, void* stream);
+
+/*
+ * Sparse attention forward with proxy correction (all sections cited above).
+ *   q, k, v   bf16 [B][H][N][d] (read)
+ *   out       fp32 [B][H][N][d] (written)
+ *   tau       threshold offset in natural-log units, 0 <= tau <= +inf
+ *   flags     SOL_F_* bits
+ *   stats     device sol_attn_stats or NULL
+ *   kpool, vmean  fp32 [B][H][Nk][d]; written by the pre-pass unless
+ *                 SOL_F_POOLED, in which case they are read as given
+ *   workspace device memory of at least sol_attn_workspace_bytes() bytes,
+ *             8-byte aligned; its content on entry does not matter
+ * Launches the pooling pre-pass (unless SOL_F_POOLED) and one fused kernel:
+ * a persistent grid takes query blocks from an atomic queue; for each it
+ * computes the proxy row on chip, routes, runs bf16 MFMA attention over the
+ * kept key blocks with an online softmax, and folds the skipped blocks'
+ * correction into the same accumulator.
+ */
+int sol_attn_forward(const void* q, const void* k, const void* v, float* out,
+                     int B, int H, int N, int d, int Bq, int Bk, float tau,
+                     unsigned flags, sol_attn_stats* stats,
+                     float* kpool, float* vmean,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sol_attn_forward plus an export of the routing decisions it used: the same
+ * kernel, with the kept-block bitmap written as it routes.
+ *   kept_bitmap  device uint32 [B][H][Nq][ceil(Nk/32)]; bit (j % 32) of word
+ *                j / 32 of row (b, h, i) is 1 iff key block j was kept for
+ *                query block i. Must not be NULL.
+ */
+int sol_attn_forward_debug(const void* q, const void* k, const void* v, float* out,
+                           int B, int H, int N, int d, int Bq, int Bk, float tau,
+                           unsigned flags, sol_attn_stats* stats,
+                           float* kpool, float* vmean,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           uint32_t* kept_bitmap);
+
+/* Static description of a return code. */
+const char* sol_attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOL_ATTN_H */

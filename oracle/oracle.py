@@ -95,6 +95,7 @@ def attend_head(
     tau: float,
     keep_override: Optional[np.ndarray] = None,
     query_blocks: Optional[Iterable[int]] = None,
+    correction: bool = True,
 ) -> Dict[str, np.ndarray]:
     """Sparse-plus-corrected attention of one head; q, k, v are [N, d].
 
@@ -108,6 +109,8 @@ def attend_head(
     condition on another implementation's choices at near-ties).
     ``query_blocks`` restricts the work to those query blocks; output rows of
     other blocks are NaN and their s/M/keep rows are NaN/False.
+    ``correction=False`` drops the skipped blocks instead (the keep-or-drop
+    "exact-only" baseline of §4 "Ablations", same selected blocks).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -136,7 +139,7 @@ def attend_head(
     for i in rows:
         r0, r1 = qb[i]
         kept = np.flatnonzero(keep[i])
-        skipped = np.flatnonzero(~keep[i])
+        skipped = np.flatnonzero(~keep[i]) if correction else np.zeros(0, dtype=np.int64)
         tok = (np.concatenate([np.arange(kb[j, 0], kb[j, 1]) for j in kept])
                if len(kept) else np.zeros(0, dtype=np.int64))
         x = (q[r0:r1] @ k[tok].T) * scale                     # exact logits [n_i, T]

@@ -1,0 +1,86 @@
+"""Shared parity machinery for the GPU tests: run the HIP path through the C
+ABI, run the fp64 oracle on the same bf16 inputs, compare.
+
+Tolerances:
+  * kept-block bitmap: exact, except blocks whose fp64 proxy lies within 1e-3
+    of the threshold M_i - tau (either decision is correct there);
+  * output: max |gpu - oracle| <= 2e-2 with the oracle conditioned on the
+    GPU's routing (bf16 inputs, fp32 accumulation, unit-scale outputs);
+  * stats: exact integer agreement with the exported bitmap.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+import torch
+
+import block_sparse_attention_14_amd as sa
+from oracle import attend_head, route_head
+from workloads import bf16_bits_to_f64
+
+BITMAP_TIE = 1e-3
+OUT_ATOL = 2e-2
+
+
+def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def run_gpu(qb, kb, vb, tau, flags=0, runner: Optional[sa.SolAttention] = None, device="cuda"):
+    """Returns (out fp32 numpy, keep bool [B,H,Nq,Nk], stats dict)."""
+    B, H, N, d = qb.shape
+    q, k, v = (to_device_bf16(x, device) for x in (qb, kb, vb))
+    runner = runner or sa.SolAttention(B, H, N, d, device)
+    bm = torch.zeros(sa.bitmap_shape(B, H, N), dtype=torch.int32, device=device)
+    out = runner(q, k, v, tau, flags=flags, bitmap=bm)
+    torch.cuda.synchronize()
+    keep = sa.unpack_bitmap(bm, -(-N // 64))
+    return out.cpu().numpy(), keep, runner.read_stats()
+
+
+def check_bitmap(gpu_keep: np.ndarray, s: np.ndarray, M: np.ndarray, keep: np.ndarray, tau: float, where=""):
+    if math.isinf(tau):
+        assert gpu_keep.all(), f"{where}: tau=inf must keep every block"
+        return
+    near = np.abs(s - (M[:, None] - tau)) <= BITMAP_TIE
+    bad = (gpu_keep != keep) & ~near
+    assert not bad.any(), f"{where}: {int(bad.sum())} routing decisions differ away from the threshold, " \
+                          f"first at {np.argwhere(bad)[:3].tolist()}"
+    assert gpu_keep.sum(axis=1).min() >= 1, f"{where}: a query block kept nothing"
+    # every kept block is within the tie band of the threshold or above it
+    assert (s[gpu_keep] >= (M[:, None] - tau - BITMAP_TIE).repeat(s.shape[1], axis=1)[gpu_keep]).all()
+
+
+def check_head(qb, kb, vb, out_gpu, keep_gpu, tau, query_blocks: Optional[Iterable[int]] = None, where=""):
+    """Bitmap on every query block of the head; outputs on `query_blocks` (all if None)."""
+    q, k, v = (bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    s, M, keep = route_head(q, k, 64, 64, tau)
+    check_bitmap(keep_gpu, s, M, keep, tau, where)
+    r = attend_head(q, k, v, 64, 64, tau, keep_override=keep_gpu, query_blocks=query_blocks)
+    rows = np.concatenate([np.arange(i * 64, min(q.shape[0], i * 64 + 64)) for i in r["rows"]])
+    err = np.abs(out_gpu[rows] - r["out"][rows]).max()
+    assert np.isfinite(out_gpu[rows]).all(), f"{where}: non-finite output"
+    assert err <= OUT_ATOL, f"{where}: max abs error {err:.3e} > {OUT_ATOL}"
+    return err
+
+
+def check_stats(stats, keep_all: np.ndarray, N: int):
+    """keep_all: [B, H, Nq, Nk] bool from the bitmap."""
+    Nq, Nk = keep_all.shape[-2:]
+    n = np.minimum(64, N - 64 * np.arange(Nk)).astype(np.int64)
+    per = keep_all.sum(axis=-1)
+    assert stats["kept_blocks"] == int(keep_all.sum())
+    assert stats["total_blocks"] == int(np.prod(keep_all.shape))
+    assert stats["min_kept"] == int(per.min()) and stats["max_kept"] == int(per.max())
+    pairs = (keep_all * n[None, None, None, :]).sum(axis=-1) * n[None, None, :]  # n_i == n_j sizes
+    assert stats["kept_pairs"] == int(pairs.sum())
+
+
+def sample_blocks(Nq: int, rng: np.random.Generator, k: int = 6) -> Sequence[int]:
+    """First, last (ragged) and a few random query blocks."""
+    picks = {0, Nq - 1}
+    picks.update(rng.choice(Nq, size=min(k, Nq), replace=False).tolist())
+    return sorted(picks)

@@ -1,0 +1,118 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects every bad argument on the host before launching anything.
+
+Every call below is invalid on purpose; pointer values are fake and are never
+dereferenced because validation fails first.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_14_amd as sa
+from block_sparse_attention_14_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sol_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sa.LIB_PATH), reason="libsolattn.so not built")
+
+P = 0x10000  # fake, 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sol_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    L = sa.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_strerror():
+    for code in (0, -1, -2, -3, -4):
+        assert sa.strerror(code) and sa.strerror(code) != sa.strerror(-99)
+
+
+def test_workspace_bytes():
+    L = sa.lib()
+    assert L.sol_attn_workspace_bytes(1, 12, 32760, 128, 64, 64) >= 8
+    assert L.sol_attn_workspace_bytes(1, 12, 32760, 96, 64, 64) == 0
+    assert L.sol_attn_workspace_bytes(1, 12, 32760, 128, 32, 64) == 0
+    assert L.sol_attn_workspace_bytes(0, 12, 32760, 128, 64, 64) == 0
+    assert L.sol_attn_workspace_bytes(1, 1, sa.SOL_ATTN_MAX_N + 1, 128, 64, 64) == 0
+
+
+def fwd(**over):
+    a = dict(q=P, k=P, v=P, out=P, B=1, H=2, N=1000, d=128, Bq=64, Bk=64, tau=2.0, flags=0, stats=None,
+             kpool=P, vmean=P, ws=P, ws_bytes=256, stream=None)
+    a.update(over)
+    return sa.lib().sol_attn_forward(a["q"], a["k"], a["v"], a["out"], a["B"], a["H"], a["N"], a["d"],
+                                     a["Bq"], a["Bk"], ctypes.c_float(a["tau"]), ctypes.c_uint(a["flags"]),
+                                     a["stats"], a["kpool"], a["vmean"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), sa.SOL_EINVAL),
+    (dict(k=None), sa.SOL_EINVAL),
+    (dict(v=None), sa.SOL_EINVAL),
+    (dict(out=None), sa.SOL_EINVAL),
+    (dict(kpool=None), sa.SOL_EINVAL),
+    (dict(vmean=None), sa.SOL_EINVAL),
+    (dict(ws=None), sa.SOL_EINVAL),
+    (dict(q=P + 2), sa.SOL_EINVAL),
+    (dict(out=P + 4), sa.SOL_EINVAL),
+    (dict(ws=P + 4), sa.SOL_EINVAL),
+    (dict(stats=P + 4), sa.SOL_EINVAL),
+    (dict(B=0), sa.SOL_EINVAL),
+    (dict(H=-1), sa.SOL_EINVAL),
+    (dict(N=0), sa.SOL_EINVAL),
+    (dict(d=0), sa.SOL_EINVAL),
+    (dict(tau=-1e-6), sa.SOL_EINVAL),
+    (dict(tau=float("nan")), sa.SOL_EINVAL),
+    (dict(tau=-math.inf), sa.SOL_EINVAL),
+    (dict(flags=1 << 7), sa.SOL_EINVAL),
+    (dict(d=96), sa.SOL_EUNSUPPORTED),
+    (dict(d=256), sa.SOL_EUNSUPPORTED),
+    (dict(Bq=32), sa.SOL_EUNSUPPORTED),
+    (dict(Bk=128), sa.SOL_EUNSUPPORTED),
+    (dict(N=sa.SOL_ATTN_MAX_N + 1), sa.SOL_EUNSUPPORTED),
+    (dict(ws_bytes=4), sa.SOL_EWORKSPACE),
+])
+def test_forward_rejects_before_launch(over, code):
+    assert fwd(**over) == code
+
+
+def test_debug_requires_bitmap():
+    L = sa.lib()
+    rc = L.sol_attn_forward_debug(P, P, P, P, 1, 2, 1000, 128, 64, 64, ctypes.c_float(2.0), ctypes.c_uint(0),
+                                  None, P, P, P, 256, None, None)
+    assert rc == sa.SOL_EINVAL
+    rc = L.sol_attn_forward_debug(P, P, P, P, 1, 2, 1000, 128, 64, 64, ctypes.c_float(2.0), ctypes.c_uint(0),
+                                  None, P, P, P, 256, None, P + 2)
+    assert rc == sa.SOL_EINVAL
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, P, P, 1, 2, 100, 128, 64, None), sa.SOL_EINVAL),
+    ((P, P, None, P, 1, 2, 100, 128, 64, None), sa.SOL_EINVAL),
+    ((P, P + 8, P, P, 1, 2, 100, 128, 64, None), sa.SOL_EINVAL),
+    ((P, P, P, P, 1, 2, 0, 128, 64, None), sa.SOL_EINVAL),
+    ((P, P, P, P, 1, 2, 100, 80, 64, None), sa.SOL_EUNSUPPORTED),
+    ((P, P, P, P, 1, 2, 100, 128, 16, None), sa.SOL_EUNSUPPORTED),
+])
+def test_pool_rejects_before_launch(args, code):
+    assert sa.lib().sol_attn_pool(*args) == code
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

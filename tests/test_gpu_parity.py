@@ -1,0 +1,170 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: routing bitmap exact away from a 1e-3 band around the threshold; output
+max-abs error <= 2e-2 with the oracle conditioned on the GPU's routing; stats
+equal to what the exported bitmap implies; bitwise-deterministic reruns.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_14_amd as sa
+from oracle import attend_head, block_means
+from workloads import Workload, bf16_bits_to_f64, get_workload, make_inputs
+
+from parity import check_head, check_stats, run_gpu, sample_blocks, to_device_bf16
+
+pytestmark = pytest.mark.gpu
+
+INF = math.inf
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sa.lib()
+
+
+def _report(name, tau, err):
+    print(f"[parity] {name} tau={tau} max_abs_err={err:.3e}", flush=True)
+
+
+def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, seed=0):
+    x = inputs or make_inputs(wl)
+    out, keep, stats = run_gpu(x["q"], x["k"], x["v"], tau)
+    check_stats(stats, keep, wl.N)
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            qbs = None if query_blocks_per_head is None else sample_blocks(wl.Nq, rng, query_blocks_per_head)
+            worst = max(worst, check_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], out[b, h], keep[b, h],
+                                          tau, qbs, where=f"{wl.name} b={b} h={h} tau={tau}"))
+    _report(wl.name, tau, worst)
+    return out, keep, stats
+
+
+# ---------------------------------------------------------------------------
+# small shapes: full oracle on every row
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tau", [0.0, 2.0, 4.0, INF])
+def test_tiny_fp32_layer(tau):
+    _full_parity(get_workload("tiny_fp32"), tau)
+
+
+def _custom(N, d, H=3, B=1, seed=77, grid=None):
+    return Workload(name=f"custom_N{N}_d{d}", B=B, H=H, grid=grid or (1, 1, N), d=d, dtype="bf16",
+                    taus=(), seed=seed)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 40, 63, 64, 65, 130, 1000])
+@pytest.mark.parametrize("tau", [0.0, 1.5, INF])
+def test_ragged_and_edge_lengths(N, d, tau):
+    _full_parity(_custom(N, d, H=2, seed=N + d), tau)
+
+
+@pytest.mark.parametrize("tau", [2.0, 4.0, 8.0])
+def test_image_dit_4k(tau):
+    _full_parity(get_workload("image_dit_4k"), tau)
+
+
+# ---------------------------------------------------------------------------
+# the video-sized layers: bitmap on every query block, outputs sampled
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def video32k():
+    return make_inputs(get_workload("video_dit_32k"))
+
+
+@pytest.mark.parametrize("tau", [2.0, 4.0, 8.0, INF])
+def test_video_dit_32k(video32k, tau):
+    _full_parity(get_workload("video_dit_32k"), tau, video32k, query_blocks_per_head=4, seed=int(tau) if tau < INF else 99)
+
+
+def test_video_dit_32k_imbalance():
+    wl = get_workload("video_dit_32k_imbalance")
+    out, keep, stats = _full_parity(wl, 8.0, query_blocks_per_head=4, seed=3)
+    per_q = keep.sum(axis=-1)
+    # sink heads route almost nothing, diffuse heads route almost everything
+    assert per_q[0, 6:].mean() > 0.5 * wl.Nk
+    assert per_q[0, :2].mean() < 0.05 * wl.Nk
+
+
+@pytest.fixture(scope="module")
+def video119k():
+    return make_inputs(get_workload("video_dit_119k"))
+
+
+@pytest.mark.parametrize("tau", [2.0, 4.0, 8.0])
+def test_video_dit_119k(video119k, tau):
+    _full_parity(get_workload("video_dit_119k"), tau, video119k, query_blocks_per_head=2, seed=int(tau))
+
+
+# ---------------------------------------------------------------------------
+# behaviour of the boundary
+# ---------------------------------------------------------------------------
+
+def test_deterministic_reruns(video32k):
+    a, ka, _ = run_gpu(video32k["q"], video32k["k"], video32k["v"], 4.0)
+    b, kb, _ = run_gpu(video32k["q"], video32k["k"], video32k["v"], 4.0)
+    assert (ka == kb).all()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_pool_pass_matches_block_means(d):
+    wl = _custom(1000, d, H=3, B=2, seed=5)
+    x = make_inputs(wl)
+    k, v = to_device_bf16(x["k"]), to_device_bf16(x["v"])
+    kp, vm = sa.pool(k, v)
+    torch.cuda.synchronize()
+    kp, vm = kp.cpu().numpy(), vm.cpu().numpy()
+    for b in range(wl.B):
+        for h in range(wl.H):
+            ek, _ = block_means(bf16_bits_to_f64(x["k"][b, h]), 64)
+            ev, _ = block_means(bf16_bits_to_f64(x["v"][b, h]), 64)
+            np.testing.assert_allclose(kp[b, h], ek, rtol=0, atol=2e-6 * max(1.0, np.abs(ek).max()))
+            np.testing.assert_allclose(vm[b, h], ev, rtol=0, atol=2e-6 * max(1.0, np.abs(ev).max()))
+
+
+def test_pooled_flag_and_stream_reuse():
+    wl = get_workload("image_dit_4k")
+    x = make_inputs(wl, heads=[(0, h) for h in range(wl.H)] + [(1, h) for h in range(wl.H)])
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    base = r(q, k, v, 4.0).clone()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        sa.pool(k, v, kpool=r.kpool, vmean=r.vmean)
+        again = r(q, k, v, 4.0, flags=sa.SOL_F_POOLED)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(base.view(torch.int32), again.view(torch.int32))
+
+
+def test_exact_only_ablation():
+    wl = _custom(1000, 128, H=2, seed=9)
+    x = make_inputs(wl)
+    out, keep, _ = run_gpu(x["q"], x["k"], x["v"], 1.0, flags=sa.SOL_F_EXACT_ONLY)
+    for h in range(wl.H):
+        q, k, v = (bf16_bits_to_f64(x[n][0, h]) for n in "qkv")
+        r = attend_head(q, k, v, 64, 64, 1.0, keep_override=keep[0, h], correction=False)
+        err = np.abs(out[0, h] - r["out"]).max()
+        assert err <= 2e-2, err
+
+
+def test_invalid_arguments_raise():
+    wl = _custom(100, 128, H=1)
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    r = sa.SolAttention(1, 1, 100, 128)
+    with pytest.raises(sa.SolAttnError):
+        r(q, k, v, -1.0)
+    with pytest.raises(sa.SolAttnError):
+        r(q, k, v, float("nan"))

@@ -256,3 +256,24 @@ def test_batched_attend_matches_per_head():
             one = attend_head(q[b, h], k[b, h], v[b, h], 32, 32, 1.5)
             np.testing.assert_array_equal(r["out"][b, h], one["out"])
             np.testing.assert_array_equal(r["keep"][b, h], one["keep"])
+
+
+# ---------------------------------------------------------------------------
+# Exact-only (keep-or-drop) baseline of §4 "Ablations": softmax attention
+# restricted to the tokens of the kept blocks, i.e. a masked library SDPA.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,Bq,Bk,tau", [(300, 32, 32, 0.2), (250, 64, 48, 0.1), (130, 16, 64, 0.0)])
+def test_exact_only_equals_masked_sdpa(N, Bq, Bk, tau):
+    rng = np.random.default_rng(N + Bk)
+    d = 8
+    q, k, v = rand(rng, N, d, scale=2.0), rand(rng, N, d, scale=2.0), rand(rng, N, d)
+    r = attend_head(q, k, v, Bq, Bk, tau, correction=False)
+    mask = np.zeros((N, N), dtype=bool)
+    for i in range(r["keep"].shape[0]):
+        for j in np.flatnonzero(r["keep"][i]):
+            mask[i * Bq:(i + 1) * Bq, j * Bk:(j + 1) * Bk] = True
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=torch.from_numpy(mask))[0, 0]
+    np.testing.assert_allclose(r["out"], ref.numpy(), rtol=0, atol=1e-12)
+    assert (~r["keep"]).any()
