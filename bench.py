@@ -1,0 +1,274 @@
+"""Benchmark of the Sol-Attn sparse attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tau T]
+
+A step is one full pass of the hot path over the video-DiT layer
+(B=1, H=12, 21x30x52 grid -> N=32760, d=128, bf16 inputs resident in HBM):
+the pooling pre-pass plus the fused routing / exact / correction kernel, one
+C-ABI call. The headline tau is 8; taus 2, 4 and +inf (the same kernel run
+dense) are reported alongside. Prints ONE JSON line.
+
+value = dense-equivalent TFLOP/s = 4*B*H*N^2*d / (seconds per call).
+roofline = the fused kernel's own HIP-event time against the bf16 MFMA peak
+(kept work) or the HBM peak (its algorithmic bytes), whichever floor is higher.
+cpu_baseline = the fp64 oracle on this host's cores, on a bounded sample of
+query blocks, extrapolated to a full call.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+HEADLINE_TAU = 8.0
+METRIC = "sparse-attn ms/call + dense-equiv TFLOP/s at N=32760,d=128; kept-block %"
+KERNEL_SOURCES = ["block_sparse_attention_14_amd/csrc/fwd.hip", "block_sparse_attention_14_amd/csrc/common.h",
+                  "block_sparse_attention_14_amd/csrc/kernels.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_traffic_video_dit_32k_tau8.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video_dit_32k")
+    ap.add_argument("--tau", type=float, default=HEADLINE_TAU)
+    ap.add_argument("--taus", default="2,4,8,inf", help="taus reported alongside the headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--profile-only", action="store_true", help="headline tau only, for profilers")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on one GPU only: the sparse forward shards per (batch, head) with no "
+              f"exchange, so a multi-GPU figure is one GPU's work repeated; --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_14_amd as sa
+    from workloads import get_workload, make_inputs
+
+    wl = get_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    x = make_inputs(wl)
+    gen_s = time.perf_counter() - t0
+    q, k, v = (torch.from_numpy(x[n].view(np.int16)).to(dev).view(torch.bfloat16) for n in "qkv")
+    B, H, N, d = wl.B, wl.H, wl.N, wl.d
+    runner = sa.SolAttention(B, H, N, d, dev)
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    dense = wl.dense_flops()
+    stream = torch.cuda.current_stream(dev)
+
+    def measure(tau: float, steps: int, warmup: int):
+        for _ in range(warmup):
+            runner(q, k, v, tau, out=out)
+        torch.cuda.synchronize()
+        # whole-call timing: one C-ABI call (pool + fused) per step
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            runner(q, k, v, tau, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        ms_call = e0.elapsed_time(e1) / steps
+        # per-kernel split: pool pass, then the fused kernel on the pooled buffers
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b, c in ev:
+            a.record(stream)
+            sa.pool(k, v, kpool=runner.kpool, vmean=runner.vmean)
+            b.record(stream)
+            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED)
+            c.record(stream)
+        torch.cuda.synchronize()
+        ms_pool = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+        ms_fwd = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+        stats = runner.read_stats()
+        return ms_call, ms_pool, ms_fwd, wall, stats
+
+    def kv_unique_blocks(tau: float):
+        """Key blocks kept by at least one query block, per head (from the exported bitmap)."""
+        bm = torch.zeros(sa.bitmap_shape(B, H, N), dtype=torch.int32, device=dev)
+        runner(q, k, v, tau, out=out, bitmap=bm)
+        torch.cuda.synchronize()
+        keep = sa.unpack_bitmap(bm, wl.Nk)  # [B, H, Nq, Nk]
+        used = keep.any(axis=2)             # [B, H, Nk]
+        n = np.minimum(64, N - 64 * np.arange(wl.Nk))
+        return int((used * n[None, None, :]).sum()), keep
+
+    def fwd_algorithmic(tau, stats):
+        flops = 4.0 * d * stats["kept_pairs"]
+        kv_tokens, _ = kv_unique_blocks(tau)
+        nbytes = (B * H * N * d * 2            # q, read once
+                  + 2 * kv_tokens * d * 2      # K and V of every block kept anywhere, read once
+                  + B * H * N * d * 4          # out, fp32, written once
+                  + 2 * B * H * wl.Nk * d * 4)  # pooled k and mean v, read once
+        return flops, nbytes
+
+    taus = [args.tau] if args.profile_only else sorted(
+        {args.tau} | {math.inf if t.strip() == "inf" else float(t) for t in args.taus.split(",")})
+    per_tau = {}
+    head = None
+    for tau in taus:
+        steps = args.steps if tau == args.tau else max(3, args.steps // 2)
+        ms_call, ms_pool, ms_fwd, wall, stats = measure(tau, steps, args.warmup if tau == args.tau else 2)
+        flops, nbytes = fwd_algorithmic(tau, stats)
+        t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        kept_pct = 100.0 * stats["kept_blocks"] / stats["total_blocks"]
+        rec = {
+            "ms_per_call": round(ms_call, 4),
+            "ms_pool": round(ms_pool, 4),
+            "ms_fwd": round(ms_fwd, 4),
+            "dense_equiv_tflops": round(dense / (ms_call * 1e-3) / 1e12, 1),
+            "kept_block_pct": round(kept_pct, 3),
+            "kept_token_pct": round(100.0 * stats["kept_pairs"] / (B * H * N * N), 3),
+            "kept_per_query_block_min_max": [stats["min_kept"], stats["max_kept"]],
+            "fwd_mfma_frac_of_peak": round(flops / (ms_fwd * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "fwd_hbm_frac_of_peak": round(nbytes / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "fwd_floor_bound": "mfma" if t_mfma >= t_hbm else "hbm",
+            "pool_gbs": round((2 * B * H * N * d * 2 + 2 * B * H * wl.Nk * d * 4) / (ms_pool * 1e-3) / 1e9, 1),
+        }
+        per_tau["inf" if math.isinf(tau) else f"{tau:g}"] = rec
+        print(f"[bench] tau={tau:g} {json.dumps(rec)}", file=sys.stderr, flush=True)
+        if tau == args.tau:
+            head = (ms_call, ms_pool, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps)
+
+    ms_call, ms_pool, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps = head
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    if bound == "mfma":
+        achieved, peak, unit = flops / (ms_fwd * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = nbytes / (ms_fwd * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == kernel_hash() and args.workload == "video_dit_32k" and args.tau == 8.0:
+            traffic = tr.get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.profile_only:
+        cpu = cpu_baseline(wl, x, args.tau, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(dense / (ms_call * 1e-3) / 1e12, 1),
+        "unit": "TFLOP/s (dense-equivalent, 4*B*H*N^2*d per call)",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_call, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H": H, "grid_thw": list(wl.grid), "N": N, "d": d,
+                   "Bq": wl.Bq, "Bk": wl.Bk, "tau": args.tau, "out_dtype": "fp32"},
+        "ms_per_call": round(ms_call, 4),
+        "kept_block_pct": round(kept_pct, 3),
+        "ms_pool": round(ms_pool, 4),
+        "ms_fwd": round(ms_fwd, 4),
+        "roofline": {
+            "kernel": "fwd_kernel<128> (fused routing + kept MFMA + correction)",
+            "bound": bound,
+            "achieved": round(achieved, 1),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "algorithmic_flops": flops,
+            "algorithmic_bytes": nbytes,
+        },
+        "cpu_baseline": cpu,
+        "per_tau": per_tau,
+        "context": {
+            "pages_end_to_end_speedup_video_generation": "2.1x vs dense attention (hardware not stated)",
+            "pages_end_to_end_speedup_video_editing": "2.3x vs dense attention (hardware not stated)",
+        },
+        "input_generation_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(wl, x, tau, budget_s):
+    """The fp64 oracle timed on this host on a sample of query blocks, scaled to a full call."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attend_head
+    from workloads import bf16_bits_to_f64
+
+    rng = np.random.default_rng(123)
+    heads = [(0, h) for h in range(wl.H)]
+    rng.shuffle(heads)
+    done_blocks = 0
+    t_total = 0.0
+    t_start = time.perf_counter()
+    for b, h in heads:
+        qh, kh, vh = (bf16_bits_to_f64(x[n][b, h]) for n in "qkv")
+        blocks = sorted(rng.choice(wl.Nq, size=min(64, wl.Nq), replace=False).tolist())
+        t0 = time.perf_counter()
+        attend_head(qh, kh, vh, wl.Bq, wl.Bk, tau, query_blocks=blocks)
+        t_total += time.perf_counter() - t0
+        done_blocks += len(blocks)
+        if time.perf_counter() - t_start > budget_s:
+            break
+    per_block = t_total / done_blocks
+    full_s = per_block * wl.B * wl.H * wl.Nq
+    threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    return {
+        "value": round(wl.dense_flops() / full_s / 1e12, 4),
+        "unit": "TFLOP/s (dense-equivalent, 4*B*H*N^2*d per call)",
+        "ms_per_call": round(full_s * 1e3, 1),
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done_blocks} of {wl.B * wl.H * wl.Nq} query blocks (64 random blocks per head, seed 123) "
+                  f"at tau={tau:g}: {t_total:.1f} s of oracle time, extrapolated linearly to the full call",
+        "host_cpu": cpu_model(),
+    }
+
+
+if __name__ == "__main__":
+    main()
