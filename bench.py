@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--profile-only", action="store_true", help="headline tau only, for profilers")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -176,6 +178,16 @@ def main():
             tr = json.load(f)
         if tr.get("kernel_hash") == kernel_hash() and args.workload == "video_dit_32k" and args.tau == 8.0:
             traffic = tr.get("bytes_per_launch")
+
+    if args.copy_ref_mib > 0:
+        # a plain copy of known size: reads and writes exactly copy_ref_mib MiB per launch
+        nel = args.copy_ref_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline and not args.profile_only:

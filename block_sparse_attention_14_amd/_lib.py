@@ -16,7 +16,7 @@ SOL_EHIP = -4
 SOL_F_POOLED = 1 << 0
 SOL_F_EXACT_ONLY = 1 << 1
 
-SOL_ATTN_MAX_N = 8192 * 64
+SOL_ATTN_MAX_N = 4096 * 64
 
 EXPORTS = (
     "sol_attn_workspace_bytes",

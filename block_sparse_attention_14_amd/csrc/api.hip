@@ -16,6 +16,7 @@ int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
   if (Bq != 64 || Bk != 64) return SOL_EUNSUPPORTED;
   if (N > SOL_ATTN_MAX_N) return SOL_EUNSUPPORTED;
   const long long nq = (N + 63) / 64;
+  if (nq > sol::forward_max_blocks(d)) return SOL_EUNSUPPORTED;
   if ((long long)B * H * nq > (1ll << 30)) return SOL_EUNSUPPORTED;  // ticket space
   return SOL_OK;
 }
@@ -67,7 +68,7 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   p.N = N;
   p.Nq = Nq;
   p.Nk = Nk;
-  p.nitems = BH * Nq;
+  p.nitems = sol::forward_items(BH, Nq);
   p.nwords = (Nk + 31) / 32;
   p.tau = tau;
   p.proxy_scale = (float)(1.0 / sqrt((double)d));

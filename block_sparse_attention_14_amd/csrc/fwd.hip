@@ -5,33 +5,47 @@
 // On-the-Fly Attention Sparsification", paperlayer.ai summary):
 //   §2 "Block-Sparse Attention"      proxy s_ij = mean(q_i).mean(k_j)/sqrt(d)
 //   §3 "Dynamic threshold routing"   keep j iff s_ij >= max_j s_ij - tau
-//   §3 "On-the-fly sparsification"   the proxy row and the kept list live in
-//                                    LDS only; nothing routing-related is
-//                                    written to device memory
+//   §3 "On-the-fly sparsification"   proxy rows and kept lists live in LDS
+//                                    only; nothing routing-related is written
+//                                    to device memory
 //   §3 "Approximate correction"      skipped j adds n_j e^{s_ij} mean(v_j) to the
 //                                    numerator and n_j e^{s_ij} to the denominator
 //   §3 "Unified execution"           one online-softmax state per row holds the
 //                                    exact and the corrected terms
 //
-// Work decomposition. A work item is one 64-row query block (b, h, i). A
-// persistent grid of 256-thread workgroups takes items from an atomic ticket
-// counter (budgets differ wildly between query blocks, so a static split would
-// leave CUs idle). Per item:
-//   1. the Q tile is staged through LDS; each wave keeps its 16 rows as the B
-//      operand of S^T = K Q^T in registers, and the block mean q̄ is reduced;
-//   2. the proxy row s_j (fp32, Nk values) is built in LDS from pooled keys,
-//      eight lanes per key block;
-//   3. the row max M gives the threshold; a ballot/prefix pass compacts the
-//      kept indices (ascending) into LDS and replaces each skipped score by its
-//      correction weight n_j e^{s_j - M};
-//   4. for every kept block, K (row-major) and V (transposed) tiles go through
-//      LDS; each wave computes its 64x16 slice of S^T with 16x16x32 bf16 MFMAs,
-//      applies the online softmax in base 2 (one query row per lane, so row
-//      statistics need only two cross-lane steps), and accumulates O^T += V^T P^T;
-//   5. the correction numerator sum_j w_j mean(v_j) is a GEMV over the pooled
-//      values of skipped blocks;
-//   6. the exact state and the correction are merged with a common maximum and
-//      the normalised rows are stored in fp32.
+// Work decomposition. A work item is a PAIR of neighbouring 64-row query
+// blocks (b, h, 2p) and (b, h, 2p+1). A persistent grid of 256-thread
+// workgroups (two per CU) takes items from an atomic ticket counter: per-block
+// budgets differ by two orders of magnitude, so a static split would idle CUs.
+// Pairing halves the pooled-key / pooled-value traffic of routing and
+// correction (one read serves both rows) and lets one K/V tile in LDS serve
+// both blocks whenever both keep it, which neighbours usually do.
+//
+// Per item:
+//   1. both Q tiles arrive through buffer loads (rows past the sequence read
+//      as zero); the pooled queries are reduced from those registers; the
+//      tiles pass through LDS once to become, per wave, the B operand of
+//      S^T = K Q^T (waves 0-1 own block A, waves 2-3 block B, 32 rows each);
+//   2. the two fp32 proxy rows are built in LDS from pooled keys, eight lanes
+//      per key block, a batch of loads in flight before any use;
+//   3. per row: max, threshold, skipped scores turned into correction weights
+//      n_j e^{s_j - M}; a ballot/prefix pass writes the UNION of the two kept
+//      lists (ascending, 2-bit owner mask) to LDS;
+//   4. the correction numerators sum_j w_j mean(v_j) of both rows, one pass
+//      over the pooled values;
+//   5. for every union entry, the K and V tiles stream from HBM straight into
+//      LDS (buffer loads with an LDS destination, no registers involved),
+//      double-buffered in two stages, one barrier per tile, the next tile in
+//      flight while the current one is consumed. 16-byte chunks are
+//      XOR-swizzled per row through the per-lane source addresses, so both
+//      operand reads below are bank-conflict free. Each wave whose block keeps
+//      the entry computes its 64x32 S^T with 16x16x32 bf16 MFMAs, the online
+//      softmax in base 2 with a lazily raised maximum (one query row per lane:
+//      two permlane swaps reduce a row), the row sums as an MFMA against a
+//      ones operand, and O^T += V^T P^T with V^T operands read from the
+//      row-major V tile by transposing LDS reads (ds_read_b64_tr_b16);
+//   6. exact state and correction merge under a common maximum; rows are
+//      normalised and stored in fp32.
 #include <math.h>
 
 #include <algorithm>
@@ -46,344 +60,551 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
-constexpr int kVtStride = kBlk + 4;  // bf16 per row of the transposed V tile
+// A row's running max is raised only when a tile's max exceeds it by more than
+// this (base-2 units); until then probabilities may reach 2^8, which fp32 and
+// bf16 carry as exactly (relatively) as values below 1.
+constexpr float kLazyRescale = 8.0f;
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// 16-byte load; bytes at or beyond the resource's size read as zero.
+__device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float4 ld16f(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const uint4 u = ld16(r, voff, soff);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
+// max over the four lanes l, l^16, l^32, l^48 that share one query row
+__device__ __forceinline__ float rowmax4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// LDS geometry. A K or V tile is 64 rows of 2d bytes, stored unpadded with
+// the 16-byte chunks of each row XOR-swizzled (kslot / vslot below); a stage
+// holds one K tile and one V tile. Before the kept loop the two stages also
+// hold the staged Q tiles (padded rows), the routing rows and the reduction
+// scratch.
 template <int D>
-struct Smem {
-  uint16_t Ks[kBlk][D + 8];   // K tile, row-major; also stages the Q tile
-  uint16_t Vt[D][kVtStride];  // V tile, transposed (key index fastest)
-  float qbar[D];              // pooled query of the current block
-  float cnum[D];              // correction numerator
-  float red[1024];            // reduction scratch
-  float wred[8];
-  int cnt[4];
-  int item;
+struct Geom {
+  static constexpr int RB = 2 * D;           // bytes per K / V row
+  static constexpr int TILE = kBlk * RB;     // bytes per K or V tile
+  static constexpr int STAGE = 2 * TILE;     // K tile, then V tile
+  static constexpr int NCH = TILE / 1024;    // 1 KiB DMA chunks per tile
+  static constexpr int QS = D + 8;           // staged Q row stride (bf16)
 };
 
-// Global -> register loads of one K tile and one V tile (rows >= nj are zero).
+// 16-byte slot holding chunk c of row r. K: 16 consecutive rows read at one
+// chunk cover every bank group; V: the 8 rows x 2 chunks of one transposing
+// read cover every bank group.
 template <int D>
-struct KVRegs {
-  static constexpr int CH = D / 8;                 // 16-byte chunks per row
-  static constexpr int KPER = kBlk * CH / kThreads;  // K chunks per thread
-  static constexpr int RG = kBlk * CH / kThreads;    // V rows per thread (same count)
-  uint4 k[KPER];
-  uint4 v[RG];
+__device__ __forceinline__ int kslot(int r, int c) {
+  return c ^ (D == 128 ? (r & 15) : ((r >> 1) & 7));
+}
+template <int D>
+__device__ __forceinline__ int vslot(int r, int c) {
+  return c ^ (D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3));
+}
 
-  __device__ __forceinline__ void load(const uint16_t* kt, const uint16_t* vt, int nj, int tid) {
-#pragma unroll
-    for (int u = 0; u < KPER; ++u) {
-      const int id = tid + kThreads * u;
-      const int r = id / CH, c = id % CH;
-      k[u] = r < nj ? *reinterpret_cast<const uint4*>(kt + (size_t)r * D + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-    const int a = tid / CH, c = tid % CH;
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const int row = a * RG + r;
-      v[r] = row < nj ? *reinterpret_cast<const uint4*>(vt + (size_t)row * D + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-  }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-  __device__ __forceinline__ void store(Smem<D>& sm, int tid) const {
+// Transposing LDS read: within each 16-lane group, lane j's element e is
+// element (j & 3) of the 8 bytes addressed by lane 4e + (j >> 2) of the group.
+__device__ __forceinline__ uint2 ld_tr(const unsigned char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Issue the asynchronous HBM -> LDS copy of one K tile and one V tile into a
+// stage: every wave moves NCH/4 KiB of each; rows past the resource's size
+// (the ragged last block) arrive as zeros.
+template <int D>
+__device__ __forceinline__ void dma_tile(unsigned char* stage, rsrc_t rk, rsrc_t rv, int wid, int lane) {
+  using G = Geom<D>;
 #pragma unroll
-    for (int u = 0; u < KPER; ++u) {
-      const int id = tid + kThreads * u;
-      const int r = id / CH, c = id % CH;
-      *reinterpret_cast<uint4*>(&sm.Ks[r][c * 8]) = k[u];
-    }
-    const int a = tid / CH, c = tid % CH;
-    // element e of each of the RG rows -> one contiguous run of Vt[8c + e][RG*a ..]
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t h[RG];
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        const uint32_t w = (e < 2) ? v[r].x : (e < 4) ? v[r].y : (e < 6) ? v[r].z : v[r].w;
-        h[r] = (e & 1) ? (w >> 16) : (w & 0xffffu);
-      }
-      if constexpr (RG == 4) {
-        uint2 pk;
-        pk.x = h[0] | (h[1] << 16);
-        pk.y = h[2] | (h[3] << 16);
-        *reinterpret_cast<uint2*>(&sm.Vt[8 * c + e][RG * a]) = pk;
-      } else {
-        *reinterpret_cast<uint32_t*>(&sm.Vt[8 * c + e][RG * a]) = h[0] | (h[1] << 16);
-      }
-    }
+  for (int u = 0; u < G::NCH / 4; ++u) {
+    const int n = wid + 4 * u;
+    const int byte = 1024 * n + 16 * lane;
+    const int r = byte / G::RB, sl = (byte % G::RB) / 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + 1024 * n), 16,
+                                             r * G::RB + 16 * kslot<D>(r, sl), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + G::TILE + 1024 * n), 16,
+                                             r * G::RB + 16 * vslot<D>(r, sl), 0, 0, 0);
   }
+}
+
+template <int D>
+struct alignas(16) Small {
+  float qbar[2][D];  // pooled queries of blocks A and B
+  float cnum[2][D];  // correction numerators
+  float wred[2][8];
+  float cden[2];
+  int cnt[3][4];
+  int lastkept[2];
+  int item;
 };
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
-  __shared__ Smem<D> sm;
+  using G = Geom<D>;
+  // Two separate LDS objects for the two stages, so that reads of one stage
+  // never wait for copies still landing in the other.
+  __shared__ __attribute__((aligned(16))) unsigned char stA[G::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char stB[G::STAGE];
+  __shared__ Small<D> sm;
   extern __shared__ __align__(16) unsigned char dyn[];
-  float* wrow = reinterpret_cast<float*>(dyn);                  // [Nk] scores, then weights
-  uint16_t* klist = reinterpret_cast<uint16_t*>(dyn + 4 * (size_t)p.Nk);  // [Nk] kept indices
+  uint16_t* ulist = reinterpret_cast<uint16_t*>(dyn);  // [Nk] union of kept lists: j | A<<14 | B<<15
+  const int Nk = p.Nk, N = p.N;
+  float* wrow0 = reinterpret_cast<float*>(stA);  // [Nk] block A: scores, then weights (before the kept loop)
+  float* wrow1 = reinterpret_cast<float*>(stB);  // [Nk] block B
 
-  constexpr int NDS = D / 32;  // k-steps of S^T (d direction)
-  constexpr int NDT = D / 16;  // 16-row tiles of O^T (d direction)
+  constexpr int NDS = D / 32;  // k-steps of S^T along d
+  constexpr int NDT = D / 16;  // 16-row tiles of O^T along d
+  constexpr int CH = D / 8;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int N = p.N, Nk = p.Nk;
+  const int qb = wid >> 1;           // which block of the pair this wave serves
+  const int qrow0 = 32 * (wid & 1);  // first of its 32 rows in that block
+  const int npairs = (p.Nq + 1) >> 1;
+  const int nlast = N - (Nk - 1) * kBlk;
+  const float csc = p.scale_log2;
 
   for (;;) {
     if (tid == 0) sm.item = (int)atomicAdd(p.queue + kQueueTicket, 1u);
     __syncthreads();
     const int item = sm.item;
     if (item >= p.nitems) break;
-    const int bh = item / p.Nq;  // head-major: neighbouring query blocks are consecutive tickets
-    const int qi = item - bh * p.Nq;
+    const int bh = item / npairs;  // head-major: neighbouring pairs are consecutive tickets
+    const int qA = 2 * (item - bh * npairs);
+    const bool hasB = qA + 1 < p.Nq;
     const size_t hoff = (size_t)bh * N * D;
-    const int r0 = qi * kBlk;
-    const int ni = min(kBlk, N - r0);
+    const int nA = min(kBlk, N - qA * kBlk);
+    const int nB = hasB ? min(kBlk, N - (qA + 1) * kBlk) : 0;
+    const int nmine = qb ? nB : nA;
 
-    // ---- 1. Q tile -> LDS, Q^T operands -> registers, pooled query ----
+    // ---- 1. Q tiles: registers -> pooled queries, LDS -> Q^T operands ----
+    bf16x8 qop[2][NDS];
     {
-      constexpr int CH = D / 8, PER = kBlk * CH / kThreads;
-      const uint16_t* src = p.q + hoff + (size_t)r0 * D;
+      constexpr int PER = kBlk * CH / kThreads, RSTEP = kThreads / CH;
+      const uint32_t qoff = ((tid / CH) * D + (tid % CH) * 8) * 2;
+      uint4 qr[2][PER];
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int id = tid + kThreads * u;
-        const int r = id / CH, c = id % CH;
-        *reinterpret_cast<uint4*>(&sm.Ks[r][c * 8]) =
-            r < ni ? *reinterpret_cast<const uint4*>(src + (size_t)r * D + c * 8) : make_uint4(0, 0, 0, 0);
+      for (int blk = 0; blk < 2; ++blk) {
+        const int nb = blk ? nB : nA;
+        const rsrc_t r = make_rsrc(p.q + hoff + (size_t)(qA + blk) * kBlk * D, (uint32_t)nb * D * 2);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) qr[blk][u] = ld16(r, qoff, u * RSTEP * D * 2);
       }
-    }
-    __syncthreads();
-    bf16x8 qop[NDS];
+      float* part = reinterpret_cast<float*>(stA + kBlk * G::QS * 2);  // [4 waves][2][D], past Q tile A
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-      qop[ds] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.Ks[16 * wid + c16][32 * ds + 8 * g]));
-    {
-      constexpr int PARTS = kThreads / D, RP = kBlk / PARTS;
-      const int col = tid % D, part = tid / D;
-      float s = 0.f;
-      for (int r = part * RP; r < part * RP + RP; ++r) s += bf16lo(sm.Ks[r][col]);
-      sm.red[part * D + col] = s;
-    }
-    __syncthreads();
-    if (tid < D) {
-      float s = 0.f;
+      for (int blk = 0; blk < 2; ++blk) {
+        uint16_t* qd = reinterpret_cast<uint16_t*>(blk ? stB : stA) + (tid / CH) * G::QS + (tid % CH) * 8;
+        float cs[8];
 #pragma unroll
-      for (int part = 0; part < kThreads / D; ++part) s += sm.red[part * D + tid];
-      sm.qbar[tid] = s / (float)ni;
+        for (int e = 0; e < 8; ++e) cs[e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          *reinterpret_cast<uint4*>(qd + u * RSTEP * G::QS) = qr[blk][u];
+          const uint4 w = qr[blk][u];
+          cs[0] += bf16lo(w.x); cs[1] += bf16hi(w.x); cs[2] += bf16lo(w.y); cs[3] += bf16hi(w.y);
+          cs[4] += bf16lo(w.z); cs[5] += bf16hi(w.z); cs[6] += bf16lo(w.w); cs[7] += bf16hi(w.w);
+        }
+        // lanes sharing tid % CH hold the same columns of other rows
+#pragma unroll
+        for (int o = CH; o < 64; o <<= 1)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cs[e] += __shfl_xor(cs[e], o);
+        if (lane < CH) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part[(wid * 2 + blk) * D + lane * 8 + e] = cs[e];
+        }
+      }
+      __syncthreads();
+      if (tid < 2 * D) {
+        const int blk = tid / D, col = tid % D;
+        const int nb = blk ? nB : nA;
+        const float s = (part[(0 * 2 + blk) * D + col] + part[(1 * 2 + blk) * D + col]) +
+                        (part[(2 * 2 + blk) * D + col] + part[(3 * 2 + blk) * D + col]);
+        sm.qbar[blk][col] = nb > 0 ? s / (float)nb : 0.f;
+      }
+      const uint16_t* qs = reinterpret_cast<const uint16_t*>(qb ? stB : stA) + (qrow0 + c16) * G::QS + 8 * g;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds)
+          qop[qt][ds] = as_bf16x8(*reinterpret_cast<const uint4*>(&qs[16 * qt * G::QS + 32 * ds]));
     }
-    __syncthreads();
+    __syncthreads();  // qbar complete; the Q tiles may now be overwritten
 
-    // ---- 2. proxy row s_j = q̄ . k̄_j / sqrt(d) into LDS, and its maximum ----
+    // ---- 2. proxy rows s_j = q̄ . k̄_j / sqrt(d), both blocks, into LDS ----
     {
       constexpr int NV = D / 32;  // float4 per lane; 8 lanes cover one pooled key
+      constexpr int U = 4;        // key blocks in flight per lane (64 KiB per workgroup at d=128)
+      constexpr int JS = kThreads / 8;
       const int sub = tid & 7, jg = tid >> 3;
-      float4 qv[NV];
+      float4 qa[NV], qbv[NV];
 #pragma unroll
-      for (int t = 0; t < NV; ++t) qv[t] = *reinterpret_cast<const float4*>(&sm.qbar[4 * (sub + 8 * t)]);
-      const float* kp = p.kpool + (size_t)bh * Nk * D;
-      float lmax = -INFINITY;
-      for (int j0 = 0; j0 < Nk; j0 += kThreads / 8) {
-        const int j = j0 + jg;
-        float a = 0.f;
-        if (j < Nk) {
-          const float4* row = reinterpret_cast<const float4*>(kp + (size_t)j * D);
+      for (int t = 0; t < NV; ++t) {
+        qa[t] = *reinterpret_cast<const float4*>(&sm.qbar[0][4 * (sub + 8 * t)]);
+        qbv[t] = *reinterpret_cast<const float4*>(&sm.qbar[1][4 * (sub + 8 * t)]);
+      }
+      const rsrc_t rk = make_rsrc(p.kpool + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
+      const uint32_t voff = (jg * D + sub * 4) * 4;
+      float mA = -INFINITY, mB = -INFINITY;
+      for (int j0 = 0; j0 < Nk; j0 += U * JS) {
+        float4 x[U][NV];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int t = 0; t < NV; ++t) x[u][t] = ld16f(rk, voff + t * 128, (uint32_t)(j0 + u * JS) * D * 4);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * JS + jg;
+          float a = 0.f, b = 0.f;
 #pragma unroll
           for (int t = 0; t < NV; ++t) {
-            const float4 x = row[sub + 8 * t];
-            a += qv[t].x * x.x + qv[t].y * x.y + qv[t].z * x.z + qv[t].w * x.w;
+            a += qa[t].x * x[u][t].x + qa[t].y * x[u][t].y + qa[t].z * x[u][t].z + qa[t].w * x[u][t].w;
+            b += qbv[t].x * x[u][t].x + qbv[t].y * x[u][t].y + qbv[t].z * x[u][t].z + qbv[t].w * x[u][t].w;
+          }
+          a += __shfl_xor(a, 1);
+          b += __shfl_xor(b, 1);
+          a += __shfl_xor(a, 2);
+          b += __shfl_xor(b, 2);
+          a += __shfl_xor(a, 4);
+          b += __shfl_xor(b, 4);
+          a *= p.proxy_scale;
+          b *= p.proxy_scale;
+          if (j < Nk) {
+            if (sub == 0) {
+              wrow0[j] = a;
+              wrow1[j] = b;
+            }
+            mA = fmaxf(mA, a);
+            mB = fmaxf(mB, b);
           }
         }
-        a += __shfl_xor(a, 1);
-        a += __shfl_xor(a, 2);
-        a += __shfl_xor(a, 4);
-        const float sj = a * p.proxy_scale;
-        if (j < Nk) {
-          if (sub == 0) wrow[j] = sj;
-          lmax = fmaxf(lmax, sj);
-        }
       }
-      lmax = wave_max(lmax);
-      if (lane == 0) sm.wred[wid] = lmax;
+      mA = wave_max(mA);
+      mB = wave_max(mB);
+      if (lane == 0) {
+        sm.wred[0][wid] = mA;
+        sm.wred[1][wid] = mB;
+      }
     }
     __syncthreads();
-    const float M = fmaxf(fmaxf(sm.wred[0], sm.wred[1]), fmaxf(sm.wred[2], sm.wred[3]));
+    const float MA = fmaxf(fmaxf(sm.wred[0][0], sm.wred[0][1]), fmaxf(sm.wred[0][2], sm.wred[0][3]));
+    const float MB = fmaxf(fmaxf(sm.wred[1][0], sm.wred[1][1]), fmaxf(sm.wred[1][2], sm.wred[1][3]));
 
-    // ---- 3. route: keep iff s_j >= M - tau; skipped scores become weights ----
-    const float theta = M - p.tau;
-    float wsum = 0.f;
-    int nk = 0;
-    for (int j0 = 0; j0 < Nk; j0 += kThreads) {
-      const int j = j0 + tid;
-      bool keep = false;
-      if (j < Nk) {
-        const float sj = wrow[j];
-        keep = sj >= theta;
-        float w = 0.f;
-        if (!keep) w = (float)min(kBlk, N - j * kBlk) * expf(sj - M);
-        wrow[j] = w;
-        wsum += w;
+    // ---- 3. route both rows; weights for skipped blocks; union kept list ----
+    int nu = 0, nkA = 0, nkB = 0;
+    {
+      float wsA = 0.f, wsB = 0.f;
+      const float thA = MA - p.tau, thB = MB - p.tau;
+      uint32_t* bmA = p.bitmap ? p.bitmap + (size_t)(bh * p.Nq + qA) * p.nwords : nullptr;
+      uint32_t* bmB = (p.bitmap && hasB) ? bmA + p.nwords : nullptr;
+      for (int j0 = 0; j0 < Nk; j0 += kThreads) {
+        const int j = j0 + tid;
+        bool kA = false, kB = false;
+        if (j < Nk) {
+          const float nj = (float)min(kBlk, N - j * kBlk);
+          const float sa = wrow0[j];
+          kA = sa >= thA;
+          const float wa = kA ? 0.f : nj * expf(sa - MA);
+          wrow0[j] = wa;
+          wsA += wa;
+          float wb = 0.f;
+          if (hasB) {
+            const float sb = wrow1[j];
+            kB = sb >= thB;
+            wb = kB ? 0.f : nj * expf(sb - MB);
+            wsB += wb;
+          }
+          wrow1[j] = wb;
+        }
+        const unsigned long long bA = __ballot(kA), bB = __ballot(kB), bU = bA | bB;
+        if (lane == 0) {
+          sm.cnt[0][wid] = __popcll(bU);
+          sm.cnt[1][wid] = __popcll(bA);
+          sm.cnt[2][wid] = __popcll(bB);
+          const int w0 = (j0 + 64 * wid) >> 5;
+          if (bmA) {
+            if (w0 < p.nwords) bmA[w0] = (uint32_t)bA;
+            if (w0 + 1 < p.nwords) bmA[w0 + 1] = (uint32_t)(bA >> 32);
+          }
+          if (bmB) {
+            if (w0 < p.nwords) bmB[w0] = (uint32_t)bB;
+            if (w0 + 1 < p.nwords) bmB[w0 + 1] = (uint32_t)(bB >> 32);
+          }
+        }
+        if (j == Nk - 1) {
+          sm.lastkept[0] = kA;
+          sm.lastkept[1] = kB;
+        }
+        __syncthreads();
+        int off = nu;
+        for (int w2 = 0; w2 < wid; ++w2) off += sm.cnt[0][w2];
+        if (kA || kB)
+          ulist[off + __popcll(bU & ((1ull << lane) - 1ull))] = (uint16_t)(j | (kA ? 1 << 14 : 0) | (kB ? 1 << 15 : 0));
+        nu += sm.cnt[0][0] + sm.cnt[0][1] + sm.cnt[0][2] + sm.cnt[0][3];
+        nkA += sm.cnt[1][0] + sm.cnt[1][1] + sm.cnt[1][2] + sm.cnt[1][3];
+        nkB += sm.cnt[2][0] + sm.cnt[2][1] + sm.cnt[2][2] + sm.cnt[2][3];
+        __syncthreads();
       }
-      const unsigned long long bal = __ballot(keep);
-      if (lane == 0) sm.cnt[wid] = __popcll(bal);
-      if (p.bitmap != nullptr && lane == 0) {
-        const int w0 = (j0 + 64 * wid) >> 5;
-        uint32_t* brow = p.bitmap + (size_t)item * p.nwords;
-        if (w0 < p.nwords) brow[w0] = (uint32_t)bal;
-        if (w0 + 1 < p.nwords) brow[w0 + 1] = (uint32_t)(bal >> 32);
+      wsA = wave_sum(wsA);
+      wsB = wave_sum(wsB);
+      if (lane == 0) {
+        sm.wred[0][4 + wid] = wsA;
+        sm.wred[1][4 + wid] = wsB;
       }
-      __syncthreads();
-      int off = nk;
-      for (int w2 = 0; w2 < wid; ++w2) off += sm.cnt[w2];
-      if (keep) klist[off + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)j;
-      nk += sm.cnt[0] + sm.cnt[1] + sm.cnt[2] + sm.cnt[3];
-      __syncthreads();
     }
-    wsum = wave_sum(wsum);
-    if (lane == 0) sm.wred[4 + wid] = wsum;
-    __syncthreads();  // klist, wrow and wred complete
-    const float cden = (sm.wred[4] + sm.wred[5]) + (sm.wred[6] + sm.wred[7]);
 
-    // ---- 4. exact attention over the kept blocks (online softmax, base 2) ----
-    f32x4 acc[NDT];
+    // ---- 4. correction numerators cnum[b][c] = sum_j w_bj vbar_j[c] ----
+    {
+      constexpr int C4 = D / 4, JG = kThreads / C4, U = 16;  // 64 KiB of pooled values in flight
+      const int c4 = tid % C4, jg = tid / C4;
+      float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+      if (!p.exact_only && (nkA < Nk || (hasB && nkB < Nk))) {
+        const rsrc_t rv = make_rsrc(p.vmean + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
+        const uint32_t voff = (jg * D + c4 * 4) * 4;
+        for (int j0 = 0; j0 < Nk; j0 += U * JG) {
+          float4 x[U];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
-    const uint16_t* kh = p.k + hoff;
-    const uint16_t* vh = p.v + hoff;
-    KVRegs<D> regs;
-    if (nk > 0) {
-      const int j = klist[0];
-      regs.load(kh + (size_t)j * kBlk * D, vh + (size_t)j * kBlk * D, min(kBlk, N - j * kBlk), tid);
-    }
-    for (int t = 0; t < nk; ++t) {
-      const int j = klist[t];
-      const int nj = min(kBlk, N - j * kBlk);
-      __syncthreads();  // the previous tile is no longer read
-      regs.store(sm, tid);
+          for (int u = 0; u < U; ++u) x[u] = ld16f(rv, voff, (uint32_t)(j0 + u * JG) * D * 4);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * JG + jg;
+            if (j < Nk) {
+              const float w0 = wrow0[j], w1 = wrow1[j];
+              a0.x += w0 * x[u].x; a0.y += w0 * x[u].y; a0.z += w0 * x[u].z; a0.w += w0 * x[u].w;
+              a1.x += w1 * x[u].x; a1.y += w1 * x[u].y; a1.z += w1 * x[u].z; a1.w += w1 * x[u].w;
+            }
+          }
+        }
+      }
+      __syncthreads();  // weights fully read: their space becomes reduction scratch
+      float* red = reinterpret_cast<float*>(stA);  // [2][JG][D]
+      *reinterpret_cast<float4*>(&red[(0 * JG + jg) * D + 4 * c4]) = a0;
+      *reinterpret_cast<float4*>(&red[(1 * JG + jg) * D + 4 * c4]) = a1;
       __syncthreads();
-      if (t + 1 < nk) {
-        const int jn = klist[t + 1];
-        regs.load(kh + (size_t)jn * kBlk * D, vh + (size_t)jn * kBlk * D, min(kBlk, N - jn * kBlk), tid);
+      if (tid < 2 * D) {
+        const int blk = tid / D, col = tid % D;
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < JG; ++r) s += red[(blk * JG + r) * D + col];
+        sm.cnum[blk][col] = s;
       }
+      if (tid < 2) sm.cden[tid] = (sm.wred[tid][4] + sm.wred[tid][5]) + (sm.wred[tid][6] + sm.wred[tid][7]);
+      __syncthreads();  // the tile stages are free again
+    }
 
-      // S^T[kv][q] for kv in 16-row tiles kt, q = this wave's 16 rows
-      f32x4 st[4];
+    // ---- 5. exact attention over the union list (online softmax, base 2) ----
+    f32x4 acc[2][NDT];
+    f32x4 lsum[2];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < 2; ++qt) {
+      lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.Ks[16 * kt + c16][32 * ds + 8 * g]));
-          st[kt] = mfma16x16x32(a, qop[ds], st[kt]);
-        }
-      }
-      // lane holds S^T[16kt + 4g + e][c16]: one query row, 16 keys
-      float bm = -INFINITY;
+      for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float m[2] = {-INFINITY, -INFINITY};
+    {
+      const bf16x8 ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+      const uint16_t* kh = p.k + hoff;
+      const uint16_t* vh = p.v + hoff;
+      const int ownbit = 1 << (14 + qb);
+      auto dma = [&](unsigned char* stage, int t) {
+        const int j = ulist[t] & 0x3fff;
+        const uint32_t bytes = (uint32_t)min(kBlk, N - j * kBlk) * D * 2;
+        dma_tile<D>(stage, make_rsrc(kh + (size_t)j * kBlk * D, bytes), make_rsrc(vh + (size_t)j * kBlk * D, bytes),
+                    wid, lane);
+      };
+      // per-lane byte offsets of the swizzled operand reads (independent of the key tile kt)
+      int koff[NDS];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = st[kt][e] * p.scale_log2;
-          if (16 * kt + 4 * g + e >= nj) x = -INFINITY;
-          st[kt][e] = x;
-          bm = fmaxf(bm, x);
-        }
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m, bm);
-      const float alpha = exp2f(m - mn);
-      float ls = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pe = exp2f(st[kt][e] - mn);
-          st[kt][e] = pe;
-          ls += pe;
-        }
-      l = l * alpha + ls;
-      m = mn;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-
-      // P^T operands: k-slots 0-3 = keys 32ks+4g+e, slots 4-7 = keys 32ks+16+4g+e
-      bf16x8 pb[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint4 u;
-        u.x = pack_bf16x2(st[2 * ks][0], st[2 * ks][1]);
-        u.y = pack_bf16x2(st[2 * ks][2], st[2 * ks][3]);
-        u.z = pack_bf16x2(st[2 * ks + 1][0], st[2 * ks + 1][1]);
-        u.w = pack_bf16x2(st[2 * ks + 1][2], st[2 * ks + 1][3]);
-        pb[ks] = as_bf16x8(u);
-      }
-      // O^T[d][q] += V^T[d][kv] P^T[kv][q], same key permutation on both sides
+      for (int ds = 0; ds < NDS; ++ds) koff[ds] = c16 * G::RB + 16 * kslot<D>(c16, 4 * ds + g);
+      // transposing V reads: this lane addresses row 4g + e (+32ks +16h) and the
+      // 8 bytes of columns 16dt + 4cc .. +3
+      const int ve = (lane >> 2) & 3, vcc = lane & 3, vrow = 4 * g + ve;
+      int voff[NDT];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(&sm.Vt[16 * dt + c16][32 * ks + 4 * g]);
-          const uint2 hi = *reinterpret_cast<const uint2*>(&sm.Vt[16 * dt + c16][32 * ks + 16 + 4 * g]);
-          acc[dt] = mfma16x16x32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[ks], acc[dt]);
-        }
-    }
+        voff[dt] = G::TILE + vrow * G::RB + 16 * vslot<D>(vrow, 2 * dt + (vcc >> 1)) + 8 * (vcc & 1);
 
-    // ---- 5. correction numerator: cnum[c] = sum_j w_j vbar_j[c] ----
-    {
-      constexpr int C4 = D / 4, JG = kThreads / C4;
-      const int c4 = tid % C4, jg = tid / C4;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (!p.exact_only && nk < Nk) {
-        const float4* vm = reinterpret_cast<const float4*>(p.vmean + (size_t)bh * Nk * D);
-        for (int j = jg; j < Nk; j += JG) {
-          const float w = wrow[j];
-          if (w != 0.f) {
-            const float4 x = vm[(size_t)j * C4 + c4];
-            a.x += w * x.x; a.y += w * x.y; a.z += w * x.z; a.w += w * x.w;
+      auto compute = [&](const unsigned char* stage, int e) {
+        if (!(e & ownbit)) return;  // wave-uniform: this wave's block skips the entry
+        const int j = e & 0x3fff;
+        const int nj = min(kBlk, N - j * kBlk);
+        // S^T[kv][q]: 4 key tiles x 2 query tiles; each K operand serves both
+        f32x4 st[2][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          st[0][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          st[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ds = 0; ds < NDS; ++ds) {
+            const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(stage + 16 * kt * G::RB + koff[ds]));
+            st[0][kt] = mfma16x16x32(a, qop[0][ds], st[0][kt]);
+            st[1][kt] = mfma16x16x32(a, qop[1][ds], st[1][kt]);
           }
         }
-      }
-      *reinterpret_cast<float4*>(&sm.red[jg * D + 4 * c4]) = a;
-    }
-    __syncthreads();
-    if (tid < D) {
-      float s = 0.f;
+        // lane holds S^T[16kt + 4g + i][row c16 of query tile qt]
+        if (nj < kBlk) {
 #pragma unroll
-      for (int jg = 0; jg < kThreads / (D / 4); ++jg) s += sm.red[jg * D + tid];
-      sm.cnum[tid] = s;
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * kt + 4 * g + i >= nj) {
+                st[0][kt][i] = -INFINITY;
+                st[1][kt][i] = -INFINITY;
+              }
+        }
+        bool raise = false;
+        float mn[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          // two chains of three-input maxima over the lane's 16 scores
+          float b0 = fmaxf(fmaxf(st[qt][0][0], st[qt][0][1]), st[qt][0][2]);
+          float b1 = fmaxf(fmaxf(st[qt][2][0], st[qt][2][1]), st[qt][2][2]);
+          b0 = fmaxf(fmaxf(b0, st[qt][0][3]), st[qt][1][0]);
+          b1 = fmaxf(fmaxf(b1, st[qt][2][3]), st[qt][3][0]);
+          b0 = fmaxf(fmaxf(b0, st[qt][1][1]), st[qt][1][2]);
+          b1 = fmaxf(fmaxf(b1, st[qt][3][1]), st[qt][3][2]);
+          b0 = fmaxf(b0, st[qt][1][3]);
+          b1 = fmaxf(b1, st[qt][3][3]);
+          const float bm = rowmax4(fmaxf(b0, b1)) * csc;
+          mn[qt] = bm > m[qt] + kLazyRescale ? bm : m[qt];
+          raise = raise || (mn[qt] != m[qt]);
+        }
+        if (__ballot(raise)) {  // rare: a row's max rose by more than the lazy margin
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn[qt]);
+            lsum[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= alpha;
+            m[qt] = mn[qt];
+          }
+        }
+        // P^T operand slots 0-3 = keys 32ks+4g+i, slots 4-7 = keys 32ks+16+4g+i
+        bf16x8 pb[2][2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const float nm = -m[qt];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            uint32_t w[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const f32x4& sv = st[qt][2 * ks + h];
+              w[2 * h + 0] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[0], csc, nm)),
+                                         __builtin_amdgcn_exp2f(fmaf(sv[1], csc, nm)));
+              w[2 * h + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[2], csc, nm)),
+                                         __builtin_amdgcn_exp2f(fmaf(sv[3], csc, nm)));
+            }
+            pb[qt][ks] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+          }
+          // row sums of the bf16-rounded probabilities: every output row of
+          // ones x P^T is the sum over the 32 keys of the step
+          lsum[qt] = mfma16x16x32(ones, pb[qt][0], lsum[qt]);
+          lsum[qt] = mfma16x16x32(ones, pb[qt][1], lsum[qt]);
+        }
+        // O^T[d][q] += V^T[d][kv] P^T[kv][q]; the transposing reads of rows
+        // 32ks + 4g + e and 32ks + 16 + 4g + e give exactly the keys of the P^T
+        // slots; each V^T operand serves both query tiles
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const uint2 lo = ld_tr(stage + voff[dt] + 32 * ks * G::RB);
+            const uint2 hi = ld_tr(stage + voff[dt] + (32 * ks + 16) * G::RB);
+            const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+            acc[0][dt] = mfma16x16x32(a, pb[0][ks], acc[0][dt]);
+            acc[1][dt] = mfma16x16x32(a, pb[1][ks], acc[1][dt]);
+          }
+      };
+
+      // Every barrier below is preceded by an explicit wait for all of this
+      // wave's outstanding copies: the copy into one stage is issued in one
+      // loop iteration and consumed in the next, a dependency the compiler's
+      // own wait insertion does not carry across the loop back-edge.
+      if (nu > 0) dma(stA, 0);
+      if (nu > 1) dma(stB, 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // tiles 0 and 1 are in LDS
+      for (int t = 0; t < nu; t += 2) {
+        compute(stA, ulist[t]);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // tile t+1 has landed in stB; nobody reads stA any more
+        if (t + 2 < nu) dma(stA, t + 2);
+        if (t + 1 < nu) {
+          compute(stB, ulist[t + 1]);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();  // tile t+2 has landed in stA; nobody reads stB any more
+          if (t + 3 < nu) dma(stB, t + 3);
+        }
+      }
     }
-    __syncthreads();
 
     // ---- 6. fold exact and corrected terms, normalise, store ----
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
     {
-      const float M2 = M * kLog2e;
-      const float mf = p.exact_only ? m : fmaxf(m, M2);
-      const float fa = exp2f(m - mf);
-      const float fc = p.exact_only ? 0.f : exp2f(M2 - mf);
-      const float inv = 1.f / (l * fa + cden * fc);
-      const int row = 16 * wid + c16;
-      if (row < ni) {
-        float* orow = p.out + hoff + (size_t)(r0 + row) * D;
+      const float M2 = (qb ? MB : MA) * kLog2e;
+      const float cden = sm.cden[qb];
+      const int rbase = (qA + qb) * kBlk;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int c = 16 * dt + 4 * g;
-          float4 o;
-          o.x = (acc[dt][0] * fa + sm.cnum[c + 0] * fc) * inv;
-          o.y = (acc[dt][1] * fa + sm.cnum[c + 1] * fc) * inv;
-          o.z = (acc[dt][2] * fa + sm.cnum[c + 2] * fc) * inv;
-          o.w = (acc[dt][3] * fa + sm.cnum[c + 3] * fc) * inv;
-          *reinterpret_cast<float4*>(orow + c) = o;
+      for (int qt = 0; qt < 2; ++qt) {
+        const float lt = lsum[qt][0];
+        const float mf = p.exact_only ? m[qt] : fmaxf(m[qt], M2);
+        const float fa = __builtin_amdgcn_exp2f(m[qt] - mf);
+        const float fc = p.exact_only ? 0.f : __builtin_amdgcn_exp2f(M2 - mf);
+        const float inv = 1.f / (lt * fa + cden * fc);
+        const int row = qrow0 + 16 * qt + c16;
+        if (row < nmine) {
+          float* orow = p.out + hoff + (size_t)(rbase + row) * D;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const int c = 16 * dt + 4 * g;
+            float4 o;
+            o.x = (acc[qt][dt][0] * fa + sm.cnum[qb][c + 0] * fc) * inv;
+            o.y = (acc[qt][dt][1] * fa + sm.cnum[qb][c + 1] * fc) * inv;
+            o.z = (acc[qt][dt][2] * fa + sm.cnum[qb][c + 2] * fc) * inv;
+            o.w = (acc[qt][dt][3] * fa + sm.cnum[qb][c + 3] * fc) * inv;
+            *reinterpret_cast<float4*>(orow + c) = o;
+          }
         }
       }
     }
 
     if (p.stats != nullptr && tid == 0) {
-      unsigned long long kept_tokens = (unsigned long long)nk * kBlk;
-      if (nk > 0 && klist[nk - 1] == Nk - 1) kept_tokens -= (unsigned long long)(kBlk - (N - (Nk - 1) * kBlk));
-      atomicAdd(&p.stats->kept_blocks, (unsigned long long)nk);
-      atomicAdd(&p.stats->total_blocks, (unsigned long long)Nk);
-      atomicAdd(&p.stats->kept_pairs, kept_tokens * (unsigned long long)ni);
-      atomicMin(&p.stats->min_kept, (unsigned)nk);
-      atomicMax(&p.stats->max_kept, (unsigned)nk);
+      unsigned long long pairs = 0, kept = nkA, tot = Nk;
+      const unsigned long long tokA = (unsigned long long)nkA * kBlk - (sm.lastkept[0] ? kBlk - nlast : 0);
+      pairs += tokA * (unsigned long long)nA;
+      unsigned mn = nkA, mx = nkA;
+      if (hasB) {
+        const unsigned long long tokB = (unsigned long long)nkB * kBlk - (sm.lastkept[1] ? kBlk - nlast : 0);
+        pairs += tokB * (unsigned long long)nB;
+        kept += nkB;
+        tot += Nk;
+        mn = min(mn, (unsigned)nkB);
+        mx = max(mx, (unsigned)nkB);
+      }
+      atomicAdd(&p.stats->kept_blocks, kept);
+      atomicAdd(&p.stats->total_blocks, tot);
+      atomicAdd(&p.stats->kept_pairs, pairs);
+      atomicMin(&p.stats->min_kept, mn);
+      atomicMax(&p.stats->max_kept, mx);
     }
     __syncthreads();  // LDS is rewritten by the next item
   }
@@ -391,11 +612,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 
 }  // namespace
 
-size_t forward_dynamic_lds(int Nk) { return ((size_t)Nk * 6 + 15) & ~(size_t)15; }
+size_t forward_dynamic_lds(int Nk) { return ((size_t)Nk * 2 + 15) & ~(size_t)15; }
+
+int forward_items(int BH, int Nq) { return BH * ((Nq + 1) / 2); }
+
+int forward_max_blocks(int d) {
+  // each fp32 routing row lives in one stage before the kept loop
+  return d == 128 ? Geom<128>::STAGE / 4 : Geom<64>::STAGE / 4;
+}
 
 template <int D>
 static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-  // per-device CU count and occupancy (bucketed by dynamic LDS in 8 KiB steps)
+  // per-device CU count and occupancy (bucketed by dynamic LDS in 4 KiB steps)
   static std::mutex mu;
   static int cus[64] = {0};
   static int occ_cache[64][8] = {{0}};
@@ -404,7 +632,7 @@ static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   const size_t dyn = forward_dynamic_lds(p.Nk);
-  const int bucket = (int)std::min<size_t>(7, dyn / 8192);
+  const int bucket = (int)std::min<size_t>(7, dyn / 4096);
   int grid_per_cu = 0, ncu = 0;
   {
     std::lock_guard<std::mutex> lock(mu);
@@ -413,14 +641,14 @@ static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
       e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<D>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 32 * 1024);
       if (e != hipSuccess) return e;
       cus[dev] = n;
     }
     if (occ_cache[dev][bucket] == 0) {
       int occ = 0;
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&fwd_kernel<D>),
-                                                       kThreads, (size_t)(bucket + 1) * 8192);
+                                                       kThreads, (size_t)(bucket + 1) * 4096);
       if (e != hipSuccess) return e;
       occ_cache[dev][bucket] = occ < 1 ? 1 : occ;
     }

@@ -21,7 +21,7 @@ struct FwdParams {
   unsigned* queue;       // ticket counter, zero on entry
   sol_attn_stats* stats; // nullable, reset before the launch
   uint32_t* bitmap;      // nullable, [BH][Nq][nwords]
-  int N, Nq, Nk, nitems, nwords;
+  int N, Nq, Nk, nitems, nwords;  // nitems = forward_items(BH, Nq)
   float tau;             // >= 0, may be +inf
   float proxy_scale;     // 1/sqrt(d)
   float scale_log2;      // log2(e)/sqrt(d)
@@ -41,7 +41,13 @@ hipError_t launch_reset(unsigned* queue, sol_attn_stats* stats, hipStream_t stre
 // The fused routing + exact + correction kernel (persistent grid).
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t stream);
 
-// Dynamic LDS bytes the fused kernel needs for a routing row of Nk blocks.
+// Dynamic LDS bytes the fused kernel needs for the kept list of Nk blocks.
 size_t forward_dynamic_lds(int Nk);
+
+// Number of work items (pairs of query blocks) of the fused kernel.
+int forward_items(int BH, int Nq);
+
+// Largest Nk whose two fp32 routing rows fit the kernel's LDS tile buffer.
+int forward_max_blocks(int d);
 
 }  // namespace sol

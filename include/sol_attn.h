@@ -68,9 +68,9 @@ enum {
   SOL_F_EXACT_ONLY = 1u << 1
 };
 
-/* Largest supported sequence length (the per-query-block routing row of
- * Nk = N/64 scores is held on chip). */
-#define SOL_ATTN_MAX_N (8192 * 64)
+/* Largest supported sequence length: the routing rows of Nk = N/64 scores
+ * and the kept list are held on chip (4096 key blocks). */
+#define SOL_ATTN_MAX_N (4096 * 64)
 
 /* Per-call counters, written by sol_attn_forward into DEVICE memory. All
  * fields are reset at the start of every forward that receives the pointer. */
