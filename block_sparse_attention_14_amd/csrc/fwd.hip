@@ -129,20 +129,23 @@ __device__ __forceinline__ uint2 ld_tr(const unsigned char* p) {
 }
 
 // Issue the asynchronous HBM -> LDS copy of one K tile and one V tile into a
-// stage: every wave moves NCH/4 KiB of each; rows past the resource's size
-// (the ragged last block) arrive as zeros.
+// stage: wave w moves the 1 KiB chunks w, w+4, ... of each tile; rows past the
+// resource's size (the ragged last block) arrive as zeros. A lane's source
+// offset inside its chunk is the same for every chunk of the wave (the
+// swizzles depend on row bits the chunk index does not touch), so only a
+// scalar offset changes between the copies.
 template <int D>
 __device__ __forceinline__ void dma_tile(unsigned char* stage, rsrc_t rk, rsrc_t rv, int wid, int lane) {
   using G = Geom<D>;
+  constexpr int LPR = G::RB / 16;  // lanes per row of a chunk
+  const int r = (1024 * wid) / G::RB + lane / LPR, sl = lane % LPR;
+  const uint32_t ko = r * G::RB + 16 * kslot<D>(r, sl);
+  const uint32_t vo = r * G::RB + 16 * vslot<D>(r, sl);
 #pragma unroll
   for (int u = 0; u < G::NCH / 4; ++u) {
-    const int n = wid + 4 * u;
-    const int byte = 1024 * n + 16 * lane;
-    const int r = byte / G::RB, sl = (byte % G::RB) / 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + 1024 * n), 16,
-                                             r * G::RB + 16 * kslot<D>(r, sl), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + G::TILE + 1024 * n), 16,
-                                             r * G::RB + 16 * vslot<D>(r, sl), 0, 0, 0);
+    const int off = 1024 * (wid + 4 * u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + off), 16, ko, 4096 * u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + G::TILE + off), 16, vo, 4096 * u, 0, 0);
   }
 }
 
@@ -174,7 +177,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   constexpr int NDS = D / 32;  // k-steps of S^T along d
   constexpr int NDT = D / 16;  // 16-row tiles of O^T along d
   constexpr int CH = D / 8;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c16 = lane & 15;
   const int qb = wid >> 1;           // which block of the pair this wave serves
   const int qrow0 = 32 * (wid & 1);  // first of its 32 rows in that block
