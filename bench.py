@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 HEADLINE_TAU = 8.0
 METRIC = "sparse-attn ms/call + dense-equiv TFLOP/s at N=32760,d=128; kept-block %"
 KERNEL_SOURCES = ["block_sparse_attention_14_amd/csrc/fwd.hip", "block_sparse_attention_14_amd/csrc/common.h",
-                  "block_sparse_attention_14_amd/csrc/kernels.h"]
+                  "block_sparse_attention_14_amd/csrc/kernels.h"]  # the fused kernel's sources
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_traffic_video_dit_32k_tau8.json")
 
 
@@ -103,20 +103,23 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
         ms_call = e0.elapsed_time(e1) / steps
-        # per-kernel split: pool pass, then the fused kernel on the pooled buffers
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for a, b, c in ev:
+        # per-kernel split: pool pass (k, v), planning (pooled q + item order),
+        # then the fused kernel alone on the pooled and planned buffers
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for a, b, c, e in ev:
             a.record(stream)
             sa.pool(k, v, kpool=runner.kpool, vmean=runner.vmean)
             b.record(stream)
-            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED)
+            runner.plan(q, tau)
             c.record(stream)
+            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+            e.record(stream)
         torch.cuda.synchronize()
-        ms_pool = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-        ms_fwd = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+        ms_pool = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev]))
+        ms_plan = float(np.mean([b.elapsed_time(c) for _, b, c, _ in ev]))
+        ms_fwd = float(np.mean([c.elapsed_time(e) for _, _, c, e in ev]))
         stats = runner.read_stats()
-        return ms_call, ms_pool, ms_fwd, wall, stats
+        return ms_call, ms_pool, ms_plan, ms_fwd, wall, stats
 
     def kv_unique_blocks(tau: float):
         """Key blocks kept by at least one query block, per head (from the exported bitmap)."""
@@ -143,7 +146,7 @@ def main():
     head = None
     for tau in taus:
         steps = args.steps if tau == args.tau else max(3, args.steps // 2)
-        ms_call, ms_pool, ms_fwd, wall, stats = measure(tau, steps, args.warmup if tau == args.tau else 2)
+        ms_call, ms_pool, ms_plan, ms_fwd, wall, stats = measure(tau, steps, args.warmup if tau == args.tau else 2)
         flops, nbytes = fwd_algorithmic(tau, stats)
         t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
         t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
@@ -151,6 +154,7 @@ def main():
         rec = {
             "ms_per_call": round(ms_call, 4),
             "ms_pool": round(ms_pool, 4),
+            "ms_plan": round(ms_plan, 4),
             "ms_fwd": round(ms_fwd, 4),
             "dense_equiv_tflops": round(dense / (ms_call * 1e-3) / 1e12, 1),
             "kept_block_pct": round(kept_pct, 3),
@@ -164,9 +168,9 @@ def main():
         per_tau["inf" if math.isinf(tau) else f"{tau:g}"] = rec
         print(f"[bench] tau={tau:g} {json.dumps(rec)}", file=sys.stderr, flush=True)
         if tau == args.tau:
-            head = (ms_call, ms_pool, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps)
+            head = (ms_call, ms_pool, ms_plan, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps)
 
-    ms_call, ms_pool, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps = head
+    ms_call, ms_pool, ms_plan, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps = head
     bound = "mfma" if t_mfma >= t_hbm else "hbm"
     if bound == "mfma":
         achieved, peak, unit = flops / (ms_fwd * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
@@ -211,9 +215,10 @@ def main():
         "ms_per_call": round(ms_call, 4),
         "kept_block_pct": round(kept_pct, 3),
         "ms_pool": round(ms_pool, 4),
+        "ms_plan": round(ms_plan, 4),
         "ms_fwd": round(ms_fwd, 4),
         "roofline": {
-            "kernel": "fwd_kernel<128> (fused routing + kept MFMA + correction)",
+            "kernel": "fwd_kernel<128> (fused routing + kept MFMA + correction), timed alone",
             "bound": bound,
             "achieved": round(achieved, 1),
             "peak": peak,

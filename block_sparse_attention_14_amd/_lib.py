@@ -15,12 +15,14 @@ SOL_EHIP = -4
 
 SOL_F_POOLED = 1 << 0
 SOL_F_EXACT_ONLY = 1 << 1
+SOL_F_PLANNED = 1 << 2
 
 SOL_ATTN_MAX_N = 4096 * 64
 
 EXPORTS = (
     "sol_attn_workspace_bytes",
     "sol_attn_pool",
+    "sol_attn_plan",
     "sol_attn_forward",
     "sol_attn_forward_debug",
     "sol_attn_strerror",
@@ -68,6 +70,8 @@ def lib() -> ctypes.CDLL:
                 L.sol_attn_workspace_bytes.restype = ctypes.c_size_t
                 L.sol_attn_pool.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
                 L.sol_attn_pool.restype = _i
+                L.sol_attn_plan.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+                L.sol_attn_plan.restype = _i
                 L.sol_attn_forward.argtypes = _fwd_args
                 L.sol_attn_forward.restype = _i
                 L.sol_attn_forward_debug.argtypes = _fwd_args + [_vp]

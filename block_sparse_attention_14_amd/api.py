@@ -14,7 +14,7 @@ from typing import Dict, Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import SOL_F_EXACT_ONLY, SOL_F_POOLED, check, lib  # noqa: F401
+from ._lib import SOL_F_EXACT_ONLY, SOL_F_PLANNED, SOL_F_POOLED, check, lib  # noqa: F401
 
 STATS_WORDS = 4  # sol_attn_stats is 32 bytes
 
@@ -104,6 +104,7 @@ class SolAttention:
         self.kpool = torch.empty(ps, dtype=torch.float32, device=self.device)
         self.vmean = torch.empty(ps, dtype=torch.float32, device=self.device)
         self.workspace = torch.zeros(-(-nbytes // 8), dtype=torch.int64, device=self.device)
+        assert self.workspace.data_ptr() % 256 == 0
         self.stats = new_stats(self.device)
 
     def __call__(self, q, k, v, tau: float, flags: int = 0, out: Optional[torch.Tensor] = None,
@@ -134,6 +135,15 @@ class SolAttention:
             rc = lib().sol_attn_forward_debug(*args, _ptr(bitmap))
             check(rc, "sol_attn_forward_debug")
         return out
+
+    def plan(self, q: torch.Tensor, tau: float) -> None:
+        """Pooled queries and the longest-first item order into the workspace
+        (needs self.kpool to hold the pooled keys, e.g. from pool())."""
+        _check_qkv("q", q, (self.B, self.H, self.N, self.d))
+        rc = lib().sol_attn_plan(_ptr(q), _ptr(self.kpool), self.B, self.H, self.N, self.d, self.Bq, self.Bk,
+                                 ctypes.c_float(float(tau)), _ptr(self.workspace), self.workspace.numel() * 8,
+                                 _stream(self.device))
+        check(rc, "sol_attn_plan")
 
     def read_stats(self) -> Dict[str, int]:
         return read_stats(self.stats)

@@ -10,6 +10,30 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace: [header words | item costs | item order | pooled queries].
+struct WsLayout {
+  size_t cost, perm, qpool, total;
+};
+
+WsLayout ws_layout(int BH, int N, int d) {
+  const size_t Nq = (size_t)(N + 63) / 64;
+  const size_t items = (size_t)sol::forward_items(BH, (int)Nq);
+  WsLayout w;
+  w.cost = sol::kHdrWords * 4;
+  w.perm = round_up(w.cost + 4 * items, 256);
+  w.qpool = round_up(w.perm + 4 * items, 256);
+  w.total = round_up(w.qpool + (size_t)BH * Nq * (size_t)d * 4, 256);
+  return w;
+}
+
+// Items beyond this are taken in sequence order (the one-workgroup sort
+// would cost more than the balance it buys).
+constexpr int kMaxOrderedItems = 1 << 20;
+
+bool use_order(float tau, int nitems) { return !isinf(tau) && nitems > 1 && nitems <= kMaxOrderedItems; }
+
 int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return SOL_EINVAL;
   if (d != 64 && d != 128) return SOL_EUNSUPPORTED;
@@ -21,15 +45,52 @@ int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
   return SOL_OK;
 }
 
+int check_tau(float tau) { return (isnan(tau) || tau < 0.f) ? SOL_EINVAL : SOL_OK; }
+
+// Pooled queries (always), pooled keys/values (if asked), the item order
+// (finite tau) and a clean workspace header.
+hipError_t prepare(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* kpool, float* kpool_out,
+                   float* vmean_out, int BH, int N, int d, float tau, void* ws, hipStream_t s,
+                   const unsigned** perm_out) {
+  const WsLayout w = ws_layout(BH, N, d);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  const int Nq = (N + 63) / 64, Nk = Nq;
+  sol::PoolSet set;
+  set.n = 0;
+  if (kpool_out != nullptr) {
+    set.src[0] = k;
+    set.dst[0] = kpool_out;
+    set.src[1] = v;
+    set.dst[1] = vmean_out;
+    set.n = 2;
+  }
+  set.src[set.n] = q;
+  set.dst[set.n] = reinterpret_cast<float*>(wsb + w.qpool);
+  set.n += 1;
+  hipError_t e = sol::launch_pool(set, BH, N, Nk, d, static_cast<unsigned*>(ws), s);
+  if (e != hipSuccess) return e;
+  *perm_out = nullptr;
+  if (use_order(tau, sol::forward_items(BH, Nq))) {
+    unsigned* perm = reinterpret_cast<unsigned*>(wsb + w.perm);
+    e = sol::launch_plan(reinterpret_cast<const float*>(wsb + w.qpool), kpool,
+                         reinterpret_cast<unsigned*>(wsb + w.cost), perm, BH, Nq, Nk, d, tau,
+                         (float)(1.0 / sqrt((double)d)), s);
+    if (e != hipSuccess) return e;
+    *perm_out = perm;
+  }
+  return hipSuccess;
+}
+
 int check_forward(const void* q, const void* k, const void* v, const float* out, int B, int H, int N,
                   int d, int Bq, int Bk, float tau, unsigned flags, const sol_attn_stats* stats,
                   const float* kpool, const float* vmean, const void* ws, size_t ws_bytes) {
   if (!q || !k || !v || !out || !kpool || !vmean || !ws) return SOL_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(kpool, 16) || !aligned(vmean, 16) || !aligned(ws, 8) || !aligned(stats, 8))
+      !aligned(kpool, 16) || !aligned(vmean, 16) || !aligned(ws, 256) || !aligned(stats, 8))
     return SOL_EINVAL;
-  if (isnan(tau) || tau < 0.f) return SOL_EINVAL;
-  if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY)) return SOL_EINVAL;
+  if (check_tau(tau) != SOL_OK) return SOL_EINVAL;
+  if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED)) return SOL_EINVAL;
+  if ((flags & SOL_F_PLANNED) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
   const int rc = check_sizes(B, H, N, d, Bq, Bk);
   if (rc != SOL_OK) return rc;
   if (ws_bytes < sol_attn_workspace_bytes(B, H, N, d, Bq, Bk)) return SOL_EWORKSPACE;
@@ -44,37 +105,46 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int BH = B * H;
   const int Nq = (N + Bq - 1) / Bq, Nk = (N + Bk - 1) / Bk;
-  unsigned* queue = static_cast<unsigned*>(ws);
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  const WsLayout w = ws_layout(BH, N, d);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  const int nitems = sol::forward_items(BH, Nq);
 
-  hipError_t e;
-  if (flags & SOL_F_POOLED)
-    e = sol::launch_reset(queue, stats, s);
-  else
-    e = sol::launch_pool(k16, v16, kpool, vmean, BH, N, Nk, d, queue, stats, s);
-  if (e != hipSuccess) return SOL_EHIP;
+  const unsigned* perm = nullptr;
+  if (flags & SOL_F_PLANNED) {
+    // the workspace holds sol_attn_plan() of these inputs, as a previous call left it
+    perm = use_order(tau, nitems) ? reinterpret_cast<const unsigned*>(wsb + w.perm) : nullptr;
+  } else {
+    const bool pool_kv = !(flags & SOL_F_POOLED);
+    const hipError_t e = prepare(q16, k16, v16, kpool, pool_kv ? kpool : nullptr, pool_kv ? vmean : nullptr, BH, N,
+                                 d, tau, ws, s, &perm);
+    if (e != hipSuccess) return SOL_EHIP;
+  }
 
   sol::FwdParams p;
-  p.q = static_cast<const uint16_t*>(q);
+  p.q = q16;
   p.k = k16;
   p.v = v16;
   p.out = out;
   p.kpool = kpool;
   p.vmean = vmean;
-  p.queue = queue;
+  p.qpool = reinterpret_cast<const float*>(wsb + w.qpool);
+  p.perm = perm;
+  p.hdr = static_cast<unsigned*>(ws);
   p.stats = stats;
   p.bitmap = bitmap;
   p.N = N;
   p.Nq = Nq;
   p.Nk = Nk;
-  p.nitems = sol::forward_items(BH, Nq);
+  p.nitems = nitems;
   p.nwords = (Nk + 31) / 32;
   p.tau = tau;
   p.proxy_scale = (float)(1.0 / sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   p.exact_only = (flags & SOL_F_EXACT_ONLY) ? 1 : 0;
-  e = sol::launch_forward(p, d, s);
+  const hipError_t e = sol::launch_forward(p, d, s);
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 
@@ -84,7 +154,7 @@ extern "C" {
 
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk) {
   if (check_sizes(B, H, N, d, Bq, Bk) != SOL_OK) return 0;
-  return 256;  // queue counter words, padded
+  return ws_layout(B * H, N, d).total;
 }
 
 int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean, int B, int H, int N, int d,
@@ -94,9 +164,27 @@ int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean, int 
   const int rc = check_sizes(B, H, N, d, 64, Bk);
   if (rc != SOL_OK) return rc;
   const int Nk = (N + Bk - 1) / Bk;
-  const hipError_t e = sol::launch_pool(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                                        kpool, vmean, B * H, N, Nk, d, nullptr, nullptr,
-                                        reinterpret_cast<hipStream_t>(stream));
+  sol::PoolSet set;
+  set.src[0] = static_cast<const uint16_t*>(k);
+  set.dst[0] = kpool;
+  set.src[1] = static_cast<const uint16_t*>(v);
+  set.dst[1] = vmean;
+  set.n = 2;
+  const hipError_t e = sol::launch_pool(set, B * H, N, Nk, d, nullptr, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SOL_OK : SOL_EHIP;
+}
+
+int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, float tau,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kpool || !workspace) return SOL_EINVAL;
+  if (!aligned(q, 16) || !aligned(kpool, 16) || !aligned(workspace, 256)) return SOL_EINVAL;
+  if (check_tau(tau) != SOL_OK) return SOL_EINVAL;
+  const int rc = check_sizes(B, H, N, d, Bq, Bk);
+  if (rc != SOL_OK) return rc;
+  if (workspace_bytes < sol_attn_workspace_bytes(B, H, N, d, Bq, Bk)) return SOL_EWORKSPACE;
+  const unsigned* perm = nullptr;
+  const hipError_t e = prepare(static_cast<const uint16_t*>(q), nullptr, nullptr, kpool, nullptr, nullptr, B * H, N,
+                               d, tau, workspace, reinterpret_cast<hipStream_t>(stream), &perm);
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 
@@ -119,7 +207,8 @@ int sol_attn_forward_debug(const void* q, const void* k, const void* v, float* o
 const char* sol_attn_strerror(int code) {
   switch (code) {
     case SOL_OK: return "success";
-    case SOL_EINVAL: return "invalid argument (null/misaligned pointer, size <= 0, tau NaN or negative, unknown flag)";
+    case SOL_EINVAL:
+      return "invalid argument (null/misaligned pointer, size <= 0, tau NaN or negative, unknown or inconsistent flags)";
     case SOL_EUNSUPPORTED: return "unsupported configuration (d must be 64 or 128, Bq = Bk = 64, N <= SOL_ATTN_MAX_N)";
     case SOL_EWORKSPACE: return "workspace smaller than sol_attn_workspace_bytes()";
     case SOL_EHIP: return "HIP runtime error during launch";

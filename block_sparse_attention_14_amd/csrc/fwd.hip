@@ -15,17 +15,22 @@
 //
 // Work decomposition. A work item is a PAIR of neighbouring 64-row query
 // blocks (b, h, 2p) and (b, h, 2p+1). A persistent grid of 256-thread
-// workgroups (two per CU) takes items from an atomic ticket counter: per-block
+// workgroups (two per CU) takes items from atomic ticket counters: per-block
 // budgets differ by two orders of magnitude, so a static split would idle CUs.
+// There is one queue per XCD, each over a contiguous head-major range of items
+// (so an XCD's L2 holds the pooled keys and values of few heads at a time);
+// a workgroup whose queue is drained takes from the others. For finite tau
+// the tickets of a queue map to its items through an order computed by the
+// planning kernels (longest first), so no workgroup starts a heavy item late.
 // Pairing halves the pooled-key / pooled-value traffic of routing and
 // correction (one read serves both rows) and lets one K/V tile in LDS serve
 // both blocks whenever both keep it, which neighbours usually do.
 //
 // Per item:
 //   1. both Q tiles arrive through buffer loads (rows past the sequence read
-//      as zero); the pooled queries are reduced from those registers; the
-//      tiles pass through LDS once to become, per wave, the B operand of
-//      S^T = K Q^T (waves 0-1 own block A, waves 2-3 block B, 32 rows each);
+//      as zero) and pass through LDS once to become, per wave, the B operand
+//      of S^T = K Q^T (waves 0-1 own block A, waves 2-3 block B, 32 rows
+//      each); the pooled queries come from the pooling pre-pass;
 //   2. the two fp32 proxy rows are built in LDS from pooled keys, eight lanes
 //      per key block, a batch of loads in flight before any use;
 //   3. per row: max, threshold, skipped scores turned into correction weights
@@ -157,7 +162,8 @@ struct alignas(16) Small {
   float cden[2];
   int cnt[3][4];
   int lastkept[2];
-  int item;
+  int item;  // the item drawn for the next iteration (-1: none left)
+  int last;  // this workgroup finished last
 };
 
 template <int D>
@@ -186,11 +192,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   const int nlast = N - (Nk - 1) * kBlk;
   const float csc = p.scale_log2;
 
+  // Queues: the workgroup starts on its own XCD's queue (workgroups are
+  // dispatched to the XCDs round-robin) and, when that is drained, takes
+  // from the others in turn. Only thread 0 draws; qcur is its position.
+  // ticket() only issues the atomic; take() looks at the result, so the
+  // round trip of a ticket drawn early overlaps other work.
+  const int home = (int)(blockIdx.x % kQueues);
+  int qcur = 0;
+  auto ticket = [&]() -> unsigned { return atomicAdd(p.hdr + kHdrQueue + 32 * ((home + qcur) & (kQueues - 1)), 1u); };
+  auto take = [&](unsigned t) -> int {
+    for (;;) {
+      const int x = (home + qcur) & (kQueues - 1);
+      const int lo = queue_begin(x, p.nitems), n = queue_begin(x + 1, p.nitems) - lo;
+      if (t < (unsigned)n) return lo + (int)t;
+      if (++qcur >= kQueues) return -1;
+      t = ticket();
+    }
+  };
+  // per-workgroup stats, published once at the end (thread 0's registers)
+  unsigned long long st_kept = 0, st_tot = 0, st_pairs = 0;
+  unsigned st_min = 0xffffffffu, st_max = 0u;
+
+  if (tid == 0) sm.item = take(ticket());
+  __syncthreads();
   for (;;) {
-    if (tid == 0) sm.item = (int)atomicAdd(p.queue + kQueueTicket, 1u);
-    __syncthreads();
-    const int item = sm.item;
-    if (item >= p.nitems) break;
+    const int rank = sm.item;
+    if (rank < 0) break;
+    const int item = p.perm ? (int)p.perm[rank] : rank;
     const int bh = item / npairs;  // head-major: neighbouring pairs are consecutive tickets
     const int qA = 2 * (item - bh * npairs);
     const bool hasB = qA + 1 < p.Nq;
@@ -199,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     const int nB = hasB ? min(kBlk, N - (qA + 1) * kBlk) : 0;
     const int nmine = qb ? nB : nA;
 
-    // ---- 1. Q tiles: registers -> pooled queries, LDS -> Q^T operands ----
+    // ---- 1. Q tiles -> LDS -> Q^T operands; pooled queries from the pre-pass ----
     bf16x8 qop[2][NDS];
     {
       constexpr int PER = kBlk * CH / kThreads, RSTEP = kThreads / CH;
@@ -212,38 +240,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int u = 0; u < PER; ++u) qr[blk][u] = ld16(r, qoff, u * RSTEP * D * 2);
       }
-      float* part = reinterpret_cast<float*>(stA + kBlk * G::QS * 2);  // [4 waves][2][D], past Q tile A
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         uint16_t* qd = reinterpret_cast<uint16_t*>(blk ? stB : stA) + (tid / CH) * G::QS + (tid % CH) * 8;
-        float cs[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cs[e] = 0.f;
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          *reinterpret_cast<uint4*>(qd + u * RSTEP * G::QS) = qr[blk][u];
-          const uint4 w = qr[blk][u];
-          cs[0] += bf16lo(w.x); cs[1] += bf16hi(w.x); cs[2] += bf16lo(w.y); cs[3] += bf16hi(w.y);
-          cs[4] += bf16lo(w.z); cs[5] += bf16hi(w.z); cs[6] += bf16lo(w.w); cs[7] += bf16hi(w.w);
-        }
-        // lanes sharing tid % CH hold the same columns of other rows
-#pragma unroll
-        for (int o = CH; o < 64; o <<= 1)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) cs[e] += __shfl_xor(cs[e], o);
-        if (lane < CH) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) part[(wid * 2 + blk) * D + lane * 8 + e] = cs[e];
-        }
+        for (int u = 0; u < PER; ++u) *reinterpret_cast<uint4*>(qd + u * RSTEP * G::QS) = qr[blk][u];
+      }
+      if (tid < 2 * D) {  // pooled queries of the pre-pass
+        const int blk = tid / D, col = tid % D;
+        sm.qbar[blk][col] = (blk == 0 || hasB) ? p.qpool[((size_t)bh * p.Nq + qA + blk) * D + col] : 0.f;
       }
       __syncthreads();
-      if (tid < 2 * D) {
-        const int blk = tid / D, col = tid % D;
-        const int nb = blk ? nB : nA;
-        const float s = (part[(0 * 2 + blk) * D + col] + part[(1 * 2 + blk) * D + col]) +
-                        (part[(2 * 2 + blk) * D + col] + part[(3 * 2 + blk) * D + col]);
-        sm.qbar[blk][col] = nb > 0 ? s / (float)nb : 0.f;
-      }
       const uint16_t* qs = reinterpret_cast<const uint16_t*>(qb ? stB : stA) + (qrow0 + c16) * G::QS + 8 * g;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
@@ -563,6 +570,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     }
 
     // ---- 6. fold exact and corrected terms, normalise, store ----
+    // (the next ticket is drawn first, so the atomic's round trip overlaps the stores)
+    unsigned next = 0;
+    if (tid == 0) next = ticket();
     {
       const float M2 = (qb ? MB : MA) * kLog2e;
       const float cden = sm.cden[qb];
@@ -591,27 +601,57 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       }
     }
 
-    if (p.stats != nullptr && tid == 0) {
-      unsigned long long pairs = 0, kept = nkA, tot = Nk;
+    if (tid == 0) {
       const unsigned long long tokA = (unsigned long long)nkA * kBlk - (sm.lastkept[0] ? kBlk - nlast : 0);
-      pairs += tokA * (unsigned long long)nA;
-      unsigned mn = nkA, mx = nkA;
+      st_pairs += tokA * (unsigned long long)nA;
+      st_kept += nkA;
+      st_tot += Nk;
+      st_min = min(st_min, (unsigned)nkA);
+      st_max = max(st_max, (unsigned)nkA);
       if (hasB) {
         const unsigned long long tokB = (unsigned long long)nkB * kBlk - (sm.lastkept[1] ? kBlk - nlast : 0);
-        pairs += tokB * (unsigned long long)nB;
-        kept += nkB;
-        tot += Nk;
-        mn = min(mn, (unsigned)nkB);
-        mx = max(mx, (unsigned)nkB);
+        st_pairs += tokB * (unsigned long long)nB;
+        st_kept += nkB;
+        st_tot += Nk;
+        st_min = min(st_min, (unsigned)nkB);
+        st_max = max(st_max, (unsigned)nkB);
       }
-      atomicAdd(&p.stats->kept_blocks, kept);
-      atomicAdd(&p.stats->total_blocks, tot);
-      atomicAdd(&p.stats->kept_pairs, pairs);
-      atomicMin(&p.stats->min_kept, mn);
-      atomicMax(&p.stats->max_kept, mx);
     }
     __syncthreads();  // LDS is rewritten by the next item
+    if (tid == 0) sm.item = take(next);
+    __syncthreads();
   }
+
+  // Each workgroup adds its stats once; the last one to finish publishes
+  // them and leaves the header clean (zero tickets, zero counters) for the
+  // next call on this workspace.
+  if (tid == 0) {
+    unsigned long long* acc64 = reinterpret_cast<unsigned long long*>(p.hdr);
+    if (p.stats != nullptr && st_tot != 0) {
+      atomicAdd(acc64 + kHdrKept / 2, st_kept);
+      atomicAdd(acc64 + kHdrTotal / 2, st_tot);
+      atomicAdd(acc64 + kHdrPairs / 2, st_pairs);
+      atomicMin(p.hdr + kHdrMin, st_min);
+      atomicMax(p.hdr + kHdrMax, st_max);
+    }
+    __threadfence();
+    const unsigned done = atomicAdd(p.hdr + kHdrDone, 1u);
+    sm.last = done == gridDim.x - 1;
+    if (sm.last) {
+      __threadfence();
+      if (p.stats != nullptr) {
+        p.stats->kept_blocks = __hip_atomic_load(acc64 + kHdrKept / 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p.stats->total_blocks = __hip_atomic_load(acc64 + kHdrTotal / 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p.stats->kept_pairs = __hip_atomic_load(acc64 + kHdrPairs / 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p.stats->min_kept = __hip_atomic_load(p.hdr + kHdrMin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p.stats->max_kept = __hip_atomic_load(p.hdr + kHdrMax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  __syncthreads();
+  if (sm.last)
+    for (int w = tid; w < kHdrWords; w += kThreads)
+      __hip_atomic_store(p.hdr + w, w == kHdrMin ? 0xffffffffu : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

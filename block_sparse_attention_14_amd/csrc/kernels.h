@@ -8,8 +8,27 @@
 
 namespace sol {
 
-// Work-queue words at the start of the caller's workspace.
-enum { kQueueTicket = 0, kQueueWords = 4 };
+// Words at the start of the caller's workspace. The pooling step zeroes them;
+// the fused kernel's last workgroup publishes the stats and zeroes them again,
+// so a workspace is always clean between calls.
+enum {
+  kHdrKept = 0,         // u64 kept block pairs
+  kHdrTotal = 2,        // u64 block pairs
+  kHdrPairs = 4,        // u64 kept query-key pairs
+  kHdrMin = 6,          // u32 min kept per query block
+  kHdrMax = 7,          // u32 max kept per query block
+  kHdrDone = 8,         // workgroups finished
+  kHdrQueue = 32,       // ticket counter of queue x at word kHdrQueue + 32 x (own 128-byte line)
+  kQueues = 8,          // one queue per XCD
+  kHdrWords = kHdrQueue + 32 * kQueues
+};
+
+// Queue x owns the items (or, with an order, the ranks) [queue_begin(x),
+// queue_begin(x + 1)): a contiguous, head-major range, so the workgroups of one
+// XCD share the pooled keys and values of one or two heads in their L2.
+__host__ __device__ inline int queue_begin(int x, int nitems) {
+  return (int)(((long long)x * nitems) / kQueues);
+}
 
 struct FwdParams {
   const uint16_t* q;     // bf16 [BH][N][d]
@@ -18,8 +37,10 @@ struct FwdParams {
   float* out;            // fp32 [BH][N][d]
   const float* kpool;    // fp32 [BH][Nk][d]
   const float* vmean;    // fp32 [BH][Nk][d]
-  unsigned* queue;       // ticket counter, zero on entry
-  sol_attn_stats* stats; // nullable, reset before the launch
+  const float* qpool;    // fp32 [BH][Nq][d] pooled queries
+  const unsigned* perm;  // nullable: rank -> item (longest first within each queue)
+  unsigned* hdr;         // workspace header (kHdr*), clean on entry
+  sol_attn_stats* stats; // nullable, written by the last workgroup
   uint32_t* bitmap;      // nullable, [BH][Nq][nwords]
   int N, Nq, Nk, nitems, nwords;  // nitems = forward_items(BH, Nq)
   float tau;             // >= 0, may be +inf
@@ -28,15 +49,23 @@ struct FwdParams {
   int exact_only;        // skipped blocks dropped instead of corrected
 };
 
-// Pools k and v per 64-token block; when `queue` is non-null, also clears the
-// forward's queue counter and stats (so the fused kernel that follows on the
-// same stream starts from zero).
-hipError_t launch_pool(const uint16_t* k, const uint16_t* v, float* kpool, float* vmean,
-                       int BH, int N, int Nk, int d, unsigned* queue, sol_attn_stats* stats,
-                       hipStream_t stream);
+// Up to three bf16 [BH][N][d] tensors pooled per 64-token block into fp32
+// [BH][Nk][d] means.
+struct PoolSet {
+  const uint16_t* src[3];
+  float* dst[3];
+  int n;
+};
 
-// Clears the queue counter and stats without pooling.
-hipError_t launch_reset(unsigned* queue, sol_attn_stats* stats, hipStream_t stream);
+// Pools the tensors of `set`; when `hdr` is non-null, also resets the
+// workspace header words.
+hipError_t launch_pool(const PoolSet& set, int BH, int N, int Nk, int d, unsigned* hdr, hipStream_t stream);
+
+// Per-item cost estimates (union of the kept sets of each pair of query
+// blocks) and their order, longest first within each queue's range:
+// perm[rank] = item, with rank and item in the same queue range.
+hipError_t launch_plan(const float* qpool, const float* kpool, unsigned* cost, unsigned* perm, int BH, int Nq,
+                       int Nk, int d, float tau, float proxy_scale, hipStream_t stream);
 
 // The fused routing + exact + correction kernel (persistent grid).
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t stream);

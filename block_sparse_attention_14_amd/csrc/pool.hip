@@ -4,20 +4,18 @@
 // Attention": mean-pooled blocks; §3 "Approximate correction": pooled keys and
 // summed values, the latter being n_j times the mean stored here).
 //
-// One workgroup per (block j, head) and tensor (grid x = head * Nk + j). Each thread streams 16-byte
-// chunks of rows, the partial sums meet in LDS, and thread c writes column c.
-// The pass is a pure HBM stream: every input byte is read once.
+// One workgroup per (block j, head) and tensor (grid x = head * Nk + j, grid y
+// = tensor). Each thread streams 16-byte chunks of rows, the partial sums meet
+// in LDS, and thread c writes column c. The pass is a pure HBM stream: every
+// input byte is read once. The forward also pools q here (the pooled queries
+// of the routing step, computed once instead of once per work item).
 #include "common.h"
 #include "kernels.h"
 
 namespace sol {
 
 template <int D>
-__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ k,
-                                                   const uint16_t* __restrict__ v,
-                                                   float* __restrict__ kpool,
-                                                   float* __restrict__ vmean, int N, int Nk,
-                                                   unsigned* queue, sol_attn_stats* stats) {
+__global__ __launch_bounds__(256) void pool_kernel(PoolSet set, int N, int Nk, unsigned* hdr) {
   constexpr int CH = D / 8;      // 16-byte chunks per row
   constexpr int RPP = 256 / CH;  // rows covered per pass
   __shared__ float part[RPP][D];
@@ -26,18 +24,26 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   const int tid = threadIdx.x;
   const int c = tid % CH, r0 = tid / CH;
   const int nj = min(kBlk, N - j * kBlk);
-  const uint16_t* src = (which ? v : k) + ((size_t)bh * N + (size_t)j * kBlk) * D;
-  float* dst = (which ? vmean : kpool) + ((size_t)bh * Nk + j) * D;
+  const uint16_t* src = set.src[which] + ((size_t)bh * N + (size_t)j * kBlk) * D;
+  float* dst = set.dst[which] + ((size_t)bh * Nk + j) * D;
 
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int r = r0; r < nj; r += RPP) {
-    const uint4 u = *reinterpret_cast<const uint4*>(src + (size_t)r * D + c * 8);
-    acc[0] += bf16lo(u.x); acc[1] += bf16hi(u.x);
-    acc[2] += bf16lo(u.y); acc[3] += bf16hi(u.y);
-    acc[4] += bf16lo(u.z); acc[5] += bf16hi(u.z);
-    acc[6] += bf16lo(u.w); acc[7] += bf16hi(u.w);
+  // every row load of the block in flight before the first add
+  constexpr int PASSES = kBlk / RPP;
+  uint4 u[PASSES];
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const int r = r0 + i * RPP;
+    u[i] = r < nj ? *reinterpret_cast<const uint4*>(src + (size_t)r * D + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    acc[0] += bf16lo(u[i].x); acc[1] += bf16hi(u[i].x);
+    acc[2] += bf16lo(u[i].y); acc[3] += bf16hi(u[i].y);
+    acc[4] += bf16lo(u[i].z); acc[5] += bf16hi(u[i].z);
+    acc[6] += bf16lo(u[i].w); acc[7] += bf16hi(u[i].w);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[r0][c * 8 + e] = acc[e];
@@ -49,44 +55,16 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
     dst[tid] = s / (float)nj;
   }
 
-  if (queue != nullptr && j == 0 && bh == 0 && which == 0 && tid == 0) {
-    queue[kQueueTicket] = 0u;
-    if (stats != nullptr) {
-      stats->kept_blocks = 0ull;
-      stats->total_blocks = 0ull;
-      stats->kept_pairs = 0ull;
-      stats->min_kept = 0xffffffffu;
-      stats->max_kept = 0u;
-    }
-  }
+  if (hdr != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int w = tid; w < kHdrWords; w += 256) hdr[w] = w == kHdrMin ? 0xffffffffu : 0u;
 }
 
-__global__ void reset_kernel(unsigned* queue, sol_attn_stats* stats) {
-  if (threadIdx.x == 0) {
-    queue[kQueueTicket] = 0u;
-    if (stats != nullptr) {
-      stats->kept_blocks = 0ull;
-      stats->total_blocks = 0ull;
-      stats->kept_pairs = 0ull;
-      stats->min_kept = 0xffffffffu;
-      stats->max_kept = 0u;
-    }
-  }
-}
-
-hipError_t launch_pool(const uint16_t* k, const uint16_t* v, float* kpool, float* vmean, int BH,
-                       int N, int Nk, int d, unsigned* queue, sol_attn_stats* stats,
-                       hipStream_t stream) {
-  const dim3 grid((unsigned)(BH * Nk), 2), block(256);
+hipError_t launch_pool(const PoolSet& set, int BH, int N, int Nk, int d, unsigned* hdr, hipStream_t stream) {
+  const dim3 grid((unsigned)(BH * Nk), (unsigned)set.n), block(256);
   if (d == 128)
-    hipLaunchKernelGGL(pool_kernel<128>, grid, block, 0, stream, k, v, kpool, vmean, N, Nk, queue, stats);
+    hipLaunchKernelGGL(pool_kernel<128>, grid, block, 0, stream, set, N, Nk, hdr);
   else
-    hipLaunchKernelGGL(pool_kernel<64>, grid, block, 0, stream, k, v, kpool, vmean, N, Nk, queue, stats);
-  return hipGetLastError();
-}
-
-hipError_t launch_reset(unsigned* queue, sol_attn_stats* stats, hipStream_t stream) {
-  hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(64), 0, stream, queue, stats);
+    hipLaunchKernelGGL(pool_kernel<64>, grid, block, 0, stream, set, N, Nk, hdr);
   return hipGetLastError();
 }
 

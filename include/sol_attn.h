@@ -62,10 +62,14 @@ enum {
 
 /* Flags of sol_attn_forward. */
 enum {
-  /* kpool/vmean already hold sol_attn_pool() of these k and v: skip the pre-pass. */
+  /* kpool/vmean already hold sol_attn_pool() of these k and v: skip that pass. */
   SOL_F_POOLED = 1u << 0,
   /* Ablation: drop skipped blocks instead of correcting them (keep-or-drop). */
-  SOL_F_EXACT_ONLY = 1u << 1
+  SOL_F_EXACT_ONLY = 1u << 1,
+  /* The workspace holds sol_attn_plan() of these q and kpool (and this tau),
+   * possibly followed by forwards on the same inputs: launch only the fused
+   * kernel. Requires SOL_F_POOLED. */
+  SOL_F_PLANNED = 1u << 2
 };
 
 /* Largest supported sequence length: the routing rows of Nk = N/64 scores
@@ -82,8 +86,9 @@ typedef struct sol_attn_stats {
   unsigned int max_kept;           /* most kept blocks of any query block */
 } sol_attn_stats;
 
-/* Bytes of device workspace sol_attn_forward needs (work-queue counters).
- * Returns 0 for unsupported sizes. */
+/* Bytes of device workspace sol_attn_forward needs: work-queue and stats
+ * words, one cost and one order slot per work item (a pair of query blocks),
+ * and the fp32 pooled queries [B][H][Nq][d]. Returns 0 for unsupported sizes. */
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
 
 /*
@@ -98,6 +103,21 @@ int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean,
                   int B, int H, int N, int d, int Bk, void* stream);
 
 /*
+ * Planning pass of the forward, callable on its own: pools q per block into
+ * the workspace (the pooled queries of §2 "Block-Sparse Attention"), and for
+ * finite tau estimates every work item's kept budget and orders the items of
+ * each work queue longest first (a scheduling aid; the forward still routes
+ * every block itself
+ * and writes no proxy scores or block indices to device memory). Resets the
+ * workspace's queue and stats words.
+ *   q         bf16 [B][H][N][d]
+ *   kpool     fp32 [B][H][Nk][d], sol_attn_pool() of k
+ *   workspace as for sol_attn_forward
+ */
+int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, float tau,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Sparse attention forward with proxy correction (all sections cited above).
  *   q, k, v   bf16 [B][H][N][d] (read)
  *   out       fp32 [B][H][N][d] (written)
@@ -107,12 +127,16 @@ int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean,
  *   kpool, vmean  fp32 [B][H][Nk][d]; written by the pre-pass unless
  *                 SOL_F_POOLED, in which case they are read as given
  *   workspace device memory of at least sol_attn_workspace_bytes() bytes,
- *             8-byte aligned; its content on entry does not matter
- * Launches the pooling pre-pass (unless SOL_F_POOLED) and one fused kernel:
- * a persistent grid takes query blocks from an atomic queue; for each it
- * computes the proxy row on chip, routes, runs bf16 MFMA attention over the
- * kept key blocks with an online softmax, and folds the skipped blocks'
- * correction into the same accumulator.
+ *             256-byte aligned; its content on entry does not matter unless
+ *             SOL_F_PLANNED is set. Every forward leaves its queue and stats
+ *             words zeroed.
+ * Launches the pooling pass (k and v unless SOL_F_POOLED; q always), the
+ * planning kernels (finite tau), and one fused kernel; with SOL_F_PLANNED only
+ * the fused kernel. The fused kernel's persistent grid takes pairs of query
+ * blocks from an atomic queue; for each it computes the proxy rows on chip,
+ * routes, runs bf16 MFMA attention over the kept key blocks with an online
+ * softmax, and folds the skipped blocks' correction into the same
+ * accumulator. Two calls that share a workspace must not overlap in time.
  */
 int sol_attn_forward(const void* q, const void* k, const void* v, float* out,
                      int B, int H, int N, int d, int Bq, int Bk, float tau,

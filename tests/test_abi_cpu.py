@@ -51,7 +51,7 @@ def test_workspace_bytes():
 
 def fwd(**over):
     a = dict(q=P, k=P, v=P, out=P, B=1, H=2, N=1000, d=128, Bq=64, Bk=64, tau=2.0, flags=0, stats=None,
-             kpool=P, vmean=P, ws=P, ws_bytes=256, stream=None)
+             kpool=P, vmean=P, ws=P, ws_bytes=64, stream=None)
     a.update(over)
     return sa.lib().sol_attn_forward(a["q"], a["k"], a["v"], a["out"], a["B"], a["H"], a["N"], a["d"],
                                      a["Bq"], a["Bk"], ctypes.c_float(a["tau"]), ctypes.c_uint(a["flags"]),
@@ -69,6 +69,8 @@ def fwd(**over):
     (dict(q=P + 2), sa.SOL_EINVAL),
     (dict(out=P + 4), sa.SOL_EINVAL),
     (dict(ws=P + 4), sa.SOL_EINVAL),
+    (dict(ws=P + 128), sa.SOL_EINVAL),
+    (dict(flags=sa.SOL_F_PLANNED), sa.SOL_EINVAL),
     (dict(stats=P + 4), sa.SOL_EINVAL),
     (dict(B=0), sa.SOL_EINVAL),
     (dict(H=-1), sa.SOL_EINVAL),
@@ -89,13 +91,31 @@ def test_forward_rejects_before_launch(over, code):
     assert fwd(**over) == code
 
 
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 1, 2, 1000, 128, 64, 64, 2.0, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, None, 1, 2, 1000, 128, 64, 64, 2.0, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, 1, 2, 1000, 128, 64, 64, 2.0, None, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, 1, 2, 1000, 128, 64, 64, 2.0, P + 64, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, 1, 2, 1000, 128, 64, 64, -1.0, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, 1, 2, 1000, 128, 64, 64, float("nan"), P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, 0, 2, 1000, 128, 64, 64, 2.0, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, 1, 2, 1000, 96, 64, 64, 2.0, P, 1 << 30, None), sa.SOL_EUNSUPPORTED),
+    ((P, P, 1, 2, 1000, 128, 64, 32, 2.0, P, 1 << 30, None), sa.SOL_EUNSUPPORTED),
+    ((P, P, 1, 2, 1000, 128, 64, 64, 2.0, P, 64, None), sa.SOL_EWORKSPACE),
+])
+def test_plan_rejects_before_launch(args, code):
+    a = list(args)
+    a[8] = ctypes.c_float(a[8])
+    assert sa.lib().sol_attn_plan(*a) == code
+
+
 def test_debug_requires_bitmap():
     L = sa.lib()
     rc = L.sol_attn_forward_debug(P, P, P, P, 1, 2, 1000, 128, 64, 64, ctypes.c_float(2.0), ctypes.c_uint(0),
-                                  None, P, P, P, 256, None, None)
+                                  None, P, P, P, 64, None, None)
     assert rc == sa.SOL_EINVAL
     rc = L.sol_attn_forward_debug(P, P, P, P, 1, 2, 1000, 128, 64, 64, ctypes.c_float(2.0), ctypes.c_uint(0),
-                                  None, P, P, P, 256, None, P + 2)
+                                  None, P, P, P, 64, None, P + 2)
     assert rc == sa.SOL_EINVAL
 
 

@@ -168,3 +168,43 @@ def test_invalid_arguments_raise():
         r(q, k, v, -1.0)
     with pytest.raises(sa.SolAttnError):
         r(q, k, v, float("nan"))
+
+
+def test_plan_then_planned_forwards_match_one_shot():
+    """sol_attn_pool + sol_attn_plan + forward(POOLED|PLANNED), twice, equals
+    the one-shot forward bit for bit; stats are right on every call (the
+    fused kernel leaves its queue and stat words clean)."""
+    wl = get_workload("image_dit_4k")
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    one = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    ref = one(q, k, v, 4.0).clone()
+    ref_stats = one.read_stats()
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    sa.pool(k, v, kpool=r.kpool, vmean=r.vmean)
+    r.plan(q, 4.0)
+    for _ in range(2):
+        out = r(q, k, v, 4.0, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+        assert r.read_stats() == ref_stats
+    # dense: no order, still one kernel
+    dense_ref = one(q, k, v, INF).clone()
+    r.plan(q, INF)
+    out = r(q, k, v, INF, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), dense_ref.view(torch.int32))
+
+
+def test_garbage_workspace_is_reset():
+    wl = _custom(1000, 128, H=3, seed=21)
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    ref = r(q, k, v, 2.0).clone()
+    stats = r.read_stats()
+    r.workspace.fill_(-1)  # every byte 0xff
+    out = r(q, k, v, 2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    assert r.read_stats() == stats
