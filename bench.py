@@ -5,14 +5,15 @@
 A step is one full pass of the hot path over the video-DiT layer
 (B=1, H=12, 21x30x52 grid -> N=32760, d=128, bf16 inputs resident in HBM):
 the pooling pre-pass plus the fused routing / exact / correction kernel, one
-C-ABI call. The headline tau is 8; taus 2, 4 and +inf (the same kernel run
+C-ABI call. The optional planning stage (sol_attn_plan) is timed alongside
+under "planned" for every tau. The headline tau is 8; taus 2, 4 and +inf (the same kernel run
 dense) are reported alongside. Prints ONE JSON line.
 
 value = dense-equivalent TFLOP/s = 4*B*H*N^2*d / (seconds per call).
 roofline = the fused kernel's own HIP-event time against the bf16 MFMA peak
 (kept work) or the HBM peak (its algorithmic bytes), whichever floor is higher.
-cpu_baseline = the fp64 oracle on this host's cores, on a bounded sample of
-query blocks, extrapolated to a full call.
+cpu_baseline = the fp64 oracle on this host's cores over whole heads, until
+a time budget is spent (the full call when it fits), scaled to a full call.
 """
 from __future__ import annotations
 
@@ -56,7 +57,7 @@ def parse():
     ap.add_argument("--tau", type=float, default=HEADLINE_TAU)
     ap.add_argument("--taus", default="2,4,8,inf", help="taus reported alongside the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle baseline")
     ap.add_argument("--profile-only", action="store_true", help="headline tau only, for profilers")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -103,23 +104,32 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
         ms_call = e0.elapsed_time(e1) / steps
-        # per-kernel split: pool pass (k, v), planning (pooled q + item order),
-        # then the fused kernel alone on the pooled and planned buffers
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-        for a, b, c, e in ev:
+        # per-kernel split of the same call: the pool pass (k, v), then the
+        # fused kernel on the pooled buffers (after its one-workgroup header reset)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for a, b, c in ev:
             a.record(stream)
             sa.pool(k, v, kpool=runner.kpool, vmean=runner.vmean)
             b.record(stream)
-            runner.plan(q, tau)
+            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED)
             c.record(stream)
-            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
-            e.record(stream)
         torch.cuda.synchronize()
-        ms_pool = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev]))
-        ms_plan = float(np.mean([b.elapsed_time(c) for _, b, c, _ in ev]))
-        ms_fwd = float(np.mean([c.elapsed_time(e) for _, _, c, e in ev]))
+        ms_pool = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+        ms_fwd = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
         stats = runner.read_stats()
-        return ms_call, ms_pool, ms_plan, ms_fwd, wall, stats
+        # the optional planning stage (pooled q, item costs, outliers first),
+        # then the fused kernel on the planned order
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(3, steps // 2))]
+        for a, b, c in ev:
+            a.record(stream)
+            runner.plan(q, tau)
+            b.record(stream)
+            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+            c.record(stream)
+        torch.cuda.synchronize()
+        ms_plan = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+        ms_fwd_planned = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+        return ms_call, ms_pool, ms_fwd, ms_plan, ms_fwd_planned, wall, stats
 
     def kv_unique_blocks(tau: float):
         """Key blocks kept by at least one query block, per head (from the exported bitmap)."""
@@ -146,7 +156,8 @@ def main():
     head = None
     for tau in taus:
         steps = args.steps if tau == args.tau else max(3, args.steps // 2)
-        ms_call, ms_pool, ms_plan, ms_fwd, wall, stats = measure(tau, steps, args.warmup if tau == args.tau else 2)
+        ms_call, ms_pool, ms_fwd, ms_plan, ms_fwd_planned, wall, stats = measure(
+            tau, steps, args.warmup if tau == args.tau else 2)
         flops, nbytes = fwd_algorithmic(tau, stats)
         t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
         t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
@@ -154,8 +165,9 @@ def main():
         rec = {
             "ms_per_call": round(ms_call, 4),
             "ms_pool": round(ms_pool, 4),
-            "ms_plan": round(ms_plan, 4),
             "ms_fwd": round(ms_fwd, 4),
+            "planned": {"ms_plan": round(ms_plan, 4), "ms_fwd": round(ms_fwd_planned, 4),
+                        "ms_per_call": round(ms_pool + ms_plan + ms_fwd_planned, 4)},
             "dense_equiv_tflops": round(dense / (ms_call * 1e-3) / 1e12, 1),
             "kept_block_pct": round(kept_pct, 3),
             "kept_token_pct": round(100.0 * stats["kept_pairs"] / (B * H * N * N), 3),
@@ -168,9 +180,9 @@ def main():
         per_tau["inf" if math.isinf(tau) else f"{tau:g}"] = rec
         print(f"[bench] tau={tau:g} {json.dumps(rec)}", file=sys.stderr, flush=True)
         if tau == args.tau:
-            head = (ms_call, ms_pool, ms_plan, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps)
+            head = (ms_call, ms_pool, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps)
 
-    ms_call, ms_pool, ms_plan, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps = head
+    ms_call, ms_pool, ms_fwd, stats, flops, nbytes, t_mfma, t_hbm, kept_pct, wall, steps = head
     bound = "mfma" if t_mfma >= t_hbm else "hbm"
     if bound == "mfma":
         achieved, peak, unit = flops / (ms_fwd * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
@@ -215,10 +227,10 @@ def main():
         "ms_per_call": round(ms_call, 4),
         "kept_block_pct": round(kept_pct, 3),
         "ms_pool": round(ms_pool, 4),
-        "ms_plan": round(ms_plan, 4),
         "ms_fwd": round(ms_fwd, 4),
         "roofline": {
-            "kernel": "fwd_kernel<128> (fused routing + kept MFMA + correction), timed alone",
+            "kernel": "fwd_kernel<128> (fused routing + kept MFMA + correction); HIP events around the "
+                      "fused launch and its one-workgroup header reset",
             "bound": bound,
             "achieved": round(achieved, 1),
             "peak": peak,
@@ -251,38 +263,38 @@ def cpu_model() -> str:
 
 
 def cpu_baseline(wl, x, tau, budget_s):
-    """The fp64 oracle timed on this host on a sample of query blocks, scaled to a full call."""
+    """The fp64 oracle timed on this host: whole heads, in a seeded order,
+    until the time budget is spent (every head when it fits), scaled to a
+    full call."""
     from threadpoolctl import threadpool_info
 
     from oracle import attend_head
     from workloads import bf16_bits_to_f64
 
     rng = np.random.default_rng(123)
-    heads = [(0, h) for h in range(wl.H)]
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
     rng.shuffle(heads)
-    done_blocks = 0
+    done = 0
     t_total = 0.0
-    t_start = time.perf_counter()
     for b, h in heads:
         qh, kh, vh = (bf16_bits_to_f64(x[n][b, h]) for n in "qkv")
-        blocks = sorted(rng.choice(wl.Nq, size=min(64, wl.Nq), replace=False).tolist())
         t0 = time.perf_counter()
-        attend_head(qh, kh, vh, wl.Bq, wl.Bk, tau, query_blocks=blocks)
+        attend_head(qh, kh, vh, wl.Bq, wl.Bk, tau)
         t_total += time.perf_counter() - t0
-        done_blocks += len(blocks)
-        if time.perf_counter() - t_start > budget_s:
+        done += 1
+        if t_total > budget_s:
             break
-    per_block = t_total / done_blocks
-    full_s = per_block * wl.B * wl.H * wl.Nq
+    full_s = t_total / done * len(heads)
     threads = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    what = "the full call" if done == len(heads) else f"{done} of {len(heads)} heads (seeded order), " \
+                                                      f"extrapolated linearly to the full call"
     return {
         "value": round(wl.dense_flops() / full_s / 1e12, 4),
         "unit": "TFLOP/s (dense-equivalent, 4*B*H*N^2*d per call)",
         "ms_per_call": round(full_s * 1e3, 1),
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done_blocks} of {wl.B * wl.H * wl.Nq} query blocks (64 random blocks per head, seed 123) "
-                  f"at tau={tau:g}: {t_total:.1f} s of oracle time, extrapolated linearly to the full call",
+        "sample": f"{what} at tau={tau:g}: {t_total:.1f} s of fp64 oracle time (numpy, {threads} BLAS threads)",
         "host_cpu": cpu_model(),
     }
 

@@ -47,38 +47,27 @@ int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
 
 int check_tau(float tau) { return (isnan(tau) || tau < 0.f) ? SOL_EINVAL : SOL_OK; }
 
-// Pooled queries (always), pooled keys/values (if asked), the item order
-// (finite tau) and a clean workspace header.
-hipError_t prepare(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* kpool, float* kpool_out,
-                   float* vmean_out, int BH, int N, int d, float tau, void* ws, hipStream_t s,
-                   const unsigned** perm_out) {
+// Planning: pooled queries into the workspace with a clean header, then (for
+// finite tau) the item costs and the order of each queue, else the identity
+// order.
+hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d, float tau, void* ws, hipStream_t s) {
   const WsLayout w = ws_layout(BH, N, d);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   const int Nq = (N + 63) / 64, Nk = Nq;
   sol::PoolSet set;
-  set.n = 0;
-  if (kpool_out != nullptr) {
-    set.src[0] = k;
-    set.dst[0] = kpool_out;
-    set.src[1] = v;
-    set.dst[1] = vmean_out;
-    set.n = 2;
-  }
-  set.src[set.n] = q;
-  set.dst[set.n] = reinterpret_cast<float*>(wsb + w.qpool);
-  set.n += 1;
+  set.src[0] = q;
+  set.dst[0] = reinterpret_cast<float*>(wsb + w.qpool);
+  set.n = 1;
   hipError_t e = sol::launch_pool(set, BH, N, Nk, d, static_cast<unsigned*>(ws), s);
   if (e != hipSuccess) return e;
-  *perm_out = nullptr;
-  if (use_order(tau, sol::forward_items(BH, Nq))) {
-    unsigned* perm = reinterpret_cast<unsigned*>(wsb + w.perm);
-    e = sol::launch_plan(reinterpret_cast<const float*>(wsb + w.qpool), kpool,
-                         reinterpret_cast<unsigned*>(wsb + w.cost), perm, BH, Nq, Nk, d, tau,
-                         (float)(1.0 / sqrt((double)d)), s);
-    if (e != hipSuccess) return e;
-    *perm_out = perm;
-  }
-  return hipSuccess;
+  unsigned* perm = reinterpret_cast<unsigned*>(wsb + w.perm);
+  const int nitems = sol::forward_items(BH, Nq);
+  if (use_order(tau, nitems))
+    return sol::launch_plan(reinterpret_cast<const float*>(wsb + w.qpool), kpool,
+                            reinterpret_cast<unsigned*>(wsb + w.cost), perm, BH, Nq, Nk, d, tau,
+                            (float)(1.0 / sqrt((double)d)), s);
+  // a valid order even so: a planned forward at another tau may still read it
+  return sol::launch_identity_order(perm, nitems, s);
 }
 
 int check_forward(const void* q, const void* k, const void* v, const float* out, int B, int H, int N,
@@ -113,15 +102,22 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   const int nitems = sol::forward_items(BH, Nq);
 
   const unsigned* perm = nullptr;
+  hipError_t e = hipSuccess;
   if (flags & SOL_F_PLANNED) {
     // the workspace holds sol_attn_plan() of these inputs, as a previous call left it
     perm = use_order(tau, nitems) ? reinterpret_cast<const unsigned*>(wsb + w.perm) : nullptr;
+  } else if (flags & SOL_F_POOLED) {
+    e = sol::launch_reset(static_cast<unsigned*>(ws), s);
   } else {
-    const bool pool_kv = !(flags & SOL_F_POOLED);
-    const hipError_t e = prepare(q16, k16, v16, kpool, pool_kv ? kpool : nullptr, pool_kv ? vmean : nullptr, BH, N,
-                                 d, tau, ws, s, &perm);
-    if (e != hipSuccess) return SOL_EHIP;
+    sol::PoolSet set;
+    set.src[0] = k16;
+    set.dst[0] = kpool;
+    set.src[1] = v16;
+    set.dst[1] = vmean;
+    set.n = 2;
+    e = sol::launch_pool(set, BH, N, Nk, d, static_cast<unsigned*>(ws), s);
   }
+  if (e != hipSuccess) return SOL_EHIP;
 
   sol::FwdParams p;
   p.q = q16;
@@ -130,7 +126,6 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   p.out = out;
   p.kpool = kpool;
   p.vmean = vmean;
-  p.qpool = reinterpret_cast<const float*>(wsb + w.qpool);
   p.perm = perm;
   p.hdr = static_cast<unsigned*>(ws);
   p.stats = stats;
@@ -144,7 +139,7 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   p.proxy_scale = (float)(1.0 / sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   p.exact_only = (flags & SOL_F_EXACT_ONLY) ? 1 : 0;
-  const hipError_t e = sol::launch_forward(p, d, s);
+  e = sol::launch_forward(p, d, s);
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 
@@ -182,9 +177,8 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
   const int rc = check_sizes(B, H, N, d, Bq, Bk);
   if (rc != SOL_OK) return rc;
   if (workspace_bytes < sol_attn_workspace_bytes(B, H, N, d, Bq, Bk)) return SOL_EWORKSPACE;
-  const unsigned* perm = nullptr;
-  const hipError_t e = prepare(static_cast<const uint16_t*>(q), nullptr, nullptr, kpool, nullptr, nullptr, B * H, N,
-                               d, tau, workspace, reinterpret_cast<hipStream_t>(stream), &perm);
+  const hipError_t e = plan_impl(static_cast<const uint16_t*>(q), kpool, B * H, N, d, tau, workspace,
+                                 reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 

@@ -46,4 +46,33 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Cross-lane moves inside a row of 16 lanes (DPP, a VALU operand modifier;
+// no LDS round trip). Controls: quad_perm [1,0,3,2] swaps neighbours,
+// quad_perm [2,3,0,1] swaps pairs, row_half_mirror maps lane i of each
+// 8-lane half-row to lane 7 - i, row_ror:8 rotates a row by 8.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRor8 = 0x128;  // row_ror:8, lane i of a row of 16 reads lane i ^ 8
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets it.
+// After the two quad steps all four lanes of a quad hold the same value, so
+// the mirror step adds the other quad's sum.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  return x;
+}
+
 }  // namespace sol

@@ -21,7 +21,9 @@
 // (so an XCD's L2 holds the pooled keys and values of few heads at a time);
 // a workgroup whose queue is drained takes from the others. For finite tau
 // the tickets of a queue map to its items through an order computed by the
-// planning kernels (longest first), so no workgroup starts a heavy item late.
+// planning kernels: the few items far above the queue's mean cost first, the
+// rest in sequence, so no workgroup starts a heavy item late and neighbouring
+// blocks (which keep overlapping key blocks) still share K/V tiles in L2.
 // Pairing halves the pooled-key / pooled-value traffic of routing and
 // correction (one read serves both rows) and lets one K/V tile in LDS serve
 // both blocks whenever both keep it, which neighbours usually do.
@@ -30,14 +32,16 @@
 //   1. both Q tiles arrive through buffer loads (rows past the sequence read
 //      as zero) and pass through LDS once to become, per wave, the B operand
 //      of S^T = K Q^T (waves 0-1 own block A, waves 2-3 block B, 32 rows
-//      each); the pooled queries come from the pooling pre-pass;
+//      each); the pooled queries are summed from the same registers;
 //   2. the two fp32 proxy rows are built in LDS from pooled keys, eight lanes
-//      per key block, a batch of loads in flight before any use;
+//      per key block (their partial dot products meet through DPP moves), a
+//      batch of loads in flight before any use;
 //   3. per row: max, threshold, skipped scores turned into correction weights
 //      n_j e^{s_j - M}; a ballot/prefix pass writes the UNION of the two kept
 //      lists (ascending, 2-bit owner mask) to LDS;
 //   4. the correction numerators sum_j w_j mean(v_j) of both rows, one pass
-//      over the pooled values;
+//      over the pooled values, the next batch of loads in flight while one
+//      is used;
 //   5. for every union entry, the K and V tiles stream from HBM straight into
 //      LDS (buffer loads with an LDS destination, no registers involved),
 //      double-buffered in two stages, one barrier per tile, the next tile in
@@ -154,6 +158,18 @@ __device__ __forceinline__ void dma_tile(unsigned char* stage, rsrc_t rk, rsrc_t
   }
 }
 
+// Sum of a value over the lanes of a wave that share lane % CH (CH = 8 or
+// 16): one DPP step for lane ^ 8 when CH = 8, then permlane swaps for
+// lane ^ 16 and lane ^ 32. Every lane of a group ends with the same sum.
+template <int CH>
+__device__ __forceinline__ float colsum_rows(float x) {
+  if (CH == 8) x += dpp<kDppRor8>(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D>
 struct alignas(16) Small {
   float qbar[2][D];  // pooled queries of blocks A and B
@@ -162,7 +178,7 @@ struct alignas(16) Small {
   float cden[2];
   int cnt[3][4];
   int lastkept[2];
-  int item;  // the item drawn for the next iteration (-1: none left)
+  int item;  // the item of the next iteration (-1: none left)
   int last;  // this workgroup finished last
 };
 
@@ -213,12 +229,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   unsigned long long st_kept = 0, st_tot = 0, st_pairs = 0;
   unsigned st_min = 0xffffffffu, st_max = 0u;
 
-  if (tid == 0) sm.item = take(ticket());
+  // (an order entry out of range, possible only with a workspace that was
+  // never planned, ends this workgroup's work instead of being followed)
+  auto item_of = [&](int rank) {
+    const unsigned it = rank < 0 ? ~0u : (p.perm ? p.perm[rank] : (unsigned)rank);
+    return it < (unsigned)p.nitems ? (int)it : -1;
+  };
+  if (tid == 0) sm.item = item_of(take(ticket()));
   __syncthreads();
   for (;;) {
-    const int rank = sm.item;
-    if (rank < 0) break;
-    const int item = p.perm ? (int)p.perm[rank] : rank;
+    const int item = sm.item;
+    if (item < 0) break;
     const int bh = item / npairs;  // head-major: neighbouring pairs are consecutive tickets
     const int qA = 2 * (item - bh * npairs);
     const bool hasB = qA + 1 < p.Nq;
@@ -227,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     const int nB = hasB ? min(kBlk, N - (qA + 1) * kBlk) : 0;
     const int nmine = qb ? nB : nA;
 
-    // ---- 1. Q tiles -> LDS -> Q^T operands; pooled queries from the pre-pass ----
+    // ---- 1. Q tiles -> LDS -> Q^T operands; pooled queries from the same registers ----
     bf16x8 qop[2][NDS];
     {
       constexpr int PER = kBlk * CH / kThreads, RSTEP = kThreads / CH;
@@ -240,17 +261,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int u = 0; u < PER; ++u) qr[blk][u] = ld16(r, qoff, u * RSTEP * D * 2);
       }
+      float* part = reinterpret_cast<float*>(stA + kBlk * G::QS * 2);  // [4 waves][2][D], past Q tile A
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         uint16_t* qd = reinterpret_cast<uint16_t*>(blk ? stB : stA) + (tid / CH) * G::QS + (tid % CH) * 8;
+        float cs[8];
 #pragma unroll
-        for (int u = 0; u < PER; ++u) *reinterpret_cast<uint4*>(qd + u * RSTEP * G::QS) = qr[blk][u];
-      }
-      if (tid < 2 * D) {  // pooled queries of the pre-pass
-        const int blk = tid / D, col = tid % D;
-        sm.qbar[blk][col] = (blk == 0 || hasB) ? p.qpool[((size_t)bh * p.Nq + qA + blk) * D + col] : 0.f;
+        for (int e = 0; e < 8; ++e) cs[e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          *reinterpret_cast<uint4*>(qd + u * RSTEP * G::QS) = qr[blk][u];
+          const uint4 w = qr[blk][u];
+          cs[0] += bf16lo(w.x); cs[1] += bf16hi(w.x); cs[2] += bf16lo(w.y); cs[3] += bf16hi(w.y);
+          cs[4] += bf16lo(w.z); cs[5] += bf16hi(w.z); cs[6] += bf16lo(w.w); cs[7] += bf16hi(w.w);
+        }
+        // lanes l, l ^ 16, l ^ 32, l ^ 48 (and l ^ 8 when a row has 8 chunks)
+        // hold the same columns of other rows
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] = colsum_rows<CH>(cs[e]);
+        if (lane < CH) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part[(wid * 2 + blk) * D + lane * 8 + e] = cs[e];
+        }
       }
       __syncthreads();
+      if (tid < 2 * D) {
+        const int blk = tid / D, col = tid % D;
+        const int nb = blk ? nB : nA;
+        const float sq = (part[(0 * 2 + blk) * D + col] + part[(1 * 2 + blk) * D + col]) +
+                         (part[(2 * 2 + blk) * D + col] + part[(3 * 2 + blk) * D + col]);
+        sm.qbar[blk][col] = nb > 0 ? sq / (float)nb : 0.f;
+      }
       const uint16_t* qs = reinterpret_cast<const uint16_t*>(qb ? stB : stA) + (qrow0 + c16) * G::QS + 8 * g;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
@@ -290,12 +331,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
             a += qa[t].x * x[u][t].x + qa[t].y * x[u][t].y + qa[t].z * x[u][t].z + qa[t].w * x[u][t].w;
             b += qbv[t].x * x[u][t].x + qbv[t].y * x[u][t].y + qbv[t].z * x[u][t].z + qbv[t].w * x[u][t].w;
           }
-          a += __shfl_xor(a, 1);
-          b += __shfl_xor(b, 1);
-          a += __shfl_xor(a, 2);
-          b += __shfl_xor(b, 2);
-          a += __shfl_xor(a, 4);
-          b += __shfl_xor(b, 4);
+          a = sum8(a);  // the 8 lanes of key block j
+          b = sum8(b);
           a *= p.proxy_scale;
           b *= p.proxy_scale;
           if (j < Nk) {
@@ -384,16 +421,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 
     // ---- 4. correction numerators cnum[b][c] = sum_j w_bj vbar_j[c] ----
     {
-      constexpr int C4 = D / 4, JG = kThreads / C4, U = 16;  // 64 KiB of pooled values in flight
+      constexpr int C4 = D / 4, JG = kThreads / C4, U = 8;  // 2 x 32 KiB of pooled values in flight
       const int c4 = tid % C4, jg = tid / C4;
       float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
       if (!p.exact_only && (nkA < Nk || (hasB && nkB < Nk))) {
         const rsrc_t rv = make_rsrc(p.vmean + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
         const uint32_t voff = (jg * D + c4 * 4) * 4;
-        for (int j0 = 0; j0 < Nk; j0 += U * JG) {
-          float4 x[U];
+        // two batches of U pooled values per lane: one in flight while the other is used
+        // (loads past Nk read zero and are never used)
+        auto load = [&](float4 (&x)[U], int j0) {
 #pragma unroll
           for (int u = 0; u < U; ++u) x[u] = ld16f(rv, voff, (uint32_t)(j0 + u * JG) * D * 4);
+        };
+        auto use = [&](const float4 (&x)[U], int j0) {
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             const int j = j0 + u * JG + jg;
@@ -403,6 +443,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
               a1.x += w1 * x[u].x; a1.y += w1 * x[u].y; a1.z += w1 * x[u].z; a1.w += w1 * x[u].w;
             }
           }
+        };
+        float4 x0[U], x1[U];
+        load(x0, 0);
+        for (int j0 = 0; j0 < Nk; j0 += 2 * U * JG) {
+          load(x1, j0 + U * JG);
+          use(x0, j0);
+          if (j0 + U * JG >= Nk) break;
+          if (j0 + 2 * U * JG < Nk) load(x0, j0 + 2 * U * JG);
+          use(x1, j0 + U * JG);
         }
       }
       __syncthreads();  // weights fully read: their space becomes reduction scratch
@@ -420,6 +469,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       if (tid < 2) sm.cden[tid] = (sm.wred[tid][4] + sm.wred[tid][5]) + (sm.wred[tid][6] + sm.wred[tid][7]);
       __syncthreads();  // the tile stages are free again
     }
+
 
     // ---- 5. exact attention over the union list (online softmax, base 2) ----
     f32x4 acc[2][NDT];
@@ -569,10 +619,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       }
     }
 
+    // The next ticket is drawn now, so its round trip overlaps the stores
+    // below; drawing it earlier would tie an item to this workgroup while it
+    // may still spend long on this one, which others could have taken.
+    unsigned next_ticket = 0;
+    if (tid == 0) next_ticket = ticket();
+
     // ---- 6. fold exact and corrected terms, normalise, store ----
-    // (the next ticket is drawn first, so the atomic's round trip overlaps the stores)
-    unsigned next = 0;
-    if (tid == 0) next = ticket();
     {
       const float M2 = (qb ? MB : MA) * kLog2e;
       const float cden = sm.cden[qb];
@@ -618,7 +671,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       }
     }
     __syncthreads();  // LDS is rewritten by the next item
-    if (tid == 0) sm.item = take(next);
+    if (tid == 0) sm.item = item_of(take(next_ticket));
     __syncthreads();
   }
 

@@ -37,8 +37,7 @@ struct FwdParams {
   float* out;            // fp32 [BH][N][d]
   const float* kpool;    // fp32 [BH][Nk][d]
   const float* vmean;    // fp32 [BH][Nk][d]
-  const float* qpool;    // fp32 [BH][Nq][d] pooled queries
-  const unsigned* perm;  // nullable: rank -> item (longest first within each queue)
+  const unsigned* perm;  // nullable: rank -> item, within each queue's range
   unsigned* hdr;         // workspace header (kHdr*), clean on entry
   sol_attn_stats* stats; // nullable, written by the last workgroup
   uint32_t* bitmap;      // nullable, [BH][Nq][nwords]
@@ -61,11 +60,18 @@ struct PoolSet {
 // workspace header words.
 hipError_t launch_pool(const PoolSet& set, int BH, int N, int Nk, int d, unsigned* hdr, hipStream_t stream);
 
+// Resets the workspace header words (one small kernel).
+hipError_t launch_reset(unsigned* hdr, hipStream_t stream);
+
 // Per-item cost estimates (union of the kept sets of each pair of query
-// blocks) and their order, longest first within each queue's range:
+// blocks) and the order of each queue's range: items above twice the queue's
+// mean cost first, longest first, then the rest in sequence.
 // perm[rank] = item, with rank and item in the same queue range.
 hipError_t launch_plan(const float* qpool, const float* kpool, unsigned* cost, unsigned* perm, int BH, int Nq,
                        int Nk, int d, float tau, float proxy_scale, hipStream_t stream);
+
+// perm[i] = i for every item (the order of a plan that does not sort).
+hipError_t launch_identity_order(unsigned* perm, int nitems, hipStream_t stream);
 
 // The fused routing + exact + correction kernel (persistent grid).
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t stream);

@@ -1,4 +1,4 @@
-// Work ordering for the fused kernel: longest items first.
+// Work ordering for the fused kernel: outliers first.
 //
 // The per-query-block budgets of threshold routing vary by two orders of
 // magnitude (page "Sol-Attn: Accelerating Video Generation Inference via
@@ -6,9 +6,9 @@
 // routing": dynamic, query-dependent budgets). A persistent grid that takes
 // items in sequence order ends with a few workgroups finishing the heaviest
 // items while the rest idle. These two small kernels estimate every item's
-// cost (the size of the union of its two blocks' kept lists) and sort the
-// items of each XCD queue by decreasing cost, so the heavy items start first
-// and the queues stay head-major.
+// cost (the size of the union of its two blocks' kept lists) and move the
+// outliers of each XCD queue to its front, longest first, so the heavy items
+// start early while the rest keep their head-major order.
 //
 // The estimate uses bf16 MFMA products of the pooled queries and keys: it
 // only orders work. The fused kernel routes every item itself, in fp32, and
@@ -148,18 +148,36 @@ __global__ __launch_bounds__(256) void plan_kernel(const float* __restrict__ qpo
     cost[(size_t)bh * npairs + q / 2] = cred[0][c16] + cred[1][c16] + cred[2][c16] + cred[3][c16];
 }
 
-// One workgroup per queue: counting sort of the queue's items by decreasing
-// cost (cost <= Nk) into the queue's own range of perm. Items of equal cost
-// keep no particular order.
+// One workgroup per queue. Items whose cost exceeds twice the queue's mean
+// go first, by decreasing cost (a counting sort; equal costs in no particular
+// order); all other items follow in their natural, head-major order. Taking
+// only the outliers out of sequence starts them early enough to keep them off
+// the end of the queue, while neighbouring query blocks, whose kept key
+// blocks overlap, still run side by side and share those tiles in L2.
 __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict__ cost, unsigned* __restrict__ perm,
                                                      int nitems, int Nk) {
-  extern __shared__ unsigned hist[];  // [Nk + 1] counts, then running offsets
+  extern __shared__ unsigned hist[];  // [Nk + 1] counts of the outliers, then running offsets
   __shared__ unsigned part[1024];
+  __shared__ unsigned long long wsum[16];
+  __shared__ unsigned nheavy;
   const int tid = threadIdx.x, nt = blockDim.x;
-  const int lo = queue_begin(blockIdx.x, nitems), hi = queue_begin(blockIdx.x + 1, nitems);
+  const int lo = queue_begin(blockIdx.x, nitems), hi = queue_begin(blockIdx.x + 1, nitems), n = hi - lo;
+
+  // total cost of the queue
+  unsigned long long sum = 0;
+  for (int i = lo + tid; i < hi; i += nt) sum += cost[i];
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if ((tid & 63) == 0) wsum[tid >> 6] = sum;
   for (int b = tid; b <= Nk; b += nt) hist[b] = 0u;
   __syncthreads();
-  for (int i = lo + tid; i < hi; i += nt) atomicAdd(&hist[min(cost[i], (unsigned)Nk)], 1u);
+  unsigned long long total = 0;
+  for (int w = 0; w < nt / 64; ++w) total += wsum[w];
+  auto heavy = [&](unsigned c) { return (unsigned long long)c * (unsigned long long)n > 2ull * total; };
+
+  for (int i = lo + tid; i < hi; i += nt) {
+    const unsigned c = min(cost[i], (unsigned)Nk);
+    if (heavy(c)) atomicAdd(&hist[c], 1u);
+  }
   __syncthreads();
   // exclusive offsets with the highest cost first: position p is bucket Nk - p;
   // thread t owns positions [t*C, (t+1)*C)
@@ -177,6 +195,7 @@ __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict_
     part[tid] += v;
     __syncthreads();
   }
+  if (tid == nt - 1) nheavy = part[tid];
   unsigned run = (unsigned)lo + part[tid] - local;  // exclusive, offset to the queue's range
   for (int k = 0; k < C; ++k) {
     const int pos = tid * C + k;
@@ -187,10 +206,41 @@ __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict_
     }
   }
   __syncthreads();
-  for (int i = lo + tid; i < hi; i += nt) perm[atomicAdd(&hist[min(cost[i], (unsigned)Nk)], 1u)] = (unsigned)i;
+  for (int i = lo + tid; i < hi; i += nt) {
+    const unsigned c = min(cost[i], (unsigned)Nk);
+    if (heavy(c)) perm[atomicAdd(&hist[c], 1u)] = (unsigned)i;
+  }
+
+  // the rest in natural order: thread t owns items [lo + t*CI, lo + (t+1)*CI)
+  const int CI = (n + nt - 1) / nt;
+  const int i0 = lo + tid * CI, i1 = min(hi, i0 + CI);
+  unsigned light = 0;
+  for (int i = i0; i < i1; ++i) light += heavy(min(cost[i], (unsigned)Nk)) ? 0u : 1u;
+  __syncthreads();  // every reader of part is done
+  part[tid] = light;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    const unsigned v = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  unsigned dst = (unsigned)lo + nheavy + part[tid] - light;
+  for (int i = i0; i < i1; ++i)
+    if (!heavy(min(cost[i], (unsigned)Nk))) perm[dst++] = (unsigned)i;
+}
+
+__global__ __launch_bounds__(256) void iota_kernel(unsigned* __restrict__ perm, int nitems) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < nitems) perm[i] = (unsigned)i;
 }
 
 }  // namespace
+
+hipError_t launch_identity_order(unsigned* perm, int nitems, hipStream_t stream) {
+  hipLaunchKernelGGL(iota_kernel, dim3((nitems + 255) / 256), dim3(256), 0, stream, perm, nitems);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const float* qpool, const float* kpool, unsigned* cost, unsigned* perm, int BH, int Nq, int Nk,
                        int d, float tau, float proxy_scale, hipStream_t stream) {

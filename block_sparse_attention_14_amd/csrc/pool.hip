@@ -59,6 +59,15 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolSet set, int N, int Nk, u
     for (int w = tid; w < kHdrWords; w += 256) hdr[w] = w == kHdrMin ? 0xffffffffu : 0u;
 }
 
+__global__ __launch_bounds__(256) void reset_kernel(unsigned* hdr) {
+  for (int w = threadIdx.x; w < kHdrWords; w += 256) hdr[w] = w == kHdrMin ? 0xffffffffu : 0u;
+}
+
+hipError_t launch_reset(unsigned* hdr, hipStream_t stream) {
+  hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(256), 0, stream, hdr);
+  return hipGetLastError();
+}
+
 hipError_t launch_pool(const PoolSet& set, int BH, int N, int Nk, int d, unsigned* hdr, hipStream_t stream) {
   const dim3 grid((unsigned)(BH * Nk), (unsigned)set.n), block(256);
   if (d == 128)

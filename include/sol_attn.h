@@ -66,9 +66,13 @@ enum {
   SOL_F_POOLED = 1u << 0,
   /* Ablation: drop skipped blocks instead of correcting them (keep-or-drop). */
   SOL_F_EXACT_ONLY = 1u << 1,
-  /* The workspace holds sol_attn_plan() of these q and kpool (and this tau),
-   * possibly followed by forwards on the same inputs: launch only the fused
-   * kernel. Requires SOL_F_POOLED. */
+  /* The workspace holds the result of sol_attn_plan() (for these shapes;
+   * ideally for these q, kpool and tau), possibly followed by other forwards
+   * on it: launch only the fused kernel, taking the items in the planned
+   * order. The order only schedules work, so a plan made for other inputs
+   * of the same shapes gives the same result, only scheduled worse. A
+   * workspace that was never planned must not be used with this flag.
+   * Requires SOL_F_POOLED. */
   SOL_F_PLANNED = 1u << 2
 };
 
@@ -76,8 +80,8 @@ enum {
  * and the kept list are held on chip (4096 key blocks). */
 #define SOL_ATTN_MAX_N (4096 * 64)
 
-/* Per-call counters, written by sol_attn_forward into DEVICE memory. All
- * fields are reset at the start of every forward that receives the pointer. */
+/* Per-call counters, written by sol_attn_forward into DEVICE memory: every
+ * field is overwritten when the forward's last workgroup finishes. */
 typedef struct sol_attn_stats {
   unsigned long long kept_blocks;  /* number of kept (i, j) block pairs */
   unsigned long long total_blocks; /* B * H * Nq * Nk */
@@ -86,9 +90,10 @@ typedef struct sol_attn_stats {
   unsigned int max_kept;           /* most kept blocks of any query block */
 } sol_attn_stats;
 
-/* Bytes of device workspace sol_attn_forward needs: work-queue and stats
- * words, one cost and one order slot per work item (a pair of query blocks),
- * and the fp32 pooled queries [B][H][Nq][d]. Returns 0 for unsupported sizes. */
+/* Bytes of device workspace sol_attn_forward and sol_attn_plan need: the
+ * work-queue and stats words, one cost and one order slot per work item (a
+ * pair of query blocks), and the fp32 pooled queries [B][H][Nq][d] of the
+ * planning stage. Returns 0 for unsupported sizes. */
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
 
 /*
@@ -103,13 +108,15 @@ int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean,
                   int B, int H, int N, int d, int Bk, void* stream);
 
 /*
- * Planning pass of the forward, callable on its own: pools q per block into
- * the workspace (the pooled queries of §2 "Block-Sparse Attention"), and for
- * finite tau estimates every work item's kept budget and orders the items of
- * each work queue longest first (a scheduling aid; the forward still routes
- * every block itself
- * and writes no proxy scores or block indices to device memory). Resets the
- * workspace's queue and stats words.
+ * Optional planning stage, for forwards called with SOL_F_PLANNED: pools q
+ * per block into the workspace (the pooled queries of §2 "Block-Sparse
+ * Attention"), and for finite tau estimates every work item's kept budget
+ * (bf16 products of the pooled vectors) and moves the items far above their
+ * work queue's mean budget to the front of that queue, heaviest first. It is
+ * a scheduling aid only: the forward still routes every block itself, in
+ * fp32, and nothing routing-related is written to device memory beyond one
+ * count per item. For tau = +inf (and very large B*H*N) the order is the
+ * identity. Resets the workspace's queue and stats words.
  *   q         bf16 [B][H][N][d]
  *   kpool     fp32 [B][H][Nk][d], sol_attn_pool() of k
  *   workspace as for sol_attn_forward
@@ -129,14 +136,17 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
  *   workspace device memory of at least sol_attn_workspace_bytes() bytes,
  *             256-byte aligned; its content on entry does not matter unless
  *             SOL_F_PLANNED is set. Every forward leaves its queue and stats
- *             words zeroed.
- * Launches the pooling pass (k and v unless SOL_F_POOLED; q always), the
- * planning kernels (finite tau), and one fused kernel; with SOL_F_PLANNED only
- * the fused kernel. The fused kernel's persistent grid takes pairs of query
- * blocks from an atomic queue; for each it computes the proxy rows on chip,
- * routes, runs bf16 MFMA attention over the kept key blocks with an online
- * softmax, and folds the skipped blocks' correction into the same
- * accumulator. Two calls that share a workspace must not overlap in time.
+ *             words clean.
+ * Launches the pooling pass of k and v (unless SOL_F_POOLED, which launches
+ * a one-workgroup reset of the workspace words instead) and one fused kernel;
+ * with SOL_F_PLANNED only the fused kernel. The fused kernel's persistent
+ * grid takes pairs of query blocks from eight atomic queues (one per XCD,
+ * each over a contiguous range of items, stealing from the others once
+ * drained); for each it pools the two query blocks, computes their proxy
+ * rows on chip, routes, runs bf16 MFMA attention over the kept key blocks
+ * with an online softmax, and folds the skipped blocks' correction into the
+ * same accumulator. Two calls that share a workspace must not overlap in
+ * time.
  */
 int sol_attn_forward(const void* q, const void* k, const void* v, float* out,
                      int B, int H, int N, int d, int Bq, int Bk, float tau,

@@ -208,3 +208,19 @@ def test_garbage_workspace_is_reset():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
     assert r.read_stats() == stats
+
+
+@pytest.mark.parametrize("wlname,tau", [("video_dit_32k_imbalance", 8.0), ("video_dit_32k", 8.0), ("image_dit_4k", 2.0)])
+def test_every_row_written(wlname, tau):
+    """Outputs start as NaN: every row of every item must be written, whatever
+    order the planning step picks (outliers first, the rest in sequence)."""
+    wl = get_workload(wlname)
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    out = torch.full((wl.B, wl.H, wl.N, wl.d), float("nan"), dtype=torch.float32, device=q.device)
+    r(q, k, v, tau, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    st = r.read_stats()
+    assert st["total_blocks"] == wl.B * wl.H * wl.Nq * wl.Nk
