@@ -59,8 +59,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle baseline")
     ap.add_argument("--profile-only", action="store_true", help="headline tau only, for profilers")
-    ap.add_argument("--copy-ref-mib", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--copy-ref-mib", type=int, default=512,
+                    help="size of the plain device copy (reference rate, counter calibration, flush buffer)")
     return ap.parse_args()
 
 
@@ -90,46 +90,82 @@ def main():
     dense = wl.dense_flops()
     stream = torch.cuda.current_stream(dev)
 
+    # a plain device copy of known size: the reference rate for the pool pass,
+    # and (when profiling) the calibration of the traffic counters
+    copy_mib = args.copy_ref_mib or 512
+    src = torch.ones(copy_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del dst
+    scratch = src  # rewritten between calls of the flushed run (evicts L2 and the MALL)
+
+    def events(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def elapsed(ev):
+        return [a.elapsed_time(b) for a, b in ev]
+
     def measure(tau: float, steps: int, warmup: int):
         for _ in range(warmup):
             runner(q, k, v, tau, out=out)
         torch.cuda.synchronize()
-        # whole-call timing: one C-ABI call (pool + fused) per step
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # the timed steps: one C-ABI call (pool + fused) each, inputs resident in HBM
+        ev = events(steps)
         t_wall = time.perf_counter()
-        e0.record(stream)
-        for _ in range(steps):
+        for a, b in ev:
+            a.record(stream)
             runner(q, k, v, tau, out=out)
-        e1.record(stream)
+            b.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
-        ms_call = e0.elapsed_time(e1) / steps
+        r = {"call": elapsed(ev)}
+        # the same calls with L2 and the MALL flushed first
+        ev = events(steps)
+        for i, (a, b) in enumerate(ev):
+            scratch.fill_(float(i))
+            a.record(stream)
+            runner(q, k, v, tau, out=out)
+            b.record(stream)
+        torch.cuda.synchronize()
+        r["call_flushed"] = elapsed(ev)
         # per-kernel split of the same call: the pool pass (k, v), then the
         # fused kernel on the pooled buffers (after its one-workgroup header reset)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        for a, b, c in ev:
+        ev1, ev2 = events(steps), events(steps)
+        for (a, b), (c, e) in zip(ev1, ev2):
             a.record(stream)
             sa.pool(k, v, kpool=runner.kpool, vmean=runner.vmean)
             b.record(stream)
-            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED)
             c.record(stream)
+            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED)
+            e.record(stream)
         torch.cuda.synchronize()
-        ms_pool = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-        ms_fwd = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+        r["pool"], r["fwd"] = elapsed(ev1), elapsed(ev2)
         stats = runner.read_stats()
         # the optional planning stage (pooled q, item costs, outliers first),
         # then the fused kernel on the planned order
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(3, steps // 2))]
-        for a, b, c in ev:
+        n = max(3, steps // 2)
+        ev1, ev2 = events(n), events(n)
+        for (a, b), (c, e) in zip(ev1, ev2):
             a.record(stream)
             runner.plan(q, tau)
             b.record(stream)
-            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
             c.record(stream)
+            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+            e.record(stream)
         torch.cuda.synchronize()
-        ms_plan = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-        ms_fwd_planned = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
-        return ms_call, ms_pool, ms_fwd, ms_plan, ms_fwd_planned, wall, stats
+        r["plan"], r["fwd_planned"] = elapsed(ev1), elapsed(ev2)
+        return r, wall, stats
+
+    def pct(xs):
+        return {"median": round(float(np.median(xs)), 4), "p10": round(float(np.percentile(xs, 10)), 4),
+                "p90": round(float(np.percentile(xs, 90)), 4)}
 
     def kv_unique_blocks(tau: float):
         """Key blocks kept by at least one query block, per head (from the exported bitmap)."""
@@ -156,16 +192,21 @@ def main():
     head = None
     for tau in taus:
         steps = args.steps if tau == args.tau else max(3, args.steps // 2)
-        ms_call, ms_pool, ms_fwd, ms_plan, ms_fwd_planned, wall, stats = measure(
-            tau, steps, args.warmup if tau == args.tau else 2)
+        r, wall, stats = measure(tau, steps, args.warmup if tau == args.tau else 2)
+        ms_call = float(np.mean(r["call"]))
+        ms_pool, ms_fwd = float(np.median(r["pool"])), float(np.median(r["fwd"]))
+        ms_plan, ms_fwd_planned = float(np.median(r["plan"])), float(np.median(r["fwd_planned"]))
         flops, nbytes = fwd_algorithmic(tau, stats)
         t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
         t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
         kept_pct = 100.0 * stats["kept_blocks"] / stats["total_blocks"]
         rec = {
             "ms_per_call": round(ms_call, 4),
+            "call_ms": pct(r["call"]),
+            "call_ms_l2_mall_flushed": pct(r["call_flushed"]),
             "ms_pool": round(ms_pool, 4),
             "ms_fwd": round(ms_fwd, 4),
+            "fwd_ms": pct(r["fwd"]),
             "planned": {"ms_plan": round(ms_plan, 4), "ms_fwd": round(ms_fwd_planned, 4),
                         "ms_per_call": round(ms_pool + ms_plan + ms_fwd_planned, 4)},
             "dense_equiv_tflops": round(dense / (ms_call * 1e-3) / 1e12, 1),
@@ -195,16 +236,6 @@ def main():
         if tr.get("kernel_hash") == kernel_hash() and args.workload == "video_dit_32k" and args.tau == 8.0:
             traffic = tr.get("bytes_per_launch")
 
-    if args.copy_ref_mib > 0:
-        # a plain copy of known size: reads and writes exactly copy_ref_mib MiB per launch
-        nel = args.copy_ref_mib * (1 << 20) // 4
-        src = torch.ones(nel, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
     cpu = None
     if not args.no_cpu_baseline and not args.profile_only:
         cpu = cpu_baseline(wl, x, args.tau, args.cpu_seconds)
@@ -228,6 +259,8 @@ def main():
         "kept_block_pct": round(kept_pct, 3),
         "ms_pool": round(ms_pool, 4),
         "ms_fwd": round(ms_fwd, 4),
+        "pool_gbs": per_tau["inf" if math.isinf(args.tau) else f"{args.tau:g}"]["pool_gbs"],
+        "device_copy_gbs": round(copy_gbs, 1),
         "roofline": {
             "kernel": "fwd_kernel<128> (fused routing + kept MFMA + correction); HIP events around the "
                       "fused launch and its one-workgroup header reset",
