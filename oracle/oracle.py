@@ -86,6 +86,40 @@ def route(s: np.ndarray, tau: float):
     return M, keep
 
 
+def gauss_threshold(qbar: np.ndarray, kbar: np.ndarray, d: int, beta: float) -> np.ndarray:
+    """Query-dependent threshold theta_i = mu_i + beta * sigma_i from pooled-key
+    moments (§3 "Dynamic threshold routing": the mean and variance of a proxy
+    row come from first and second moments of the pooled keys, O(d^2) state;
+    App. B "Threshold variance derivation").
+
+    The statistics are over the key blocks j of a row, each block one sample:
+      mu_i      = qbar_i . m_K / sqrt(d),           m_K = mean_j kbar_j
+      sigma_i^2 = qbar_i^T C_K qbar_i / d,          C_K = mean_j (kbar_j - m_K)(kbar_j - m_K)^T
+    (population moments). Nothing of size Nq x Nk is formed.
+    """
+    qbar = np.asarray(qbar, np.float64)
+    kbar = np.asarray(kbar, np.float64)
+    m_k = kbar.mean(axis=0)
+    c = kbar - m_k
+    C_k = (c.T @ c) / kbar.shape[0]
+    mu = (qbar @ m_k) / math.sqrt(d)
+    var = np.einsum("id,de,ie->i", qbar, C_k, qbar) / d
+    return mu + beta * np.sqrt(np.maximum(var, 0.0))
+
+
+def gauss_threshold_diag(qbar: np.ndarray, kbar: np.ndarray, d: int, beta: float) -> np.ndarray:
+    """The diagonal estimator of the same threshold (App. B "Diagonal threshold
+    estimator"): C_K replaced by its diagonal v_K = per-dimension variance of
+    the pooled keys, so sigma_i^2 ~= sum_c qbar_ic^2 v_Kc / d, O(d) per block."""
+    qbar = np.asarray(qbar, np.float64)
+    kbar = np.asarray(kbar, np.float64)
+    m_k = kbar.mean(axis=0)
+    v_k = ((kbar - m_k) ** 2).mean(axis=0)
+    mu = (qbar @ m_k) / math.sqrt(d)
+    var = (qbar ** 2) @ v_k / d
+    return mu + beta * np.sqrt(var)
+
+
 def attend_head(
     q: np.ndarray,
     k: np.ndarray,
@@ -96,6 +130,9 @@ def attend_head(
     keep_override: Optional[np.ndarray] = None,
     query_blocks: Optional[Iterable[int]] = None,
     correction: bool = True,
+    rule: str = "rowmax",
+    beta: float = 0.0,
+    sinks: Optional[tuple] = None,
 ) -> Dict[str, np.ndarray]:
     """Sparse-plus-corrected attention of one head; q, k, v are [N, d].
 
@@ -111,6 +148,11 @@ def attend_head(
     other blocks are NaN and their s/M/keep rows are NaN/False.
     ``correction=False`` drops the skipped blocks instead (the keep-or-drop
     "exact-only" baseline of §4 "Ablations", same selected blocks).
+    ``rule`` picks the threshold: "rowmax" (keep s_ij >= max_j s_ij - tau),
+    "gauss" (keep s_ij >= gauss_threshold, beta the standardized cutoff;
+    tau is ignored) or "gauss_diag" (the diagonal estimator of it).
+    ``sinks`` = (first, count): key blocks first .. first+count-1 are always
+    kept in the exact branch (App. A: text key-value tokens retained as sinks).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -129,7 +171,21 @@ def attend_head(
     M = np.full(Nq, np.nan)
     keep = np.zeros((Nq, Nk), dtype=bool)
     s_sel = proxy_scores(qbar, kbar, d)
-    M_sel, keep_sel = route(s_sel, tau)
+    if rule == "rowmax":
+        M_sel, keep_sel = route(s_sel, tau)
+    elif rule in ("gauss", "gauss_diag"):
+        if not math.isfinite(beta):
+            raise ValueError("beta must be finite")
+        theta = (gauss_threshold if rule == "gauss" else gauss_threshold_diag)(qbar, kbar, d, beta)
+        M_sel = s_sel.max(axis=1) if s_sel.size else np.zeros(len(rows))
+        keep_sel = s_sel >= theta[:, None]
+    else:
+        raise ValueError(f"unknown rule {rule!r}")
+    if sinks is not None and sinks[1] > 0:
+        first, count = sinks
+        if first < 0 or first + count > Nk:
+            raise ValueError("sink blocks out of range")
+        keep_sel[:, first:first + count] = True
     s[rows], M[rows], keep[rows] = s_sel, M_sel, keep_sel
     if keep_override is not None:
         keep[rows] = np.asarray(keep_override, dtype=bool)[rows]

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attend, attend_head, block_means, route
+from oracle import attend, attend_head, block_means, gauss_threshold, gauss_threshold_diag, route
 from oracle.brute import brute_head
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
@@ -277,3 +277,120 @@ def test_exact_only_equals_masked_sdpa(N, Bq, Bk, tau):
     ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=torch.from_numpy(mask))[0, 0]
     np.testing.assert_allclose(r["out"], ref.numpy(), rtol=0, atol=1e-12)
     assert (~r["keep"]).any()
+
+
+# ---------------------------------------------------------------------------
+# Gaussian-calibrated threshold (§3 "Dynamic threshold routing"; App. B
+# "Threshold variance derivation", "Diagonal threshold estimator") and
+# forced-keep sink blocks (App. A)
+# ---------------------------------------------------------------------------
+
+GAUSS_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "gauss_sink_examples.json")
+
+
+@pytest.mark.parametrize("case", json.load(open(GAUSS_GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_gauss_and_sink_worked_examples(case):
+    ex = json.load(open(GAUSS_GOLDEN))
+    N, d = ex["N"], ex["d"]
+    q, k, v = (np.array(ex[n], dtype=np.float64).reshape(N, d) for n in "qkv")
+    sinks = tuple(case["sinks"]) if "sinks" in case else None
+    r = attend_head(q, k, v, ex["Bq"], ex["Bk"], case.get("tau", 0.0), rule=case["rule"],
+                    beta=case.get("beta", 0.0), sinks=sinks)
+    assert r["keep"].tolist() == case["keep"]
+    np.testing.assert_allclose(r["s"][0], [_closed(x) for x in ex["s"]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r["out"].ravel(), _closed(case["out"]), rtol=1e-13, atol=1e-14)
+    if case["rule"] == "gauss":
+        qbar, _ = block_means(q, ex["Bq"])
+        kbar, _ = block_means(k, ex["Bk"])
+        np.testing.assert_allclose(gauss_threshold(qbar, kbar, d, case["beta"]), _closed(case["theta"]),
+                                   rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gauss_threshold_from_moments_equals_row_statistics(seed):
+    """The moment form never builds the proxy row; its mean and population
+    standard deviation must still be those of the row, which numpy computes
+    here directly from the row."""
+    rng = np.random.default_rng(seed)
+    d, Nq, Nk = 16, 9, 37
+    qbar = rand(rng, Nq, d) + 0.5
+    kbar = rand(rng, Nk, d) @ rand(rng, d, d) * 0.3 + rand(rng, d)  # correlated, off-centre
+    s = (qbar @ kbar.T) / math.sqrt(d)
+    for beta in (-1.3, 0.0, 0.7, 2.5):
+        np.testing.assert_allclose(gauss_threshold(qbar, kbar, d, beta), s.mean(axis=1) + beta * s.std(axis=1),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_gauss_diagonal_estimator():
+    """Exact when the pooled keys' covariance is diagonal (columns centred and
+    mutually orthogonal), different otherwise."""
+    d = 4
+    H = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], dtype=np.float64)
+    kbar = np.vstack([H[:, 1:], -H[:, 1:]]) * np.array([1.0, 2.0, 0.5]) + np.array([0.3, -0.2, 0.1])
+    kbar = np.hstack([kbar, np.zeros((8, 1))])  # d = 4: the last dimension never varies
+    c = kbar - kbar.mean(axis=0)
+    cov = c.T @ c / len(kbar)
+    assert np.allclose(cov, np.diag(np.diag(cov)))
+    qbar = np.random.default_rng(3).standard_normal((5, d))
+    for beta in (-1.0, 0.5, 2.0):
+        np.testing.assert_allclose(gauss_threshold_diag(qbar, kbar, d, beta), gauss_threshold(qbar, kbar, d, beta),
+                                   rtol=1e-12, atol=1e-12)
+    kc = kbar.copy()
+    kc[:, 1] += kc[:, 0]  # correlate two dimensions
+    assert not np.allclose(gauss_threshold_diag(qbar, kc, d, 1.0), gauss_threshold(qbar, kc, d, 1.0))
+
+
+def test_gauss_routing_monotone_in_beta_and_dense_limit():
+    rng = np.random.default_rng(11)
+    N, d = 700, 8
+    q, k, v = rand(rng, N, d), rand(rng, N, d), rand(rng, N, d)
+    prev = None
+    for beta in (3.0, 1.0, 0.0, -1.0):
+        keep = attend_head(q, k, v, 64, 64, 0.0, rule="gauss", beta=beta)["keep"]
+        if prev is not None:
+            assert (prev <= keep).all()  # a lower cutoff keeps a superset
+        prev = keep
+    r = attend_head(q, k, v, 64, 64, 0.0, rule="gauss", beta=-1e6)
+    assert r["keep"].all()
+    np.testing.assert_allclose(r["out"], sdpa64(q, k, v), rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        attend_head(q, k, v, 64, 64, 0.0, rule="gauss", beta=math.nan)
+
+
+def test_sinks_are_always_kept_and_all_sinks_is_dense():
+    rng = np.random.default_rng(12)
+    N, d = 640, 8
+    q, k, v = rand(rng, N, d), rand(rng, N, d), rand(rng, N, d)
+    r = attend_head(q, k, v, 64, 64, 0.0, sinks=(2, 3))
+    assert r["keep"][:, 2:5].all()
+    base = attend_head(q, k, v, 64, 64, 0.0)["keep"]
+    assert (r["keep"][:, :2] == base[:, :2]).all() and (r["keep"][:, 5:] == base[:, 5:]).all()
+    rd = attend_head(q, k, v, 64, 64, 0.0, sinks=(0, 10))
+    np.testing.assert_allclose(rd["out"], sdpa64(q, k, v), rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        attend_head(q, k, v, 64, 64, 0.0, sinks=(8, 3))
+
+
+def test_correction_beats_exact_only_on_a_smooth_layer():
+    """§4 "Ablations": with the same selected blocks, the corrected output is
+    closer to dense attention than the exact-only one. A statistical property
+    of smooth activations; pinned on one seeded, video-like layer whose
+    queries, keys and values share a positional component (values that are
+    independent per token have block means near zero, and there the two
+    outputs nearly coincide)."""
+    from workloads.gen import pos_code
+
+    grid, d = (4, 16, 16), 64
+    N = grid[0] * grid[1] * grid[2]
+    P = pos_code(grid, d).astype(np.float64)
+    rng = np.random.default_rng(5)
+    q = rand(rng, N, d) + 3 * P
+    k = rand(rng, N, d) + 3 * P
+    v = rand(rng, N, d) + 3 * P
+    dense = sdpa64(q, k, v)
+    for tau in (0.5, 1.0, 2.0):
+        c = attend_head(q, k, v, 64, 64, tau)["out"]
+        e = attend_head(q, k, v, 64, 64, tau, correction=False)["out"]
+        err_c = np.linalg.norm(c - dense) / np.linalg.norm(dense)
+        err_e = np.linalg.norm(e - dense) / np.linalg.norm(dense)
+        assert err_c < err_e, (tau, err_c, err_e)
