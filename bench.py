@@ -59,6 +59,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle baseline")
     ap.add_argument("--profile-only", action="store_true", help="headline tau only, for profilers")
+    ap.add_argument("--no-ablation", action="store_true", help="skip the correction ablation report")
     ap.add_argument("--copy-ref-mib", type=int, default=512,
                     help="size of the plain device copy (reference rate, counter calibration, flush buffer)")
     return ap.parse_args()
@@ -236,6 +237,40 @@ def main():
         if tr.get("kernel_hash") == kernel_hash() and args.workload == "video_dit_32k" and args.tau == 8.0:
             traffic = tr.get("bytes_per_launch")
 
+    def ablation(wname, taus_ab):
+        """Corrected vs exact-only outputs for the same routing, against this
+        kernel's dense (tau = +inf) output: global relative L2 error and the
+        mean cosine similarity of rows."""
+        wl2 = get_workload(wname)
+        x2 = make_inputs(wl2)
+        q2, k2, v2 = (torch.from_numpy(x2[n].view(np.int16)).to(dev).view(torch.bfloat16) for n in "qkv")
+        r2 = sa.SolAttention(wl2.B, wl2.H, wl2.N, wl2.d, dev)
+        dense_out = r2(q2, k2, v2, math.inf).double()
+        dn = dense_out.norm()
+
+        def metrics(o):
+            o = o.double()
+            cos = torch.nn.functional.cosine_similarity(o.reshape(-1, wl2.d), dense_out.reshape(-1, wl2.d), dim=1)
+            return {"rel_l2": round(float((o - dense_out).norm() / dn), 5), "cos": round(float(cos.mean()), 5)}
+
+        rep_ = {}
+        for tau in taus_ab:
+            c = metrics(r2(q2, k2, v2, tau))
+            kept = r2.read_stats()
+            e = metrics(r2(q2, k2, v2, tau, flags=sa.SOL_F_EXACT_ONLY))
+            rep_[f"{tau:g}"] = {"kept_block_pct": round(100.0 * kept["kept_blocks"] / kept["total_blocks"], 3),
+                                "corrected": c, "exact_only": e}
+        del q2, k2, v2, r2, dense_out
+        torch.cuda.empty_cache()
+        return rep_
+
+    abl = None
+    if not args.no_ablation and not args.profile_only:
+        abl = {"reference": "this kernel at tau = +inf (dense attention)",
+               "video_dit_32k": ablation("video_dit_32k", (2.0, 4.0, 8.0)),
+               "video_dit_32k_smoothv": ablation("video_dit_32k_smoothv", (2.0, 4.0, 8.0))}
+        print(f"[bench] ablation {json.dumps(abl)}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline and not args.profile_only:
         cpu = cpu_baseline(wl, x, args.tau, args.cpu_seconds)
@@ -274,6 +309,7 @@ def main():
             "algorithmic_bytes": nbytes,
         },
         "cpu_baseline": cpu,
+        "correction_ablation": abl,
         "per_tau": per_tau,
         "context": {
             "pages_end_to_end_speedup_video_generation": "2.1x vs dense attention (hardware not stated)",

@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     SOL_F_PLANNED,
     SOL_F_POOLED,
     SOL_OK,
+    SOL_ROUTE_GAUSS,
+    SOL_ROUTE_ROWMAX,
     SolAttnError,
     lib,
     strerror,

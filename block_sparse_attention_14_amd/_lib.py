@@ -17,6 +17,9 @@ SOL_F_POOLED = 1 << 0
 SOL_F_EXACT_ONLY = 1 << 1
 SOL_F_PLANNED = 1 << 2
 
+SOL_ROUTE_ROWMAX = 0
+SOL_ROUTE_GAUSS = 1
+
 SOL_ATTN_MAX_N = 4096 * 64
 
 EXPORTS = (
@@ -24,6 +27,7 @@ EXPORTS = (
     "sol_attn_pool",
     "sol_attn_plan",
     "sol_attn_forward",
+    "sol_attn_forward_ex",
     "sol_attn_forward_debug",
     "sol_attn_strerror",
 )
@@ -42,6 +46,16 @@ class sol_attn_stats(ctypes.Structure):
         ("kept_pairs", ctypes.c_ulonglong),
         ("min_kept", ctypes.c_uint),
         ("max_kept", ctypes.c_uint),
+    ]
+
+
+class sol_attn_route(ctypes.Structure):
+    _fields_ = [
+        ("rule", ctypes.c_int),
+        ("tau", ctypes.c_float),
+        ("beta", ctypes.c_float),
+        ("sink_first", ctypes.c_int),
+        ("sink_count", ctypes.c_int),
     ]
 
 
@@ -74,6 +88,10 @@ def lib() -> ctypes.CDLL:
                 L.sol_attn_plan.restype = _i
                 L.sol_attn_forward.argtypes = _fwd_args
                 L.sol_attn_forward.restype = _i
+                L.sol_attn_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                                  ctypes.POINTER(sol_attn_route), ctypes.c_uint, _vp, _vp, _vp, _vp,
+                                                  ctypes.c_size_t, _vp, _vp]
+                L.sol_attn_forward_ex.restype = _i
                 L.sol_attn_forward_debug.argtypes = _fwd_args + [_vp]
                 L.sol_attn_forward_debug.restype = _i
                 L.sol_attn_strerror.argtypes = [_i]

@@ -108,7 +108,12 @@ class SolAttention:
         self.stats = new_stats(self.device)
 
     def __call__(self, q, k, v, tau: float, flags: int = 0, out: Optional[torch.Tensor] = None,
-                 stats: bool = True, bitmap: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 stats: bool = True, bitmap: Optional[torch.Tensor] = None, beta: Optional[float] = None,
+                 sinks: Optional[Tuple[int, int]] = None) -> torch.Tensor:
+        """Forward on the current stream. ``tau`` is the row-max offset; with
+        ``beta`` set, the Gaussian-calibrated rule (mean + beta * std of each
+        proxy row) routes instead and ``tau`` is ignored. ``sinks`` =
+        (first, count) key blocks that are always kept."""
         shape = (self.B, self.H, self.N, self.d)
         _check_qkv("q", q, shape)
         _check_qkv("k", k, shape)
@@ -118,6 +123,25 @@ class SolAttention:
         if out is None:
             out = torch.empty(shape, dtype=torch.float32, device=self.device)
         _check_f32("out", out, shape, self.device)
+        bm_ptr = None
+        if bitmap is not None:
+            bs = bitmap_shape(self.B, self.H, self.N, self.Bq, self.Bk)
+            if bitmap.dtype != torch.int32 or tuple(bitmap.shape) != bs or not bitmap.is_contiguous() \
+                    or bitmap.device != self.device:
+                raise ValueError(f"bitmap must be a contiguous int32 tensor of shape {bs} on {self.device}")
+            bm_ptr = _ptr(bitmap)
+        if beta is not None or sinks is not None:
+            route = _lib.sol_attn_route(
+                _lib.SOL_ROUTE_GAUSS if beta is not None else _lib.SOL_ROUTE_ROWMAX,
+                float(tau) if beta is None else 0.0, 0.0 if beta is None else float(beta),
+                0 if sinks is None else int(sinks[0]), 0 if sinks is None else int(sinks[1]))
+            rc = lib().sol_attn_forward_ex(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(out), self.B, self.H, self.N, self.d, self.Bq, self.Bk,
+                ctypes.byref(route), ctypes.c_uint(flags), _ptr(self.stats) if stats else None,
+                _ptr(self.kpool), _ptr(self.vmean), _ptr(self.workspace), self.workspace.numel() * 8,
+                _stream(self.device), bm_ptr)
+            check(rc, "sol_attn_forward_ex")
+            return out
         args = (
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), self.B, self.H, self.N, self.d, self.Bq, self.Bk,
             ctypes.c_float(float(tau)), ctypes.c_uint(flags), _ptr(self.stats) if stats else None,
@@ -128,11 +152,7 @@ class SolAttention:
             rc = lib().sol_attn_forward(*args)
             check(rc, "sol_attn_forward")
         else:
-            bs = bitmap_shape(self.B, self.H, self.N, self.Bq, self.Bk)
-            if bitmap.dtype != torch.int32 or tuple(bitmap.shape) != bs or not bitmap.is_contiguous() \
-                    or bitmap.device != self.device:
-                raise ValueError(f"bitmap must be a contiguous int32 tensor of shape {bs} on {self.device}")
-            rc = lib().sol_attn_forward_debug(*args, _ptr(bitmap))
+            rc = lib().sol_attn_forward_debug(*args, bm_ptr)
             check(rc, "sol_attn_forward_debug")
         return out
 
@@ -150,7 +170,8 @@ class SolAttention:
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, Bq: int = 64, Bk: int = 64,
-            flags: int = 0, return_bitmap: bool = False, return_stats: bool = False):
+            flags: int = 0, return_bitmap: bool = False, return_stats: bool = False,
+            beta: Optional[float] = None, sinks: Optional[Tuple[int, int]] = None):
     """One-shot sparse attention forward (allocates its buffers).
 
     Returns out (fp32), plus the kept-block bitmap [B, H, Nq, ceil(Nk/32)]
@@ -158,13 +179,13 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, Bq: i
     """
     _check_qkv("q", q)
     B, H, N, d = q.shape
-    if math.isnan(tau) or tau < 0:
+    if beta is None and (math.isnan(tau) or tau < 0):
         check(_lib.SOL_EINVAL, "sol_attn_forward")
     runner = SolAttention(B, H, N, d, q.device, Bq, Bk)
     bm = None
     if return_bitmap:
         bm = torch.zeros(bitmap_shape(B, H, N, Bq, Bk), dtype=torch.int32, device=q.device)
-    out = runner(q, k, v, tau, flags=flags, bitmap=bm)
+    out = runner(q, k, v, tau, flags=flags, bitmap=bm, beta=beta, sinks=sinks)
     res = [out]
     if return_bitmap:
         res.append(bm)

@@ -47,6 +47,16 @@ int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
 
 int check_tau(float tau) { return (isnan(tau) || tau < 0.f) ? SOL_EINVAL : SOL_OK; }
 
+sol_attn_route rowmax_route(float tau) {
+  sol_attn_route r;
+  r.rule = SOL_ROUTE_ROWMAX;
+  r.tau = tau;
+  r.beta = 0.f;
+  r.sink_first = 0;
+  r.sink_count = 0;
+  return r;
+}
+
 // Planning: pooled queries into the workspace with a clean header, then (for
 // finite tau) the item costs and the order of each queue, else the identity
 // order.
@@ -70,14 +80,30 @@ hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d
   return sol::launch_identity_order(perm, nitems, s);
 }
 
+int check_route(const sol_attn_route& r, int N, int Bk) {
+  if (r.rule == SOL_ROUTE_ROWMAX) {
+    if (check_tau(r.tau) != SOL_OK) return SOL_EINVAL;
+  } else if (r.rule == SOL_ROUTE_GAUSS) {
+    if (!isfinite(r.beta)) return SOL_EINVAL;
+  } else {
+    return SOL_EINVAL;
+  }
+  if (r.sink_count < 0) return SOL_EINVAL;
+  if (r.sink_count > 0) {
+    const long long nk = Bk > 0 ? (N + (long long)Bk - 1) / Bk : 0;
+    if (r.sink_first < 0 || (long long)r.sink_first + r.sink_count > nk) return SOL_EINVAL;
+  }
+  return SOL_OK;
+}
+
 int check_forward(const void* q, const void* k, const void* v, const float* out, int B, int H, int N,
-                  int d, int Bq, int Bk, float tau, unsigned flags, const sol_attn_stats* stats,
+                  int d, int Bq, int Bk, const sol_attn_route& route, unsigned flags, const sol_attn_stats* stats,
                   const float* kpool, const float* vmean, const void* ws, size_t ws_bytes) {
   if (!q || !k || !v || !out || !kpool || !vmean || !ws) return SOL_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
       !aligned(kpool, 16) || !aligned(vmean, 16) || !aligned(ws, 256) || !aligned(stats, 8))
     return SOL_EINVAL;
-  if (check_tau(tau) != SOL_OK) return SOL_EINVAL;
+  if (check_route(route, N, Bk) != SOL_OK) return SOL_EINVAL;
   if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED)) return SOL_EINVAL;
   if ((flags & SOL_F_PLANNED) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
   const int rc = check_sizes(B, H, N, d, Bq, Bk);
@@ -87,9 +113,9 @@ int check_forward(const void* q, const void* k, const void* v, const float* out,
 }
 
 int forward_impl(const void* q, const void* k, const void* v, float* out, int B, int H, int N, int d,
-                 int Bq, int Bk, float tau, unsigned flags, sol_attn_stats* stats, float* kpool,
+                 int Bq, int Bk, const sol_attn_route& route, unsigned flags, sol_attn_stats* stats, float* kpool,
                  float* vmean, void* ws, size_t ws_bytes, void* stream, uint32_t* bitmap) {
-  const int rc = check_forward(q, k, v, out, B, H, N, d, Bq, Bk, tau, flags, stats, kpool, vmean, ws, ws_bytes);
+  const int rc = check_forward(q, k, v, out, B, H, N, d, Bq, Bk, route, flags, stats, kpool, vmean, ws, ws_bytes);
   if (rc != SOL_OK) return rc;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int BH = B * H;
@@ -104,8 +130,8 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   const unsigned* perm = nullptr;
   hipError_t e = hipSuccess;
   if (flags & SOL_F_PLANNED) {
-    // the workspace holds sol_attn_plan() of these inputs, as a previous call left it
-    perm = use_order(tau, nitems) ? reinterpret_cast<const unsigned*>(wsb + w.perm) : nullptr;
+    // the workspace holds a valid order from sol_attn_plan(), as a previous call left it
+    perm = reinterpret_cast<const unsigned*>(wsb + w.perm);
   } else if (flags & SOL_F_POOLED) {
     e = sol::launch_reset(static_cast<unsigned*>(ws), s);
   } else {
@@ -135,7 +161,11 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   p.Nk = Nk;
   p.nitems = nitems;
   p.nwords = (Nk + 31) / 32;
-  p.tau = tau;
+  p.rule = route.rule;
+  p.tau = route.rule == SOL_ROUTE_ROWMAX ? route.tau : 0.f;
+  p.beta = route.rule == SOL_ROUTE_GAUSS ? route.beta : 0.f;
+  p.sink_lo = route.sink_count > 0 ? route.sink_first : 0;
+  p.sink_hi = route.sink_count > 0 ? route.sink_first + route.sink_count : 0;
   p.proxy_scale = (float)(1.0 / sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   p.exact_only = (flags & SOL_F_EXACT_ONLY) ? 1 : 0;
@@ -185,8 +215,18 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
 int sol_attn_forward(const void* q, const void* k, const void* v, float* out, int B, int H, int N, int d,
                      int Bq, int Bk, float tau, unsigned flags, sol_attn_stats* stats, float* kpool,
                      float* vmean, void* workspace, size_t workspace_bytes, void* stream) {
-  return forward_impl(q, k, v, out, B, H, N, d, Bq, Bk, tau, flags, stats, kpool, vmean, workspace,
+  return forward_impl(q, k, v, out, B, H, N, d, Bq, Bk, rowmax_route(tau), flags, stats, kpool, vmean, workspace,
                       workspace_bytes, stream, nullptr);
+}
+
+int sol_attn_forward_ex(const void* q, const void* k, const void* v, float* out, int B, int H, int N, int d,
+                        int Bq, int Bk, const sol_attn_route* route, unsigned flags, sol_attn_stats* stats,
+                        float* kpool, float* vmean, void* workspace, size_t workspace_bytes, void* stream,
+                        uint32_t* kept_bitmap) {
+  if (!route) return SOL_EINVAL;
+  if (kept_bitmap && !aligned(kept_bitmap, 4)) return SOL_EINVAL;
+  return forward_impl(q, k, v, out, B, H, N, d, Bq, Bk, *route, flags, stats, kpool, vmean, workspace,
+                      workspace_bytes, stream, kept_bitmap);
 }
 
 int sol_attn_forward_debug(const void* q, const void* k, const void* v, float* out, int B, int H, int N,
@@ -194,7 +234,7 @@ int sol_attn_forward_debug(const void* q, const void* k, const void* v, float* o
                            float* kpool, float* vmean, void* workspace, size_t workspace_bytes,
                            void* stream, uint32_t* kept_bitmap) {
   if (!kept_bitmap || !aligned(kept_bitmap, 4)) return SOL_EINVAL;
-  return forward_impl(q, k, v, out, B, H, N, d, Bq, Bk, tau, flags, stats, kpool, vmean, workspace,
+  return forward_impl(q, k, v, out, B, H, N, d, Bq, Bk, rowmax_route(tau), flags, stats, kpool, vmean, workspace,
                       workspace_bytes, stream, kept_bitmap);
 }
 
@@ -202,7 +242,8 @@ const char* sol_attn_strerror(int code) {
   switch (code) {
     case SOL_OK: return "success";
     case SOL_EINVAL:
-      return "invalid argument (null/misaligned pointer, size <= 0, tau NaN or negative, unknown or inconsistent flags)";
+      return "invalid argument (null/misaligned pointer, size <= 0, tau NaN or negative, beta not finite, "
+             "unknown rule, sink range out of bounds, unknown or inconsistent flags)";
     case SOL_EUNSUPPORTED: return "unsupported configuration (d must be 64 or 128, Bq = Bk = 64, N <= SOL_ATTN_MAX_N)";
     case SOL_EWORKSPACE: return "workspace smaller than sol_attn_workspace_bytes()";
     case SOL_EHIP: return "HIP runtime error during launch";

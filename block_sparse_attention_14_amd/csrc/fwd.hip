@@ -36,7 +36,9 @@
 //   2. the two fp32 proxy rows are built in LDS from pooled keys, eight lanes
 //      per key block (their partial dot products meet through DPP moves), a
 //      batch of loads in flight before any use;
-//   3. per row: max, threshold, skipped scores turned into correction weights
+//   3. per row: max, threshold (max - tau, or the Gaussian-calibrated
+//      mean + beta std of the row, §3 "Dynamic threshold routing"), forced
+//      sink blocks (App. A), skipped scores turned into correction weights
 //      n_j e^{s_j - M}; a ballot/prefix pass writes the UNION of the two kept
 //      lists (ascending, 2-bit owner mask) to LDS;
 //   4. the correction numerators sum_j w_j mean(v_j) of both rows, one pass
@@ -175,6 +177,7 @@ struct alignas(16) Small {
   float qbar[2][D];  // pooled queries of blocks A and B
   float cnum[2][D];  // correction numerators
   float wred[2][8];
+  float gred[2][8];  // row sums, then squared deviations (Gaussian threshold)
   float cden[2];
   int cnt[3][4];
   int lastkept[2];
@@ -356,11 +359,47 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     const float MA = fmaxf(fmaxf(sm.wred[0][0], sm.wred[0][1]), fmaxf(sm.wred[0][2], sm.wred[0][3]));
     const float MB = fmaxf(fmaxf(sm.wred[1][0], sm.wred[1][1]), fmaxf(sm.wred[1][2], sm.wred[1][3]));
 
+    // thresholds: the row max minus tau, or the Gaussian-calibrated mean +
+    // beta * std of the row (population statistics over the key blocks; the
+    // row is on chip, so both come exactly from it in two passes)
+    float thA = MA - p.tau, thB = MB - p.tau;
+    if (p.rule == SOL_ROUTE_GAUSS) {
+      float sA = 0.f, sB = 0.f;
+      for (int j = tid; j < Nk; j += kThreads) {
+        sA += wrow0[j];
+        sB += wrow1[j];
+      }
+      sA = wave_sum(sA);
+      sB = wave_sum(sB);
+      if (lane == 0) {
+        sm.gred[0][wid] = sA;
+        sm.gred[1][wid] = sB;
+      }
+      __syncthreads();
+      const float inv_nk = 1.f / (float)Nk;
+      const float muA = ((sm.gred[0][0] + sm.gred[0][1]) + (sm.gred[0][2] + sm.gred[0][3])) * inv_nk;
+      const float muB = ((sm.gred[1][0] + sm.gred[1][1]) + (sm.gred[1][2] + sm.gred[1][3])) * inv_nk;
+      float vA = 0.f, vB = 0.f;
+      for (int j = tid; j < Nk; j += kThreads) {
+        const float a = wrow0[j] - muA, b = wrow1[j] - muB;
+        vA += a * a;
+        vB += b * b;
+      }
+      vA = wave_sum(vA);
+      vB = wave_sum(vB);
+      if (lane == 0) {
+        sm.gred[0][4 + wid] = vA;
+        sm.gred[1][4 + wid] = vB;
+      }
+      __syncthreads();
+      thA = muA + p.beta * sqrtf(((sm.gred[0][4] + sm.gred[0][5]) + (sm.gred[0][6] + sm.gred[0][7])) * inv_nk);
+      thB = muB + p.beta * sqrtf(((sm.gred[1][4] + sm.gred[1][5]) + (sm.gred[1][6] + sm.gred[1][7])) * inv_nk);
+    }
+
     // ---- 3. route both rows; weights for skipped blocks; union kept list ----
     int nu = 0, nkA = 0, nkB = 0;
     {
       float wsA = 0.f, wsB = 0.f;
-      const float thA = MA - p.tau, thB = MB - p.tau;
       uint32_t* bmA = p.bitmap ? p.bitmap + (size_t)(bh * p.Nq + qA) * p.nwords : nullptr;
       uint32_t* bmB = (p.bitmap && hasB) ? bmA + p.nwords : nullptr;
       for (int j0 = 0; j0 < Nk; j0 += kThreads) {
@@ -369,14 +408,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         if (j < Nk) {
           const float nj = (float)min(kBlk, N - j * kBlk);
           const float sa = wrow0[j];
-          kA = sa >= thA;
+          const bool sink = (unsigned)(j - p.sink_lo) < (unsigned)(p.sink_hi - p.sink_lo);
+          kA = sa >= thA || sink;
           const float wa = kA ? 0.f : nj * expf(sa - MA);
           wrow0[j] = wa;
           wsA += wa;
           float wb = 0.f;
           if (hasB) {
             const float sb = wrow1[j];
-            kB = sb >= thB;
+            kB = sb >= thB || sink;
             wb = kB ? 0.f : nj * expf(sb - MB);
             wsB += wb;
           }

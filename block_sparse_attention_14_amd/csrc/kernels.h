@@ -42,7 +42,10 @@ struct FwdParams {
   sol_attn_stats* stats; // nullable, written by the last workgroup
   uint32_t* bitmap;      // nullable, [BH][Nq][nwords]
   int N, Nq, Nk, nitems, nwords;  // nitems = forward_items(BH, Nq)
-  float tau;             // >= 0, may be +inf
+  int rule;              // SOL_ROUTE_ROWMAX or SOL_ROUTE_GAUSS
+  float tau;             // ROWMAX: >= 0, may be +inf
+  float beta;            // GAUSS: standardized cutoff, finite
+  int sink_lo, sink_hi;  // key blocks [sink_lo, sink_hi) are always kept
   float proxy_scale;     // 1/sqrt(d)
   float scale_log2;      // log2(e)/sqrt(d)
   int exact_only;        // skipped blocks dropped instead of corrected

@@ -76,6 +76,29 @@ enum {
   SOL_F_PLANNED = 1u << 2
 };
 
+/* Routing rules of sol_attn_forward_ex (§3 "Dynamic threshold routing":
+ * a query-dependent threshold on the block proxy scores s_ij). */
+enum {
+  /* keep key block j of query block i iff s_ij >= max_j s_ij - tau */
+  SOL_ROUTE_ROWMAX = 0,
+  /* keep iff s_ij >= mean_j s_ij + beta * std_j s_ij: the Gaussian-calibrated
+   * threshold with a shared standardized cutoff beta (population statistics
+   * over the key blocks of the row; they equal the pooled-key first and
+   * second moment form of App. B "Threshold variance derivation", and are
+   * computed here from the proxy row, which stays on chip) */
+  SOL_ROUTE_GAUSS = 1
+};
+
+/* Routing of sol_attn_forward_ex, read from HOST memory during the call. */
+typedef struct sol_attn_route {
+  int rule;        /* SOL_ROUTE_ROWMAX or SOL_ROUTE_GAUSS */
+  float tau;       /* ROWMAX: 0 <= tau <= +inf (ignored by GAUSS) */
+  float beta;      /* GAUSS: any finite value (ignored by ROWMAX) */
+  int sink_first;  /* key blocks sink_first .. sink_first + sink_count - 1 are */
+  int sink_count;  /* always kept, computed exactly (App. A: text key-value    */
+                   /* tokens retained as sinks); sink_count = 0: none          */
+} sol_attn_route;
+
 /* Largest supported sequence length: the routing rows of Nk = N/64 scores
  * and the kept list are held on chip (4096 key blocks). */
 #define SOL_ATTN_MAX_N (4096 * 64)
@@ -153,6 +176,23 @@ int sol_attn_forward(const void* q, const void* k, const void* v, float* out,
                      unsigned flags, sol_attn_stats* stats,
                      float* kpool, float* vmean,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sol_attn_forward with a routing rule and forced-keep sink blocks.
+ *   route       host pointer to the routing parameters (not NULL)
+ *   kept_bitmap NULL, or as for sol_attn_forward_debug
+ * All other arguments, the launches and the errors are those of
+ * sol_attn_forward; in addition SOL_EINVAL for an unknown rule, a NaN or
+ * negative tau (ROWMAX), a non-finite beta (GAUSS), or a sink range outside
+ * 0 .. ceil(N/Bk) - 1. sol_attn_forward(..., tau, ...) is this call with
+ * {SOL_ROUTE_ROWMAX, tau, 0, 0, 0}.
+ */
+int sol_attn_forward_ex(const void* q, const void* k, const void* v, float* out,
+                        int B, int H, int N, int d, int Bq, int Bk,
+                        const sol_attn_route* route, unsigned flags, sol_attn_stats* stats,
+                        float* kpool, float* vmean,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        uint32_t* kept_bitmap);
 
 /*
  * sol_attn_forward plus an export of the routing decisions it used: the same

@@ -3,7 +3,8 @@ ABI, run the fp64 oracle on the same bf16 inputs, compare.
 
 Tolerances:
   * kept-block bitmap: exact, except blocks whose fp64 proxy lies within 1e-3
-    of the threshold M_i - tau (either decision is correct there);
+    of the threshold (M_i - tau, or mean_i + beta std_i for the Gaussian
+    rule; either decision is correct there); forced sink blocks exactly kept;
   * output: max |gpu - oracle| <= 2e-2 with the oracle conditioned on the
     GPU's routing (bf16 inputs, fp32 accumulation, unit-scale outputs);
   * stats: exact integer agreement with the exported bitmap.
@@ -17,7 +18,7 @@ import numpy as np
 import torch
 
 import block_sparse_attention_14_amd as sa
-from oracle import attend_head, route_head
+from oracle import attend_head, block_means, gauss_threshold, proxy_scores, route
 from workloads import bf16_bits_to_f64
 
 BITMAP_TIE = 1e-3
@@ -29,36 +30,60 @@ def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
     return t.to(device).view(torch.bfloat16)
 
 
-def run_gpu(qb, kb, vb, tau, flags=0, runner: Optional[sa.SolAttention] = None, device="cuda"):
+def run_gpu(qb, kb, vb, tau, flags=0, runner: Optional[sa.SolAttention] = None, device="cuda", beta=None,
+            sinks=None):
     """Returns (out fp32 numpy, keep bool [B,H,Nq,Nk], stats dict)."""
     B, H, N, d = qb.shape
     q, k, v = (to_device_bf16(x, device) for x in (qb, kb, vb))
     runner = runner or sa.SolAttention(B, H, N, d, device)
     bm = torch.zeros(sa.bitmap_shape(B, H, N), dtype=torch.int32, device=device)
-    out = runner(q, k, v, tau, flags=flags, bitmap=bm)
+    out = runner(q, k, v, tau, flags=flags, bitmap=bm, beta=beta, sinks=sinks)
     torch.cuda.synchronize()
     keep = sa.unpack_bitmap(bm, -(-N // 64))
     return out.cpu().numpy(), keep, runner.read_stats()
 
 
-def check_bitmap(gpu_keep: np.ndarray, s: np.ndarray, M: np.ndarray, keep: np.ndarray, tau: float, where=""):
-    if math.isinf(tau):
+def oracle_route(q, k, tau, beta=None, sinks=None):
+    """fp64 proxy scores, thresholds, keep mask and the forced-sink mask of one head."""
+    d = q.shape[1]
+    qbar, _ = block_means(q, 64)
+    kbar, _ = block_means(k, 64)
+    s = proxy_scores(qbar, kbar, d)
+    if beta is None:
+        M, keep = route(s, tau)
+        theta = M - tau
+    else:
+        theta = gauss_threshold(qbar, kbar, d, beta)
+        keep = s >= theta[:, None]
+    forced = np.zeros_like(keep)
+    if sinks is not None and sinks[1] > 0:
+        forced[:, sinks[0]:sinks[0] + sinks[1]] = True
+    return s, theta, keep | forced, forced
+
+
+def check_bitmap(gpu_keep: np.ndarray, s: np.ndarray, theta: np.ndarray, keep: np.ndarray, forced: np.ndarray,
+                 rowmax: bool, where=""):
+    if not np.isfinite(theta).any() and rowmax:
         assert gpu_keep.all(), f"{where}: tau=inf must keep every block"
         return
-    near = np.abs(s - (M[:, None] - tau)) <= BITMAP_TIE
+    assert gpu_keep[forced].all(), f"{where}: a forced sink block was not kept"
+    near = (np.abs(s - theta[:, None]) <= BITMAP_TIE) & ~forced
     bad = (gpu_keep != keep) & ~near
     assert not bad.any(), f"{where}: {int(bad.sum())} routing decisions differ away from the threshold, " \
                           f"first at {np.argwhere(bad)[:3].tolist()}"
-    assert gpu_keep.sum(axis=1).min() >= 1, f"{where}: a query block kept nothing"
-    # every kept block is within the tie band of the threshold or above it
-    assert (s[gpu_keep] >= (M[:, None] - tau - BITMAP_TIE).repeat(s.shape[1], axis=1)[gpu_keep]).all()
+    if rowmax:
+        assert gpu_keep.sum(axis=1).min() >= 1, f"{where}: a query block kept nothing"
+    # every kept block is forced, or within the tie band of the threshold, or above it
+    above = s >= theta[:, None] - BITMAP_TIE
+    assert (above | forced)[gpu_keep].all()
 
 
-def check_head(qb, kb, vb, out_gpu, keep_gpu, tau, query_blocks: Optional[Iterable[int]] = None, where=""):
+def check_head(qb, kb, vb, out_gpu, keep_gpu, tau, query_blocks: Optional[Iterable[int]] = None, where="",
+               beta=None, sinks=None):
     """Bitmap on every query block of the head; outputs on `query_blocks` (all if None)."""
     q, k, v = (bf16_bits_to_f64(x) for x in (qb, kb, vb))
-    s, M, keep = route_head(q, k, 64, 64, tau)
-    check_bitmap(keep_gpu, s, M, keep, tau, where)
+    s, theta, keep, forced = oracle_route(q, k, tau, beta, sinks)
+    check_bitmap(keep_gpu, s, theta, keep, forced, beta is None, where)
     r = attend_head(q, k, v, 64, 64, tau, keep_override=keep_gpu, query_blocks=query_blocks)
     rows = np.concatenate([np.arange(i * 64, min(q.shape[0], i * 64 + 64)) for i in r["rows"]])
     err = np.abs(out_gpu[rows] - r["out"][rows]).max()

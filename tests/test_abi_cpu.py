@@ -136,3 +136,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def fwd_ex(route, bitmap=None, **over):
+    a = dict(q=P, k=P, v=P, out=P, B=1, H=2, N=1000, d=128, Bq=64, Bk=64, flags=0, stats=None,
+             kpool=P, vmean=P, ws=P, ws_bytes=64, stream=None)
+    a.update(over)
+    rp = None if route is None else ctypes.byref(_lib.sol_attn_route(*route))
+    return sa.lib().sol_attn_forward_ex(a["q"], a["k"], a["v"], a["out"], a["B"], a["H"], a["N"], a["d"],
+                                        a["Bq"], a["Bk"], rp, ctypes.c_uint(a["flags"]), a["stats"], a["kpool"],
+                                        a["vmean"], a["ws"], a["ws_bytes"], a["stream"], bitmap)
+
+
+@pytest.mark.parametrize("route,bitmap,code", [
+    (None, None, sa.SOL_EINVAL),
+    ((2, 1.0, 0.0, 0, 0), None, sa.SOL_EINVAL),                       # unknown rule
+    ((0, -1.0, 0.0, 0, 0), None, sa.SOL_EINVAL),                      # negative tau
+    ((0, math.nan, 0.0, 0, 0), None, sa.SOL_EINVAL),
+    ((1, 0.0, math.inf, 0, 0), None, sa.SOL_EINVAL),                  # beta not finite
+    ((1, 0.0, math.nan, 0, 0), None, sa.SOL_EINVAL),
+    ((0, 1.0, 0.0, 0, -1), None, sa.SOL_EINVAL),                      # negative sink count
+    ((0, 1.0, 0.0, -1, 1), None, sa.SOL_EINVAL),                      # sink range before 0
+    ((0, 1.0, 0.0, 15, 2), None, sa.SOL_EINVAL),                      # past Nk = 16
+    ((0, 1.0, 0.0, 0, 0), P + 2, sa.SOL_EINVAL),                      # misaligned bitmap
+    ((1, 0.0, 1.0, 15, 1), None, sa.SOL_EWORKSPACE),                  # valid route, small workspace
+    ((0, math.inf, 0.0, 0, 16), None, sa.SOL_EWORKSPACE),
+])
+def test_forward_ex_rejects_before_launch(route, bitmap, code):
+    assert fwd_ex(route, bitmap) == code

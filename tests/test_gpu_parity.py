@@ -28,22 +28,25 @@ def _gpu():
     sa.lib()
 
 
-def _report(name, tau, err):
-    print(f"[parity] {name} tau={tau} max_abs_err={err:.3e}", flush=True)
+def _report(name, tag, err):
+    print(f"[parity] {name} {tag} max_abs_err={err:.3e}", flush=True)
 
 
-def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, seed=0):
+def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, seed=0, beta=None, sinks=None):
     x = inputs or make_inputs(wl)
-    out, keep, stats = run_gpu(x["q"], x["k"], x["v"], tau)
+    out, keep, stats = run_gpu(x["q"], x["k"], x["v"], tau, beta=beta, sinks=sinks)
     check_stats(stats, keep, wl.N)
     rng = np.random.default_rng(seed)
     worst = 0.0
+    tag = f"tau={tau}" if beta is None else f"beta={beta}"
+    if sinks is not None:
+        tag += f" sinks={sinks}"
     for b in range(wl.B):
         for h in range(wl.H):
             qbs = None if query_blocks_per_head is None else sample_blocks(wl.Nq, rng, query_blocks_per_head)
             worst = max(worst, check_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], out[b, h], keep[b, h],
-                                          tau, qbs, where=f"{wl.name} b={b} h={h} tau={tau}"))
-    _report(wl.name, tau, worst)
+                                          tau, qbs, where=f"{wl.name} b={b} h={h} {tag}", beta=beta, sinks=sinks))
+    _report(wl.name, tag, worst)
     return out, keep, stats
 
 
@@ -224,3 +227,56 @@ def test_every_row_written(wlname, tau):
     assert bool(torch.isfinite(out).all())
     st = r.read_stats()
     assert st["total_blocks"] == wl.B * wl.H * wl.Nq * wl.Nk
+
+
+# ---------------------------------------------------------------------------
+# Gaussian-calibrated threshold and forced-keep sink blocks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("beta", [-0.5, 0.5, 1.5, 3.0])
+def test_gauss_rule_tiny(beta):
+    _full_parity(get_workload("tiny_fp32"), 0.0, beta=beta)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 65, 1000])
+@pytest.mark.parametrize("beta", [0.0, 2.0])
+def test_gauss_rule_ragged(N, d, beta):
+    _full_parity(_custom(N, d, H=2, seed=N + d + 7), 0.0, beta=beta)
+
+
+def test_gauss_rule_image_and_video(video32k):
+    _full_parity(get_workload("image_dit_4k"), 0.0, beta=2.0)
+    _full_parity(get_workload("video_dit_32k"), 0.0, video32k, query_blocks_per_head=3, seed=5, beta=3.0)
+
+
+@pytest.mark.parametrize("sinks_at", ["start", "end"])
+@pytest.mark.parametrize("N,d", [(1000, 64), (1000, 128), (130, 128)])
+def test_sinks_rowmax(N, d, sinks_at):
+    nk = -(-N // 64)
+    sinks = (0, 2) if sinks_at == "start" else (nk - 2, 2)
+    _full_parity(_custom(N, d, H=2, seed=N + 3), 0.0, sinks=sinks)
+    _full_parity(_custom(N, d, H=2, seed=N + 3), 2.0, sinks=sinks)
+
+
+def test_sinks_with_gauss_rule_and_exact_only():
+    wl = get_workload("tiny_fp32")
+    _full_parity(wl, 0.0, beta=1.0, sinks=(3, 2))
+    x = make_inputs(wl)
+    out, keep, _ = run_gpu(x["q"], x["k"], x["v"], 1.0, flags=sa.SOL_F_EXACT_ONLY, sinks=(0, 1))
+    assert keep[..., 0].all()
+    for h in range(wl.H):
+        q, k, v = (bf16_bits_to_f64(x[n][0, h]) for n in "qkv")
+        r = attend_head(q, k, v, 64, 64, 1.0, keep_override=keep[0, h], correction=False)
+        assert np.abs(out[0, h] - r["out"]).max() <= 2e-2
+
+
+def test_route_arguments_rejected():
+    wl = _custom(1000, 128, H=1)
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    r = sa.SolAttention(1, 1, 1000, 128)
+    for kw in (dict(beta=math.inf), dict(beta=math.nan), dict(sinks=(15, 2)), dict(sinks=(-1, 1)),
+               dict(sinks=(0, -1))):
+        with pytest.raises(sa.SolAttnError):
+            r(q, k, v, 2.0, **kw)

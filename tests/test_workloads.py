@@ -22,6 +22,7 @@ def test_workload_shapes():
         "image_dit_4k": (2, 24, 4096, 128, 64),
         "video_dit_32k": (1, 12, 32760, 128, 512),
         "video_dit_32k_imbalance": (1, 12, 32760, 128, 512),
+        "video_dit_32k_smoothv": (1, 12, 32760, 128, 512),
         "video_dit_119k": (1, 24, 118800, 128, 1857),
     }
     for name, (B, H, N, d, Nq) in expect.items():
@@ -85,4 +86,15 @@ def test_imbalance_construction():
 
 def test_all_workloads_registered():
     assert set(WORKLOADS) == {"tiny_fp32", "image_dit_4k", "video_dit_32k",
-                              "video_dit_32k_imbalance", "video_dit_119k"}
+                              "video_dit_32k_imbalance", "video_dit_32k_smoothv", "video_dit_119k"}
+
+
+def test_smooth_values_share_the_position_code():
+    from workloads.gen import make_head, pos_code
+
+    w = get_workload("video_dit_32k_smoothv")
+    q, k, v = make_head(w, 0, 0)
+    P = pos_code(w.grid, w.d)
+    # v = noise + 3 P: its projection on P is about 3 |P|^2 per token
+    c = float((v.astype(np.float64) * P).sum() / (P * P).sum())
+    assert abs(c - 3.0) < 0.05

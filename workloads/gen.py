@@ -45,6 +45,8 @@ class Workload:
     # heads whose first `sink_blocks` KV blocks get k += 2 * mean_t(q)
     sink_heads: Tuple[int, ...] = ()
     sink_blocks: int = 0
+    # scale of the position code added to v (0: values independent per token)
+    value_locality: float = 0.0
     description: str = ""
 
     @property
@@ -103,6 +105,13 @@ WORKLOADS: Dict[str, Workload] = {
             sink_heads=(0, 1), sink_blocks=4,
             description=("budget-imbalance video-DiT layer, N=32760, heads 0-5 local, "
                          "6-11 diffuse, 4 sink KV blocks on heads 0-1"),
+        ),
+        _wl(
+            name="video_dit_32k_smoothv",
+            B=1, H=12, grid=(21, 30, 52), d=128, dtype="bf16",
+            taus=(2.0, 4.0, 8.0), seed=1005, value_locality=3.0,
+            description=("video-DiT layer, N=32760, values sharing the position code "
+                         "(spatially smooth), for the correction ablation"),
         ),
         _wl(
             name="video_dit_119k",
@@ -201,6 +210,8 @@ def make_head(wl: Workload, b: int, h: int) -> Tuple[np.ndarray, np.ndarray, np.
         P = _pos32(wl.grid, d)
         q += np.float32(alpha) * P
         k += np.float32(alpha) * P
+    if wl.value_locality != 0.0:
+        v += np.float32(wl.value_locality) * _pos32(wl.grid, d)
     if h in wl.sink_heads and wl.sink_blocks > 0:
         shift = (2.0 * q.astype(np.float64).mean(axis=0)).astype(np.float32)
         k[: wl.sink_blocks * wl.Bk] += shift[None, :]
