@@ -14,4 +14,6 @@ from .oracle import (  # noqa: F401
     proxy_scores,
     route,
     route_head,
+    topk_mask,
+    topp_mask,
 )

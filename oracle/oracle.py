@@ -258,3 +258,37 @@ def route_head(q: np.ndarray, k: np.ndarray, Bq: int, Bk: int, tau: float):
     s = proxy_scores(qbar, kbar, d)
     M, keep = route(s, tau)
     return s, M, keep
+
+
+def topk_mask(s: np.ndarray, k: int) -> np.ndarray:
+    """Keep the k highest proxy scores of each row, a fixed budget (§2
+    "Block-Sparse Attention": top-k routing). Equal scores are taken in order
+    of increasing block index. k is clipped to [0, Nk]."""
+    s = np.asarray(s, np.float64)
+    nk = s.shape[1]
+    k = max(0, min(int(k), nk))
+    keep = np.zeros(s.shape, dtype=bool)
+    for i in range(s.shape[0]):
+        order = sorted(range(nk), key=lambda j: (-s[i, j], j))
+        keep[i, order[:k]] = True
+    return keep
+
+
+def topp_mask(s: np.ndarray, p: float) -> np.ndarray:
+    """Keep, per row, the fewest highest-scoring blocks whose share of the
+    row's softmax mass over the proxy scores reaches p (§2 "Block-Sparse
+    Attention": top-p routing, a dynamic budget). Scores are taken from the
+    highest down, equal scores in order of increasing block index; the block
+    at which the running share first reaches p is kept. p <= 0 keeps the top
+    block only; p >= 1 keeps every block."""
+    s = np.asarray(s, np.float64)
+    nk = s.shape[1]
+    keep = np.zeros(s.shape, dtype=bool)
+    for i in range(s.shape[0]):
+        order = sorted(range(nk), key=lambda j: (-s[i, j], j))
+        w = np.exp(s[i, order] - s[i, order[0]])
+        share = np.cumsum(w) / w.sum()
+        reach = np.flatnonzero(share >= p)
+        last = int(reach[0]) if len(reach) else nk - 1
+        keep[i, order[:last + 1]] = True
+    return keep

@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attend, attend_head, block_means, gauss_threshold, gauss_threshold_diag, route
+from oracle import (attend, attend_head, block_means, gauss_threshold, gauss_threshold_diag, route, topk_mask,
+                    topp_mask)
 from oracle.brute import brute_head
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
@@ -394,3 +395,55 @@ def test_correction_beats_exact_only_on_a_smooth_layer():
         err_c = np.linalg.norm(c - dense) / np.linalg.norm(dense)
         err_e = np.linalg.norm(e - dense) / np.linalg.norm(dense)
         assert err_c < err_e, (tau, err_c, err_e)
+
+
+# ---------------------------------------------------------------------------
+# Top-k and top-p masks, the routing baselines of §2 "Block-Sparse Attention"
+# ---------------------------------------------------------------------------
+
+def test_topk_topp_worked_example():
+    """s = [0, 1, 2, 3]: softmax shares e^j / (1 + e + e^2 + e^3), from the top
+    0.6439, 0.2369, 0.0871, 0.0321 (cumulative 0.6439, 0.8808, 0.9679, 1)."""
+    s = np.array([[0.0, 1.0, 2.0, 3.0], [3.0, 2.0, 1.0, 0.0]])
+    assert topk_mask(s, 1).tolist() == [[False, False, False, True], [True, False, False, False]]
+    assert topk_mask(s, 3).tolist() == [[False, True, True, True], [True, True, True, False]]
+    assert topk_mask(s, 0).sum() == 0 and topk_mask(s, 9).all()
+    e = math.e
+    z = 1 + e + e * e + e ** 3
+    top1, top2, top3 = e ** 3 / z, (e ** 3 + e * e) / z, (e ** 3 + e * e + e) / z
+    assert topp_mask(s, top1 - 1e-9)[0].tolist() == [False, False, False, True]
+    assert topp_mask(s, top1 + 1e-9)[0].tolist() == [False, False, True, True]
+    assert topp_mask(s, top2 + 1e-9)[0].tolist() == [False, True, True, True]
+    assert topp_mask(s, top3 + 1e-9)[0].tolist() == [True, True, True, True]
+    assert topp_mask(s, 0.0).sum(axis=1).tolist() == [1, 1]
+    assert topp_mask(s, 1.0).all()
+
+
+def test_topk_ties_by_index_and_budget():
+    s = np.array([[1.0, 2.0, 2.0, 2.0, 0.0]])
+    assert topk_mask(s, 2).tolist() == [[False, True, True, False, False]]
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal((7, 40))
+    for k in (1, 5, 40):
+        m = topk_mask(s, k)
+        assert (m.sum(axis=1) == k).all()
+        # every kept score is at least every dropped one
+        for i in range(7):
+            if k < 40:
+                assert s[i, m[i]].min() >= s[i, ~m[i]].max()
+
+
+def test_topp_is_the_smallest_top_set_reaching_p():
+    rng = np.random.default_rng(6)
+    s = rng.standard_normal((9, 50)) * 2
+    for p in (0.3, 0.7, 0.95):
+        m = topp_mask(s, p)
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        share = (w * m).sum(axis=1) / w.sum(axis=1)
+        assert (share >= p - 1e-12).all()
+        for i in range(9):
+            kept = np.flatnonzero(m[i])
+            assert s[i, kept].min() >= s[i, ~m[i]].max() if (~m[i]).any() else True
+            # dropping the smallest kept block falls below p
+            smallest = kept[np.argmin(s[i, kept])]
+            assert (w[i, kept].sum() - w[i, smallest]) / w[i].sum() < p
