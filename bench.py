@@ -60,6 +60,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle baseline")
     ap.add_argument("--profile-only", action="store_true", help="headline tau only, for profilers")
     ap.add_argument("--no-ablation", action="store_true", help="skip the correction ablation report")
+    ap.add_argument("--no-routing-cost", action="store_true", help="skip the router comparison")
     ap.add_argument("--copy-ref-mib", type=int, default=512,
                     help="size of the plain device copy (reference rate, counter calibration, flush buffer)")
     return ap.parse_args()
@@ -264,6 +265,49 @@ def main():
         torch.cuda.empty_cache()
         return rep_
 
+    def routing_cost(tau, kept_blocks):
+        """The kept-block bitmap from three routers on the same layer: on-chip
+        threshold routing (no proxy map) against top-k and top-p, which pool q,
+        write the full proxy map to device memory and sort each row. top-k is
+        given the threshold rule's mean budget."""
+        mb = sa.MaskBuilder(B, H, N, d, dev)
+        kp, _ = sa.pool(k, v)
+        kk = max(1, round(kept_blocks / (B * H * wl.Nq)))
+
+        def timed(fn, n=10):
+            fn()
+            torch.cuda.synchronize()
+            ev = events(n)
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median(elapsed(ev)))
+
+        res = {}
+        for name, fn in (("threshold_on_chip", lambda: mb.threshold(q, kp, tau=tau)),
+                         ("topk_proxy_map", lambda: mb.topk(q, kp, kk)),
+                         ("topp_proxy_map", lambda: mb.topp(q, kp, 0.9))):
+            ms = timed(fn)
+            kept = int(sa.unpack_bitmap(mb.bitmap, wl.Nk).sum())
+            res[name] = {"ms": round(ms, 4), "kept_block_pct": round(100.0 * kept / (B * H * wl.Nq * wl.Nk), 3)}
+        res["topk_proxy_map"]["k"] = kk
+        res["topp_proxy_map"]["p"] = 0.9
+        res["proxy_map_bytes"] = B * H * wl.Nq * wl.Nk * 4
+        t0 = res["threshold_on_chip"]["ms"]
+        res["speedup_vs_topk"] = round(res["topk_proxy_map"]["ms"] / t0, 2)
+        res["speedup_vs_topp"] = round(res["topp_proxy_map"]["ms"] / t0, 2)
+        res["tau"] = tau
+        del mb
+        torch.cuda.empty_cache()
+        return res
+
+    rcost = None
+    if not args.no_routing_cost and not args.profile_only:
+        rcost = routing_cost(args.tau, stats["kept_blocks"])
+        print(f"[bench] routing_cost {json.dumps(rcost)}", file=sys.stderr, flush=True)
+
     abl = None
     if not args.no_ablation and not args.profile_only:
         abl = {"reference": "this kernel at tau = +inf (dense attention)",
@@ -310,6 +354,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "correction_ablation": abl,
+        "routing_cost": rcost,
         "per_tau": per_tau,
         "context": {
             "pages_end_to_end_speedup_video_generation": "2.1x vs dense attention (hardware not stated)",

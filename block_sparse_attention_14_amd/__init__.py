@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     strerror,
 )
 from .api import (  # noqa: F401
+    MaskBuilder,
     SolAttention,
     bitmap_shape,
     forward,

@@ -29,6 +29,10 @@ EXPORTS = (
     "sol_attn_forward",
     "sol_attn_forward_ex",
     "sol_attn_forward_debug",
+    "sol_attn_mask_workspace_bytes",
+    "sol_attn_mask_threshold",
+    "sol_attn_mask_topk",
+    "sol_attn_mask_topp",
     "sol_attn_strerror",
 )
 
@@ -94,6 +98,16 @@ def lib() -> ctypes.CDLL:
                 L.sol_attn_forward_ex.restype = _i
                 L.sol_attn_forward_debug.argtypes = _fwd_args + [_vp]
                 L.sol_attn_forward_debug.restype = _i
+                L.sol_attn_mask_workspace_bytes.argtypes = [_i] * 6
+                L.sol_attn_mask_workspace_bytes.restype = ctypes.c_size_t
+                L.sol_attn_mask_threshold.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i,
+                                                      ctypes.POINTER(sol_attn_route), _vp, _vp]
+                L.sol_attn_mask_threshold.restype = _i
+                L.sol_attn_mask_topk.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, ctypes.c_size_t, _vp]
+                L.sol_attn_mask_topk.restype = _i
+                L.sol_attn_mask_topp.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp, _vp,
+                                                 ctypes.c_size_t, _vp]
+                L.sol_attn_mask_topp.restype = _i
                 L.sol_attn_strerror.argtypes = [_i]
                 L.sol_attn_strerror.restype = ctypes.c_char_p
                 _lib = L

@@ -45,6 +45,11 @@ def _check_f32(name: str, t: torch.Tensor, shape, device) -> None:
         raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)} on {device}")
 
 
+def _device(device) -> torch.device:
+    dev = torch.device(device)
+    return torch.device("cuda", torch.cuda.current_device()) if dev.index is None else dev
+
+
 def workspace_bytes(B: int, H: int, N: int, d: int, Bq: int = 64, Bk: int = 64) -> int:
     return int(lib().sol_attn_workspace_bytes(B, H, N, d, Bq, Bk))
 
@@ -93,9 +98,7 @@ class SolAttention:
 
     def __init__(self, B: int, H: int, N: int, d: int, device="cuda", Bq: int = 64, Bk: int = 64):
         self.B, self.H, self.N, self.d, self.Bq, self.Bk = B, H, N, d, Bq, Bk
-        self.device = torch.device(device)
-        if self.device.index is None:
-            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.device = _device(device)
         nbytes = workspace_bytes(B, H, N, d, Bq, Bk)
         if nbytes == 0:
             rc = _lib.SOL_EUNSUPPORTED if d > 0 and N > 0 and B > 0 and H > 0 else _lib.SOL_EINVAL
@@ -201,3 +204,46 @@ def unpack_bitmap(words: torch.Tensor, Nk: int):
     w = words.detach().cpu().numpy().view(np.uint32)
     bits = (w[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1
     return bits.reshape(*w.shape[:-1], -1)[..., :Nk].astype(bool)
+
+
+class MaskBuilder:
+    """Routing alone, for one [B, H, N, d] shape: the kept-block bitmap from
+    on-chip threshold routing, or from the top-k / top-p routers that write
+    the full proxy map first. ``kpool`` is sol_attn_pool() of k."""
+
+    def __init__(self, B: int, H: int, N: int, d: int, device="cuda", Bq: int = 64, Bk: int = 64):
+        self.B, self.H, self.N, self.d, self.Bq, self.Bk = B, H, N, d, Bq, Bk
+        self.device = _device(device)
+        nbytes = int(lib().sol_attn_mask_workspace_bytes(B, H, N, d, Bq, Bk))
+        if nbytes == 0:
+            check(_lib.SOL_EUNSUPPORTED, "sol_attn_mask_workspace_bytes")
+        self.workspace = torch.empty(-(-nbytes // 8), dtype=torch.int64, device=self.device)
+        self.bitmap = torch.zeros(bitmap_shape(B, H, N, Bq, Bk), dtype=torch.int32, device=self.device)
+
+    def _common(self, q, kpool):
+        _check_qkv("q", q, (self.B, self.H, self.N, self.d))
+        _check_f32("kpool", kpool, pooled_shape(self.B, self.H, self.N, self.d, self.Bk), self.device)
+        return (_ptr(q), _ptr(kpool), self.B, self.H, self.N, self.d, self.Bq, self.Bk)
+
+    def threshold(self, q, kpool, tau: float = 0.0, beta: Optional[float] = None,
+                  sinks: Optional[Tuple[int, int]] = None) -> torch.Tensor:
+        route = _lib.sol_attn_route(
+            _lib.SOL_ROUTE_GAUSS if beta is not None else _lib.SOL_ROUTE_ROWMAX,
+            float(tau) if beta is None else 0.0, 0.0 if beta is None else float(beta),
+            0 if sinks is None else int(sinks[0]), 0 if sinks is None else int(sinks[1]))
+        rc = lib().sol_attn_mask_threshold(*self._common(q, kpool), ctypes.byref(route), _ptr(self.bitmap),
+                                           _stream(self.device))
+        check(rc, "sol_attn_mask_threshold")
+        return self.bitmap
+
+    def topk(self, q, kpool, k: int) -> torch.Tensor:
+        rc = lib().sol_attn_mask_topk(*self._common(q, kpool), int(k), _ptr(self.bitmap), _ptr(self.workspace),
+                                      self.workspace.numel() * 8, _stream(self.device))
+        check(rc, "sol_attn_mask_topk")
+        return self.bitmap
+
+    def topp(self, q, kpool, p: float) -> torch.Tensor:
+        rc = lib().sol_attn_mask_topp(*self._common(q, kpool), ctypes.c_float(float(p)), _ptr(self.bitmap),
+                                      _ptr(self.workspace), self.workspace.numel() * 8, _stream(self.device))
+        check(rc, "sol_attn_mask_topp")
+        return self.bitmap

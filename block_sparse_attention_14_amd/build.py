@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsolattn.so")
-SOURCES = ["pool.hip", "plan.hip", "fwd.hip", "api.hip"]
+SOURCES = ["pool.hip", "plan.hip", "fwd.hip", "masks.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -34,6 +34,9 @@ constexpr int kMaxOrderedItems = 1 << 20;
 
 bool use_order(float tau, int nitems) { return !isinf(tau) && nitems > 1 && nitems <= kMaxOrderedItems; }
 
+// Largest B * H of the launches whose grid has one row per head (plan, masks).
+constexpr int kMaxGridHeads = 65535;
+
 int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return SOL_EINVAL;
   if (d != 64 && d != 128) return SOL_EUNSUPPORTED;
@@ -72,7 +75,7 @@ hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d
   if (e != hipSuccess) return e;
   unsigned* perm = reinterpret_cast<unsigned*>(wsb + w.perm);
   const int nitems = sol::forward_items(BH, Nq);
-  if (use_order(tau, nitems))
+  if (use_order(tau, nitems) && BH <= kMaxGridHeads)
     return sol::launch_plan(reinterpret_cast<const float*>(wsb + w.qpool), kpool,
                             reinterpret_cast<unsigned*>(wsb + w.cost), perm, BH, Nq, Nk, d, tau,
                             (float)(1.0 / sqrt((double)d)), s);
@@ -173,9 +176,92 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 
+// Workspace of the top-k / top-p mask builders: pooled queries, then the map.
+struct MaskWs {
+  size_t map, total;
+};
+
+MaskWs mask_ws(int BH, int N, int d) {
+  const size_t Nq = (size_t)(N + 63) / 64;
+  MaskWs w;
+  w.map = round_up((size_t)BH * Nq * (size_t)d * 4, 256);
+  w.total = round_up(w.map + (size_t)BH * Nq * Nq * 4, 256);
+  return w;
+}
+
+int check_mask(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, const uint32_t* bitmap) {
+  if (!q || !kpool || !bitmap) return SOL_EINVAL;
+  if (!aligned(q, 16) || !aligned(kpool, 16) || !aligned(bitmap, 4)) return SOL_EINVAL;
+  const int rc = check_sizes(B, H, N, d, Bq, Bk);
+  if (rc != SOL_OK) return rc;
+  if ((long long)B * H > kMaxGridHeads) return SOL_EUNSUPPORTED;
+  return SOL_OK;
+}
+
+int sorted_mask(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, int topk, float topp,
+                int mode, uint32_t* bitmap, void* ws, size_t ws_bytes, void* stream) {
+  const int rc = check_mask(q, kpool, B, H, N, d, Bq, Bk, bitmap);
+  if (rc != SOL_OK) return rc;
+  if (mode == 1 && isnan(topp)) return SOL_EINVAL;
+  if (!ws || !aligned(ws, 256)) return SOL_EINVAL;
+  const int BH = B * H, Nq = (N + 63) / 64, Nk = Nq;
+  const MaskWs w = mask_ws(BH, N, d);
+  if (ws_bytes < w.total) return SOL_EWORKSPACE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  float* qpool = reinterpret_cast<float*>(wsb);
+  float* map = reinterpret_cast<float*>(wsb + w.map);
+  sol::PoolSet set;
+  set.src[0] = static_cast<const uint16_t*>(q);
+  set.dst[0] = qpool;
+  set.n = 1;
+  hipError_t e = sol::launch_pool(set, BH, N, Nk, d, nullptr, s);
+  if (e == hipSuccess) e = sol::launch_proxy_map(qpool, kpool, map, BH, Nq, Nk, d, (float)(1.0 / sqrt((double)d)), s);
+  if (e == hipSuccess) e = sol::launch_sort_mask(map, bitmap, BH, Nq, Nk, topk, topp, mode, s);
+  return e == hipSuccess ? SOL_OK : SOL_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t sol_attn_mask_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk) {
+  if (check_sizes(B, H, N, d, Bq, Bk) != SOL_OK || (long long)B * H > kMaxGridHeads) return 0;
+  return mask_ws(B * H, N, d).total;
+}
+
+int sol_attn_mask_threshold(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk,
+                            const sol_attn_route* route, uint32_t* kept_bitmap, void* stream) {
+  int rc = check_mask(q, kpool, B, H, N, d, Bq, Bk, kept_bitmap);
+  if (rc != SOL_OK) return rc;
+  if (!route || check_route(*route, N, Bk) != SOL_OK) return SOL_EINVAL;
+  sol::MaskParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.kpool = kpool;
+  p.bitmap = kept_bitmap;
+  p.N = N;
+  p.Nq = (N + 63) / 64;
+  p.Nk = p.Nq;
+  p.nwords = (p.Nk + 31) / 32;
+  p.rule = route->rule;
+  p.tau = route->rule == SOL_ROUTE_ROWMAX ? route->tau : 0.f;
+  p.beta = route->rule == SOL_ROUTE_GAUSS ? route->beta : 0.f;
+  p.proxy_scale = (float)(1.0 / sqrt((double)d));
+  p.sink_lo = route->sink_count > 0 ? route->sink_first : 0;
+  p.sink_hi = route->sink_count > 0 ? route->sink_first + route->sink_count : 0;
+  const hipError_t e = sol::launch_mask_threshold(p, d, B * H, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SOL_OK : SOL_EHIP;
+}
+
+int sol_attn_mask_topk(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, int k,
+                       uint32_t* kept_bitmap, void* workspace, size_t workspace_bytes, void* stream) {
+  return sorted_mask(q, kpool, B, H, N, d, Bq, Bk, k, 0.f, 0, kept_bitmap, workspace, workspace_bytes, stream);
+}
+
+int sol_attn_mask_topp(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, float p,
+                       uint32_t* kept_bitmap, void* workspace, size_t workspace_bytes, void* stream) {
+  return sorted_mask(q, kpool, B, H, N, d, Bq, Bk, 0, p, 1, kept_bitmap, workspace, workspace_bytes, stream);
+}
 
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk) {
   if (check_sizes(B, H, N, d, Bq, Bk) != SOL_OK) return 0;

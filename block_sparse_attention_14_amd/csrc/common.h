@@ -75,4 +75,35 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// 16-byte load; bytes at or beyond the resource's size read as zero.
+__device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float4 ld16f(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const uint4 u = ld16(r, voff, soff);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
+// Sum of a value over the lanes of a wave that share lane % CH (CH = 8 or
+// 16): one DPP step for lane ^ 8 when CH = 8, then permlane swaps for
+// lane ^ 16 and lane ^ 32. Every lane of a group ends with the same sum.
+template <int CH>
+__device__ __forceinline__ float colsum_rows(float x) {
+  if (CH == 8) x += dpp<kDppRor8>(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace sol

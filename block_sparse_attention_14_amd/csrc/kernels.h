@@ -79,6 +79,25 @@ hipError_t launch_identity_order(unsigned* perm, int nitems, hipStream_t stream)
 // The fused routing + exact + correction kernel (persistent grid).
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t stream);
 
+// The mask builders (masks.hip).
+struct MaskParams {
+  const uint16_t* q;     // bf16 [BH][N][d]
+  const float* kpool;    // fp32 [BH][Nk][d]
+  uint32_t* bitmap;      // [BH][Nq][nwords]
+  int N, Nq, Nk, nwords;
+  int rule;              // SOL_ROUTE_*
+  float tau, beta, proxy_scale;
+  int sink_lo, sink_hi;
+};
+// On-chip threshold routing, one workgroup per pair of query blocks.
+hipError_t launch_mask_threshold(const MaskParams& p, int d, int BH, hipStream_t stream);
+// map[bh][i][j] = qpool_i . kpool_j * scale (fp32, written to device memory).
+hipError_t launch_proxy_map(const float* qpool, const float* kpool, float* map, int BH, int Nq, int Nk, int d,
+                            float scale, hipStream_t stream);
+// Per-row sort of the map; mode 0 keeps the top `topk`, mode 1 the top-p prefix.
+hipError_t launch_sort_mask(const float* map, uint32_t* bitmap, int BH, int Nq, int Nk, int topk, float topp,
+                            int mode, hipStream_t stream);
+
 // Dynamic LDS bytes the fused kernel needs for the kept list of Nk blocks.
 size_t forward_dynamic_lds(int Nk);
 

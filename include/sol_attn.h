@@ -195,6 +195,36 @@ int sol_attn_forward_ex(const void* q, const void* k, const void* v, float* out,
                         uint32_t* kept_bitmap);
 
 /*
+ * Routing alone: the kept-block bitmap, without attention. Three routers with
+ * one output layout (that of sol_attn_forward_debug), for comparing routing
+ * costs (§2 "Block-Sparse Attention": top-k sets a fixed budget, top-p a
+ * dynamic one, both traversing the proxy scores; §4 "Efficient On-the-Fly
+ * Sparsification" compares their cost with on-chip threshold routing).
+ *   q          bf16 [B][H][N][d]; kpool fp32 [B][H][Nk][d] (sol_attn_pool)
+ *   kept_bitmap device uint32 [B][H][Nq][ceil(Nk/32)], written in full
+ * Errors as for sol_attn_forward; SOL_EUNSUPPORTED also when B * H > 65535.
+ *
+ * sol_attn_mask_threshold: the forward's own routing (pooled queries from the
+ * Q tiles, both proxy rows of a pair of query blocks in LDS, the rule and
+ * sinks of `route`); writes nothing but the bitmap.
+ *
+ * sol_attn_mask_topk / sol_attn_mask_topp: pool q into the workspace, write
+ * the full fp32 proxy map [B][H][Nq][Nk] to the workspace, then sort each
+ * row: top-k keeps the k highest scores (k clipped to 0..Nk; equal scores by
+ * lower block index); top-p keeps the fewest highest scores whose share of
+ * the row's softmax mass over the proxy scores reaches p (p <= 0: the top
+ * block; p >= 1: all; SOL_EINVAL for NaN). The workspace must hold
+ * sol_attn_mask_workspace_bytes() bytes, 256-byte aligned.
+ */
+size_t sol_attn_mask_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
+int sol_attn_mask_threshold(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk,
+                            const sol_attn_route* route, uint32_t* kept_bitmap, void* stream);
+int sol_attn_mask_topk(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, int k,
+                       uint32_t* kept_bitmap, void* workspace, size_t workspace_bytes, void* stream);
+int sol_attn_mask_topp(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, float p,
+                       uint32_t* kept_bitmap, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * sol_attn_forward plus an export of the routing decisions it used: the same
  * kernel, with the kept-block bitmap written as it routes.
  *   kept_bitmap  device uint32 [B][H][Nq][ceil(Nk/32)]; bit (j % 32) of word

@@ -164,3 +164,42 @@ def fwd_ex(route, bitmap=None, **over):
 ])
 def test_forward_ex_rejects_before_launch(route, bitmap, code):
     assert fwd_ex(route, bitmap) == code
+
+
+def test_mask_workspace_bytes():
+    L = sa.lib()
+    n = L.sol_attn_mask_workspace_bytes(1, 12, 32760, 128, 64, 64)
+    assert n >= 12 * 512 * 512 * 4 + 12 * 512 * 128 * 4
+    assert L.sol_attn_mask_workspace_bytes(1, 12, 32760, 96, 64, 64) == 0
+    assert L.sol_attn_mask_workspace_bytes(1, 70000, 64, 128, 64, 64) == 0  # B * H beyond one grid row per head
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, 1, 2, 1000, 128, 64, 64), sa.SOL_EINVAL),
+    ((P, None, 1, 2, 1000, 128, 64, 64), sa.SOL_EINVAL),
+    ((P + 2, P, 1, 2, 1000, 128, 64, 64), sa.SOL_EINVAL),
+    ((P, P, 0, 2, 1000, 128, 64, 64), sa.SOL_EINVAL),
+    ((P, P, 1, 2, 1000, 96, 64, 64), sa.SOL_EUNSUPPORTED),
+    ((P, P, 1, 70000, 64, 128, 64, 64), sa.SOL_EUNSUPPORTED),
+])
+def test_mask_builders_reject_before_launch(args, code):
+    L = sa.lib()
+    route = ctypes.byref(_lib.sol_attn_route(0, 2.0, 0.0, 0, 0))
+    assert L.sol_attn_mask_threshold(*args, route, P, None) == code
+    assert L.sol_attn_mask_topk(*args, 4, P, P, 1 << 40, None) == code
+    assert L.sol_attn_mask_topp(*args, ctypes.c_float(0.9), P, P, 1 << 40, None) == code
+
+
+def test_mask_builders_reject_bad_route_bitmap_workspace():
+    L = sa.lib()
+    a = (P, P, 1, 2, 1000, 128, 64, 64)
+    good = ctypes.byref(_lib.sol_attn_route(0, 2.0, 0.0, 0, 0))
+    assert L.sol_attn_mask_threshold(*a, None, P, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_threshold(*a, ctypes.byref(_lib.sol_attn_route(1, 0.0, math.nan, 0, 0)), P,
+                                     None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_threshold(*a, good, None, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_threshold(*a, good, P + 2, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_topk(*a, 4, P, None, 1 << 40, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_topk(*a, 4, P, P + 64, 1 << 40, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_topk(*a, 4, P, P, 64, None) == sa.SOL_EWORKSPACE
+    assert L.sol_attn_mask_topp(*a, ctypes.c_float(math.nan), P, P, 1 << 40, None) == sa.SOL_EINVAL
