@@ -133,6 +133,7 @@ def attend_head(
     rule: str = "rowmax",
     beta: float = 0.0,
     sinks: Optional[tuple] = None,
+    row_correction: bool = False,
 ) -> Dict[str, np.ndarray]:
     """Sparse-plus-corrected attention of one head; q, k, v are [N, d].
 
@@ -153,6 +154,11 @@ def attend_head(
     tau is ignored) or "gauss_diag" (the diagonal estimator of it).
     ``sinks`` = (first, count): key blocks first .. first+count-1 are always
     kept in the exact branch (App. A: text key-value tokens retained as sinks).
+    ``row_correction=True`` gives every row its own correction logit for a
+    skipped block, q_r . kbar_j / sqrt(d) (one token-to-block score per row
+    and key block, §3 "Unified execution"; App. B analyses one query row),
+    instead of the block's s_ij; weight n_j and value vbar_j are unchanged.
+    Routing stays block-level.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -199,7 +205,10 @@ def attend_head(
         tok = (np.concatenate([np.arange(kb[j, 0], kb[j, 1]) for j in kept])
                if len(kept) else np.zeros(0, dtype=np.int64))
         x = (q[r0:r1] @ k[tok].T) * scale                     # exact logits [n_i, T]
-        sc = np.broadcast_to(s[i, skipped], (r1 - r0, len(skipped)))  # proxy logits
+        if row_correction:
+            sc = (q[r0:r1] @ kbar[skipped].T) * scale             # token-to-block logits
+        else:
+            sc = np.broadcast_to(s[i, skipped], (r1 - r0, len(skipped)))  # proxy logits
         m = np.full(r1 - r0, -np.inf)
         if x.shape[1]:
             m = np.maximum(m, x.max(axis=1))

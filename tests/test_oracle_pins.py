@@ -447,3 +447,82 @@ def test_topp_is_the_smallest_top_set_reaching_p():
             # dropping the smallest kept block falls below p
             smallest = kept[np.argmin(s[i, kept])]
             assert (w[i, kept].sum() - w[i, smallest]) / w[i].sum() < p
+
+
+# ---------------------------------------------------------------------------
+# Token-to-block (per-row) correction (§3 "Unified execution": one shared
+# token-to-block score tile; App. B "Approximation error" for one query row)
+# ---------------------------------------------------------------------------
+
+def test_row_correction_worked_example():
+    """d = 1, one query block of two rows q = (1, 3) (qbar = 2), key blocks
+    k = (0, 0 | 1, 1), v = (1, 1 | 2, 4), tau = 0.5: s = (0, 2), block 1 kept.
+    Row q=1: exact terms e^1 (v=2), e^1 (v=4); block 0 corrected with the
+    row's own logit 1*0 = 0, weight 2, vbar = 1: (6e + 2)/(2e + 2).
+    Row q=3: (6e^3 + 2)/(2e^3 + 2). Block-level correction uses s = 0 for both
+    rows here too (kbar_0 = 0), so take a shifted block: k = (1, 1 | 3, 3),
+    s = (2, 6), kbar = (1, 3): row logits for block 0 are 1 and 3."""
+    q = np.array([[1.0], [3.0]])
+    k = np.array([[1.0], [1.0], [3.0], [3.0]])
+    v = np.array([[1.0], [1.0], [2.0], [4.0]])
+    q4 = np.vstack([q, q])  # two query blocks, the same rows
+    e = math.e
+    r = attend_head(q4, k, v, 2, 2, 0.5, row_correction=True)
+    assert r["keep"].tolist() == [[False, True], [False, True]]
+    row1 = (6 * e ** 3 + 2 * e) / (2 * e ** 3 + 2 * e)     # exact e^3 (v 2, 4); corrected 2 e^1 * 1
+    row3 = (6 * e ** 9 + 2 * e ** 3) / (2 * e ** 9 + 2 * e ** 3)
+    np.testing.assert_allclose(r["out"][:2, 0], [row1, row3], rtol=1e-14)
+    # block-level: both rows use s_00 = qbar * kbar_0 = 2
+    b = attend_head(q4, k, v, 2, 2, 0.5)
+    blk1 = (6 * e ** 3 + 2 * e ** 2) / (2 * e ** 3 + 2 * e ** 2)
+    blk3 = (6 * e ** 9 + 2 * e ** 2) / (2 * e ** 9 + 2 * e ** 2)
+    np.testing.assert_allclose(b["out"][:2, 0], [blk1, blk3], rtol=1e-14)
+
+
+def test_row_correction_exact_for_constant_key_blocks():
+    """Keys constant inside every block make each token's logit equal the
+    row's token-to-block logit, so the per-row correction is exact for any
+    queries and values (tau = 0 keeps almost nothing); the block-level one is
+    not, because queries vary inside a block."""
+    rng = np.random.default_rng(21)
+    N, d, Bk = 640, 8, 64
+    q, v = rand(rng, N, d), rand(rng, N, d)
+    kb = rand(rng, N // Bk, d)
+    k = np.repeat(kb, Bk, axis=0)
+    dense = sdpa64(q, k, v)
+    r = attend_head(q, k, v, 64, Bk, 0.0, row_correction=True)
+    assert r["keep"].sum() < r["keep"].size  # blocks were skipped
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-11, atol=1e-12)
+    b = attend_head(q, k, v, 64, Bk, 0.0)
+    assert np.abs(b["out"] - dense).max() > 1e-3
+
+
+def test_query_and_key_spread_error_orders():
+    """Queries spread inside a block by eps around qbar, keys constant per
+    block: the block-level correction's error is first order in eps (halving
+    eps halves it) while the per-row correction is exact. Keys spread by eps
+    with values constant per block: the per-row error is second order
+    (App. B: the denominator error is second order in the centred spread)."""
+    rng = np.random.default_rng(8)
+    N, d = 256, 4
+
+    def centred(a):
+        return a - np.repeat(a.reshape(N // 64, 64, d).mean(axis=1), 64, axis=0)
+
+    base_q = np.repeat(rand(rng, N // 64, d), 64, axis=0)
+    uq, uk = centred(rand(rng, N, d)), centred(rand(rng, N, d))
+    kb = np.repeat(rand(rng, N // 64, d), 64, axis=0)
+    v = rand(rng, N, d)
+    vb = np.repeat(rand(rng, N // 64, d), 64, axis=0)
+    keep = np.zeros((N // 64, N // 64), dtype=bool)
+    keep[:, 0] = True
+
+    def err(q, k, vv, row):
+        r = attend_head(q, k, vv, 64, 64, 0.0, keep_override=keep, row_correction=row)
+        return np.abs(r["out"] - sdpa64(q, k, vv)).max()
+
+    blk = [err(base_q + e * uq, kb, v, False) for e in (0.02, 0.01)]
+    assert blk[0] / blk[1] == pytest.approx(2.0, rel=0.05)
+    assert max(err(base_q + e * uq, kb, v, True) for e in (0.02, 0.01)) < 1e-13
+    row = [err(base_q, kb + e * uk, vb, True) for e in (0.02, 0.01)]
+    assert row[0] / row[1] == pytest.approx(4.0, rel=0.05)
