@@ -163,6 +163,14 @@ def main():
             e.record(stream)
         torch.cuda.synchronize()
         r["plan"], r["fwd_planned"] = elapsed(ev1), elapsed(ev2)
+        # the whole call with the token-to-block (per-row) correction
+        ev = events(n)
+        for a, b in ev:
+            a.record(stream)
+            runner(q, k, v, tau, out=out, flags=sa.SOL_F_ROW_CORRECTION)
+            b.record(stream)
+        torch.cuda.synchronize()
+        r["call_row_correction"] = elapsed(ev)
         return r, wall, stats
 
     def pct(xs):
@@ -211,6 +219,7 @@ def main():
             "fwd_ms": pct(r["fwd"]),
             "planned": {"ms_plan": round(ms_plan, 4), "ms_fwd": round(ms_fwd_planned, 4),
                         "ms_per_call": round(ms_pool + ms_plan + ms_fwd_planned, 4)},
+            "row_correction_ms_per_call": round(float(np.median(r["call_row_correction"])), 4),
             "dense_equiv_tflops": round(dense / (ms_call * 1e-3) / 1e12, 1),
             "kept_block_pct": round(kept_pct, 3),
             "kept_token_pct": round(100.0 * stats["kept_pairs"] / (B * H * N * N), 3),
@@ -239,9 +248,9 @@ def main():
             traffic = tr.get("bytes_per_launch")
 
     def ablation(wname, taus_ab):
-        """Corrected vs exact-only outputs for the same routing, against this
-        kernel's dense (tau = +inf) output: global relative L2 error and the
-        mean cosine similarity of rows."""
+        """Block-level corrected, per-row corrected and exact-only outputs for
+        the same routing, against this kernel's dense (tau = +inf) output:
+        global relative L2 error and the mean cosine similarity of rows."""
         wl2 = get_workload(wname)
         x2 = make_inputs(wl2)
         q2, k2, v2 = (torch.from_numpy(x2[n].view(np.int16)).to(dev).view(torch.bfloat16) for n in "qkv")
@@ -259,8 +268,9 @@ def main():
             c = metrics(r2(q2, k2, v2, tau))
             kept = r2.read_stats()
             e = metrics(r2(q2, k2, v2, tau, flags=sa.SOL_F_EXACT_ONLY))
+            rc = metrics(r2(q2, k2, v2, tau, flags=sa.SOL_F_ROW_CORRECTION))
             rep_[f"{tau:g}"] = {"kept_block_pct": round(100.0 * kept["kept_blocks"] / kept["total_blocks"], 3),
-                                "corrected": c, "exact_only": e}
+                                "corrected": c, "row_corrected": rc, "exact_only": e}
         del q2, k2, v2, r2, dense_out
         torch.cuda.empty_cache()
         return rep_

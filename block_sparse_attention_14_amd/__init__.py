@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     SOL_F_EXACT_ONLY,
     SOL_F_PLANNED,
     SOL_F_POOLED,
+    SOL_F_ROW_CORRECTION,
     SOL_OK,
     SOL_ROUTE_GAUSS,
     SOL_ROUTE_ROWMAX,

@@ -16,6 +16,7 @@ SOL_EHIP = -4
 SOL_F_POOLED = 1 << 0
 SOL_F_EXACT_ONLY = 1 << 1
 SOL_F_PLANNED = 1 << 2
+SOL_F_ROW_CORRECTION = 1 << 3
 
 SOL_ROUTE_ROWMAX = 0
 SOL_ROUTE_GAUSS = 1

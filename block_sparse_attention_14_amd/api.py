@@ -14,7 +14,7 @@ from typing import Dict, Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import SOL_F_EXACT_ONLY, SOL_F_PLANNED, SOL_F_POOLED, check, lib  # noqa: F401
+from ._lib import SOL_F_EXACT_ONLY, SOL_F_PLANNED, SOL_F_POOLED, SOL_F_ROW_CORRECTION, check, lib  # noqa: F401
 
 STATS_WORDS = 4  # sol_attn_stats is 32 bytes
 

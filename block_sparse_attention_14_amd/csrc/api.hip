@@ -14,7 +14,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: [header words | item costs | item order | pooled queries].
 struct WsLayout {
-  size_t cost, perm, qpool, total;
+  size_t cost, perm, qpool, khi16, klo16, vbar16, total;
 };
 
 WsLayout ws_layout(int BH, int N, int d) {
@@ -24,7 +24,10 @@ WsLayout ws_layout(int BH, int N, int d) {
   w.cost = sol::kHdrWords * 4;
   w.perm = round_up(w.cost + 4 * items, 256);
   w.qpool = round_up(w.perm + 4 * items, 256);
-  w.total = round_up(w.qpool + (size_t)BH * Nq * (size_t)d * 4, 256);
+  w.khi16 = round_up(w.qpool + (size_t)BH * Nq * (size_t)d * 4, 256);
+  w.klo16 = round_up(w.khi16 + (size_t)BH * Nq * (size_t)d * 2, 256);
+  w.vbar16 = round_up(w.klo16 + (size_t)BH * Nq * (size_t)d * 2, 256);
+  w.total = round_up(w.vbar16 + (size_t)BH * Nq * (size_t)d * 2, 256);
   return w;
 }
 
@@ -107,7 +110,8 @@ int check_forward(const void* q, const void* k, const void* v, const float* out,
       !aligned(kpool, 16) || !aligned(vmean, 16) || !aligned(ws, 256) || !aligned(stats, 8))
     return SOL_EINVAL;
   if (check_route(route, N, Bk) != SOL_OK) return SOL_EINVAL;
-  if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED)) return SOL_EINVAL;
+  if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION)) return SOL_EINVAL;
+  if ((flags & SOL_F_EXACT_ONLY) && (flags & SOL_F_ROW_CORRECTION)) return SOL_EINVAL;
   if ((flags & SOL_F_PLANNED) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
   const int rc = check_sizes(B, H, N, d, Bq, Bk);
   if (rc != SOL_OK) return rc;
@@ -147,6 +151,13 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
     e = sol::launch_pool(set, BH, N, Nk, d, static_cast<unsigned*>(ws), s);
   }
   if (e != hipSuccess) return SOL_EHIP;
+  uint16_t* khi16 = reinterpret_cast<uint16_t*>(wsb + w.khi16);
+  uint16_t* klo16 = reinterpret_cast<uint16_t*>(wsb + w.klo16);
+  uint16_t* vbar16 = reinterpret_cast<uint16_t*>(wsb + w.vbar16);
+  if (flags & SOL_F_ROW_CORRECTION) {
+    e = sol::launch_to_bf16(kpool, khi16, klo16, vmean, vbar16, (size_t)BH * Nk * d, s);
+    if (e != hipSuccess) return SOL_EHIP;
+  }
 
   sol::FwdParams p;
   p.q = q16;
@@ -172,6 +183,10 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   p.proxy_scale = (float)(1.0 / sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   p.exact_only = (flags & SOL_F_EXACT_ONLY) ? 1 : 0;
+  p.row_corr = (flags & SOL_F_ROW_CORRECTION) ? 1 : 0;
+  p.khi16 = khi16;
+  p.klo16 = klo16;
+  p.vbar16 = vbar16;
   e = sol::launch_forward(p, d, s);
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }

@@ -61,6 +61,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -75,6 +76,7 @@ constexpr int kThreads = 256;
 // this (base-2 units); until then probabilities may reach 2^8, which fp32 and
 // bf16 carry as exactly (relatively) as values below 1.
 constexpr float kLazyRescale = 8.0f;
+constexpr int kMaxKeyWords = (SOL_ATTN_MAX_N / kBlk + 31) / 32;
 // max over the four lanes l, l^16, l^32, l^48 that share one query row
 __device__ __forceinline__ float rowmax4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -126,6 +128,18 @@ __device__ __forceinline__ uint2 ld_tr(const unsigned char* p) {
 // offset inside its chunk is the same for every chunk of the wave (the
 // swizzles depend on row bits the chunk index does not touch), so only a
 // scalar offset changes between the copies.
+// One 64-row tile into dst, chunks placed as K rows (kslot) or V rows (vslot).
+template <int D, bool KROWS>
+__device__ __forceinline__ void dma_one(unsigned char* dst, rsrc_t r, int wid, int lane) {
+  using G = Geom<D>;
+  constexpr int LPR = G::RB / 16;
+  const int row = (1024 * wid) / G::RB + lane / LPR, sl = lane % LPR;
+  const uint32_t o = row * G::RB + 16 * (KROWS ? kslot<D>(row, sl) : vslot<D>(row, sl));
+#pragma unroll
+  for (int u = 0; u < G::NCH / 4; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 1024 * (wid + 4 * u)), 16, o, 4096 * u, 0, 0);
+}
+
 template <int D>
 __device__ __forceinline__ void dma_tile(unsigned char* stage, rsrc_t rk, rsrc_t rv, int wid, int lane) {
   using G = Geom<D>;
@@ -147,6 +161,7 @@ struct alignas(16) Small {
   float cnum[2][D];  // correction numerators
   float wred[2][8];
   float gred[2][8];  // row sums, then squared deviations (Gaussian threshold)
+  uint32_t kbits[2][kMaxKeyWords];  // kept-block bits of blocks A and B
   float cden[2];
   int cnt[3][4];
   int lastkept[2];
@@ -154,7 +169,8 @@ struct alignas(16) Small {
   int last;  // this workgroup finished last
 };
 
-template <int D>
+// RC: the per-row (token-to-block) correction replaces the block-level one.
+template <int D, bool RC>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   using G = Geom<D>;
   // Two separate LDS objects for the two stages, so that reads of one stage
@@ -397,6 +413,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
           sm.cnt[1][wid] = __popcll(bA);
           sm.cnt[2][wid] = __popcll(bB);
           const int w0 = (j0 + 64 * wid) >> 5;
+          if (w0 < kMaxKeyWords) {
+            sm.kbits[0][w0] = (uint32_t)bA;
+            sm.kbits[1][w0] = (uint32_t)bB;
+          }
+          if (w0 + 1 < kMaxKeyWords) {
+            sm.kbits[0][w0 + 1] = (uint32_t)(bA >> 32);
+            sm.kbits[1][w0 + 1] = (uint32_t)(bB >> 32);
+          }
           if (bmA) {
             if (w0 < p.nwords) bmA[w0] = (uint32_t)bA;
             if (w0 + 1 < p.nwords) bmA[w0 + 1] = (uint32_t)(bA >> 32);
@@ -433,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       constexpr int C4 = D / 4, JG = kThreads / C4, U = 8;  // 2 x 32 KiB of pooled values in flight
       const int c4 = tid % C4, jg = tid / C4;
       float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-      if (!p.exact_only && (nkA < Nk || (hasB && nkB < Nk))) {
+      if (!RC && !p.exact_only && (nkA < Nk || (hasB && nkB < Nk))) {
         const rsrc_t rv = make_rsrc(p.vmean + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
         const uint32_t voff = (jg * D + c4 * 4) * 4;
         // two batches of U pooled values per lane: one in flight while the other is used
@@ -475,7 +499,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         for (int r = 0; r < JG; ++r) s += red[(blk * JG + r) * D + col];
         sm.cnum[blk][col] = s;
       }
-      if (tid < 2) sm.cden[tid] = (sm.wred[tid][4] + sm.wred[tid][5]) + (sm.wred[tid][6] + sm.wred[tid][7]);
+      if (tid < 2)
+        sm.cden[tid] = RC ? 0.f : (sm.wred[tid][4] + sm.wred[tid][5]) + (sm.wred[tid][6] + sm.wred[tid][7]);
       __syncthreads();  // the tile stages are free again
     }
 
@@ -495,11 +520,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       const uint16_t* kh = p.k + hoff;
       const uint16_t* vh = p.v + hoff;
       const int ownbit = 1 << (14 + qb);
+      // K and V tiles of kept key block ulist[t] into one stage
       auto dma = [&](unsigned char* stage, int t) {
         const int j = ulist[t] & 0x3fff;
         const uint32_t bytes = (uint32_t)min(kBlk, N - j * kBlk) * D * 2;
         dma_tile<D>(stage, make_rsrc(kh + (size_t)j * kBlk * D, bytes), make_rsrc(vh + (size_t)j * kBlk * D, bytes),
                     wid, lane);
+      };
+      // pooled tile c (per-row correction): the two bf16 parts of the pooled
+      // keys fill stage A (both as K rows), the pooled values stage B's V half
+      auto dma_pooled = [&](int c) {
+        const uint32_t bytes = (uint32_t)min(kBlk, Nk - c * kBlk) * D * 2;
+        const size_t off = ((size_t)bh * Nk + (size_t)c * kBlk) * D;
+        dma_one<D, true>(stA, make_rsrc(p.khi16 + off, bytes), wid, lane);
+        dma_one<D, true>(stA + G::TILE, make_rsrc(p.klo16 + off, bytes), wid, lane);
+        dma_one<D, false>(stB + G::TILE, make_rsrc(p.vbar16 + off, bytes), wid, lane);
       };
       // per-lane byte offsets of the swizzled operand reads (independent of the key tile kt)
       int koff[NDS];
@@ -513,10 +548,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       for (int dt = 0; dt < NDT; ++dt)
         voff[dt] = G::TILE + vrow * G::RB + 16 * vslot<D>(vrow, 2 * dt + (vcc >> 1)) + 8 * (vcc & 1);
 
-      auto compute = [&](const unsigned char* stage, int e) {
-        if (!(e & ownbit)) return;  // wave-uniform: this wave's block skips the entry
+      auto compute = [&](const unsigned char* stage, int e, auto pooled) {
+        constexpr bool kPooled = decltype(pooled)::value;
+        if (!kPooled && !(e & ownbit)) return;  // wave-uniform: this wave's block skips the entry
         const int j = e & 0x3fff;
-        const int nj = min(kBlk, N - j * kBlk);
+        const int nj = kPooled ? kBlk : min(kBlk, N - j * kBlk);
         // S^T[kv][q]: 4 key tiles x 2 query tiles; each K operand serves both
         f32x4 st[2][4];
 #pragma unroll
@@ -528,10 +564,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
             const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(stage + 16 * kt * G::RB + koff[ds]));
             st[0][kt] = mfma16x16x32(a, qop[0][ds], st[0][kt]);
             st[1][kt] = mfma16x16x32(a, qop[1][ds], st[1][kt]);
+            if (kPooled) {  // the remainder part of the pooled keys, one tile further on
+              const bf16x8 b =
+                  as_bf16x8(*reinterpret_cast<const uint4*>(stage + G::TILE + 16 * kt * G::RB + koff[ds]));
+              st[0][kt] = mfma16x16x32(b, qop[0][ds], st[0][kt]);
+              st[1][kt] = mfma16x16x32(b, qop[1][ds], st[1][kt]);
+            }
           }
         }
         // lane holds S^T[16kt + 4g + i][row c16 of query tile qt]
-        if (nj < kBlk) {
+        if (kPooled) {
+          // pooled key 64e + 16kt + 4g + i: masked when kept by this wave's
+          // block (it is in the exact branch) or past Nk; otherwise its
+          // weight n_j enters as log2(n_j) on the base-2 logit, added here in
+          // raw dot-product units (n_j = 64 but for the ragged last block)
+          const uint32_t* kb = sm.kbits[qb];
+          const int valid = Nk - e * kBlk;
+          uint64_t off = (uint64_t)kb[2 * e] | ((uint64_t)kb[2 * e + 1] << 32);
+          if (valid < kBlk) off |= ~0ull << valid;
+          off >>= 4 * g;
+          const float bias = 6.f / csc;
+          const int last = Nk - 1 - e * kBlk - 4 * g;  // lane position of the last block, if here
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool masked = (off >> (16 * kt + i)) & 1ull;
+              const float b = 16 * kt + i == last ? __log2f((float)nlast) / csc : bias;
+              st[0][kt][i] = masked ? -INFINITY : st[0][kt][i] + b;
+              st[1][kt][i] = masked ? -INFINITY : st[1][kt][i] + b;
+            }
+        } else if (nj < kBlk) {
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -594,12 +657,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         // O^T[d][q] += V^T[d][kv] P^T[kv][q]; the transposing reads of rows
         // 32ks + 4g + e and 32ks + 16 + 4g + e give exactly the keys of the P^T
         // slots; each V^T operand serves both query tiles
+        const unsigned char* vstage = kPooled ? stB : stage;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const uint2 lo = ld_tr(stage + voff[dt] + 32 * ks * G::RB);
-            const uint2 hi = ld_tr(stage + voff[dt] + (32 * ks + 16) * G::RB);
+            const uint2 lo = ld_tr(vstage + voff[dt] + 32 * ks * G::RB);
+            const uint2 hi = ld_tr(vstage + voff[dt] + (32 * ks + 16) * G::RB);
             const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
             acc[0][dt] = mfma16x16x32(a, pb[0][ks], acc[0][dt]);
             acc[1][dt] = mfma16x16x32(a, pb[1][ks], acc[1][dt]);
@@ -615,15 +679,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // tiles 0 and 1 are in LDS
       for (int t = 0; t < nu; t += 2) {
-        compute(stA, ulist[t]);
+        compute(stA, ulist[t], std::false_type{});
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // tile t+1 has landed in stB; nobody reads stA any more
         if (t + 2 < nu) dma(stA, t + 2);
         if (t + 1 < nu) {
-          compute(stB, ulist[t + 1]);
+          compute(stB, ulist[t + 1], std::false_type{});
           __builtin_amdgcn_s_waitcnt(0);
           __syncthreads();  // tile t+2 has landed in stA; nobody reads stB any more
           if (t + 3 < nu) dma(stB, t + 3);
+        }
+      }
+      if (RC) {
+        // pooled tiles, one at a time: each fills stage A and half of stage B
+        const int npool = (Nk + kBlk - 1) / kBlk;
+        for (int c = 0; c < npool; ++c) {
+          dma_pooled(c);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();  // pooled tile c is in LDS
+          compute(stA, c, std::true_type{});
+          __syncthreads();  // nobody reads the pooled tile any more
         }
       }
     }
@@ -727,7 +802,7 @@ int forward_max_blocks(int d) {
   return d == 128 ? Geom<128>::STAGE / 4 : Geom<64>::STAGE / 4;
 }
 
-template <int D>
+template <int D, bool RC>
 static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   // per-device CU count and occupancy (bucketed by dynamic LDS in 4 KiB steps)
   static std::mutex mu;
@@ -746,14 +821,14 @@ static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
       int n = 0;
       e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<D>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<D, RC>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 32 * 1024);
       if (e != hipSuccess) return e;
       cus[dev] = n;
     }
     if (occ_cache[dev][bucket] == 0) {
       int occ = 0;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&fwd_kernel<D>),
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&fwd_kernel<D, RC>),
                                                        kThreads, (size_t)(bucket + 1) * 4096);
       if (e != hipSuccess) return e;
       occ_cache[dev][bucket] = occ < 1 ? 1 : occ;
@@ -762,12 +837,13 @@ static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     grid_per_cu = occ_cache[dev][bucket];
   }
   const int grid = (int)std::min<long long>((long long)ncu * grid_per_cu, p.nitems);
-  hipLaunchKernelGGL(fwd_kernel<D>, dim3(grid), dim3(kThreads), dyn, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, RC>), dim3(grid), dim3(kThreads), dyn, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t stream) {
-  return d == 128 ? launch_d<128>(p, stream) : launch_d<64>(p, stream);
+  if (p.row_corr) return d == 128 ? launch_d<128, true>(p, stream) : launch_d<64, true>(p, stream);
+  return d == 128 ? launch_d<128, false>(p, stream) : launch_d<64, false>(p, stream);
 }
 
 }  // namespace sol

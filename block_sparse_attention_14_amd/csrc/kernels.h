@@ -49,6 +49,10 @@ struct FwdParams {
   float proxy_scale;     // 1/sqrt(d)
   float scale_log2;      // log2(e)/sqrt(d)
   int exact_only;        // skipped blocks dropped instead of corrected
+  int row_corr;          // per-row (token-to-block) correction over the pooled tiles below
+  const uint16_t* khi16;   // bf16 [BH][Nk][d] pooled keys, high part (row_corr)
+  const uint16_t* klo16;   // bf16 [BH][Nk][d] pooled keys, the remainder (row_corr)
+  const uint16_t* vbar16;  // bf16 [BH][Nk][d] pooled values (row_corr)
 };
 
 // Up to three bf16 [BH][N][d] tensors pooled per 64-token block into fp32
@@ -62,6 +66,11 @@ struct PoolSet {
 // Pools the tensors of `set`; when `hdr` is non-null, also resets the
 // workspace header words.
 hipError_t launch_pool(const PoolSet& set, int BH, int N, int Nk, int d, unsigned* hdr, hipStream_t stream);
+
+// a = a_hi + a_lo in two bf16 parts (each rounded to nearest even; the pair
+// carries about 16 significant bits) and b16 = bf16(b), for n values each.
+hipError_t launch_to_bf16(const float* a, uint16_t* a_hi, uint16_t* a_lo, const float* b, uint16_t* b16, size_t n,
+                          hipStream_t stream);
 
 // Resets the workspace header words (one small kernel).
 hipError_t launch_reset(unsigned* hdr, hipStream_t stream);

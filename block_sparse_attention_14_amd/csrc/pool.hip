@@ -59,6 +59,25 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolSet set, int N, int Nk, u
     for (int w = tid; w < kHdrWords; w += 256) hdr[w] = w == kHdrMin ? 0xffffffffu : 0u;
 }
 
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ a, uint16_t* __restrict__ a_hi,
+                                                      uint16_t* __restrict__ a_lo, const float* __restrict__ b,
+                                                      uint16_t* __restrict__ b16, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    const uint32_t hi = pack_bf16x2(a[i], 0.f) & 0xffffu;
+    a_hi[i] = (uint16_t)hi;
+    a_lo[i] = (uint16_t)(pack_bf16x2(a[i] - __uint_as_float(hi << 16), 0.f) & 0xffffu);
+    b16[i] = (uint16_t)(pack_bf16x2(b[i], 0.f) & 0xffffu);
+  }
+}
+
+hipError_t launch_to_bf16(const float* a, uint16_t* a_hi, uint16_t* a_lo, const float* b, uint16_t* b16, size_t n,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a, a_hi, a_lo, b, b16,
+                     n);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void reset_kernel(unsigned* hdr) {
   for (int w = threadIdx.x; w < kHdrWords; w += 256) hdr[w] = w == kHdrMin ? 0xffffffffu : 0u;
 }

@@ -73,7 +73,15 @@ enum {
    * of the same shapes gives the same result, only scheduled worse. A
    * workspace that was never planned must not be used with this flag.
    * Requires SOL_F_POOLED. */
-  SOL_F_PLANNED = 1u << 2
+  SOL_F_PLANNED = 1u << 2,
+  /* Token-to-block correction (§3 "Unified execution": one score tile per
+   * query row and key block; App. B analyses one query row): a skipped block
+   * j adds, for every row r of the query block, the logit q_r . kbar_j /
+   * sqrt(d) (instead of the block's s_ij) with weight n_j and value vbar_j.
+   * Routing stays block-level. Computed in bf16 MFMA tiles over the pooled
+   * keys and values (bf16-rounded copies made in the workspace), in the same
+   * online softmax as the kept blocks. Not with SOL_F_EXACT_ONLY. */
+  SOL_F_ROW_CORRECTION = 1u << 3
 };
 
 /* Routing rules of sol_attn_forward_ex (§3 "Dynamic threshold routing":
@@ -115,8 +123,9 @@ typedef struct sol_attn_stats {
 
 /* Bytes of device workspace sol_attn_forward and sol_attn_plan need: the
  * work-queue and stats words, one cost and one order slot per work item (a
- * pair of query blocks), and the fp32 pooled queries [B][H][Nq][d] of the
- * planning stage. Returns 0 for unsupported sizes. */
+ * pair of query blocks), the fp32 pooled queries [B][H][Nq][d] of the
+ * planning stage, and bf16 copies of the pooled keys and values
+ * [B][H][Nk][d] for SOL_F_ROW_CORRECTION. Returns 0 for unsupported sizes. */
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
 
 /*

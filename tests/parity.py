@@ -79,12 +79,13 @@ def check_bitmap(gpu_keep: np.ndarray, s: np.ndarray, theta: np.ndarray, keep: n
 
 
 def check_head(qb, kb, vb, out_gpu, keep_gpu, tau, query_blocks: Optional[Iterable[int]] = None, where="",
-               beta=None, sinks=None):
+               beta=None, sinks=None, row_correction=False):
     """Bitmap on every query block of the head; outputs on `query_blocks` (all if None)."""
     q, k, v = (bf16_bits_to_f64(x) for x in (qb, kb, vb))
     s, theta, keep, forced = oracle_route(q, k, tau, beta, sinks)
     check_bitmap(keep_gpu, s, theta, keep, forced, beta is None, where)
-    r = attend_head(q, k, v, 64, 64, tau, keep_override=keep_gpu, query_blocks=query_blocks)
+    r = attend_head(q, k, v, 64, 64, tau, keep_override=keep_gpu, query_blocks=query_blocks,
+                    row_correction=row_correction)
     rows = np.concatenate([np.arange(i * 64, min(q.shape[0], i * 64 + 64)) for i in r["rows"]])
     err = np.abs(out_gpu[rows] - r["out"][rows]).max()
     assert np.isfinite(out_gpu[rows]).all(), f"{where}: non-finite output"

@@ -80,6 +80,7 @@ def fwd(**over):
     (dict(tau=float("nan")), sa.SOL_EINVAL),
     (dict(tau=-math.inf), sa.SOL_EINVAL),
     (dict(flags=1 << 7), sa.SOL_EINVAL),
+    (dict(flags=sa.SOL_F_EXACT_ONLY | sa.SOL_F_ROW_CORRECTION), sa.SOL_EINVAL),
     (dict(d=96), sa.SOL_EUNSUPPORTED),
     (dict(d=256), sa.SOL_EUNSUPPORTED),
     (dict(Bq=32), sa.SOL_EUNSUPPORTED),

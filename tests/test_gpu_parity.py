@@ -32,20 +32,25 @@ def _report(name, tag, err):
     print(f"[parity] {name} {tag} max_abs_err={err:.3e}", flush=True)
 
 
-def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, seed=0, beta=None, sinks=None):
+def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, seed=0, beta=None, sinks=None,
+                 flags=0):
     x = inputs or make_inputs(wl)
-    out, keep, stats = run_gpu(x["q"], x["k"], x["v"], tau, beta=beta, sinks=sinks)
+    out, keep, stats = run_gpu(x["q"], x["k"], x["v"], tau, beta=beta, sinks=sinks, flags=flags)
     check_stats(stats, keep, wl.N)
     rng = np.random.default_rng(seed)
     worst = 0.0
     tag = f"tau={tau}" if beta is None else f"beta={beta}"
     if sinks is not None:
         tag += f" sinks={sinks}"
+    rowc = bool(flags & sa.SOL_F_ROW_CORRECTION)
+    if rowc:
+        tag += " row-correction"
     for b in range(wl.B):
         for h in range(wl.H):
             qbs = None if query_blocks_per_head is None else sample_blocks(wl.Nq, rng, query_blocks_per_head)
             worst = max(worst, check_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], out[b, h], keep[b, h],
-                                          tau, qbs, where=f"{wl.name} b={b} h={h} {tag}", beta=beta, sinks=sinks))
+                                          tau, qbs, where=f"{wl.name} b={b} h={h} {tag}", beta=beta, sinks=sinks,
+                                          row_correction=rowc))
     _report(wl.name, tag, worst)
     return out, keep, stats
 
@@ -280,3 +285,47 @@ def test_route_arguments_rejected():
                dict(sinks=(0, -1))):
         with pytest.raises(sa.SolAttnError):
             r(q, k, v, 2.0, **kw)
+
+
+# ---------------------------------------------------------------------------
+# Token-to-block (per-row) correction
+# ---------------------------------------------------------------------------
+
+RC = sa.SOL_F_ROW_CORRECTION
+
+
+@pytest.mark.parametrize("tau", [0.0, 2.0, 4.0, INF])
+def test_row_correction_tiny(tau):
+    _full_parity(get_workload("tiny_fp32"), tau, flags=RC)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 65, 130, 1000])
+@pytest.mark.parametrize("tau", [0.0, 1.5])
+def test_row_correction_ragged(N, d, tau):
+    _full_parity(_custom(N, d, H=2, seed=N + d + 11), tau, flags=RC)
+
+
+def test_row_correction_image_video_smooth(video32k):
+    _full_parity(get_workload("image_dit_4k"), 2.0, flags=RC)
+    _full_parity(get_workload("video_dit_32k"), 2.0, video32k, query_blocks_per_head=3, seed=6, flags=RC)
+    _full_parity(get_workload("video_dit_32k_smoothv"), 2.0, query_blocks_per_head=3, seed=7, flags=RC)
+
+
+def test_row_correction_with_gauss_and_sinks():
+    _full_parity(get_workload("tiny_fp32"), 0.0, beta=1.0, sinks=(2, 2), flags=RC)
+    _full_parity(_custom(1000, 128, H=2, seed=3), 1.0, sinks=(15, 1), flags=RC)
+
+
+def test_row_correction_planned_matches_one_shot():
+    wl = get_workload("image_dit_4k")
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    one = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    ref = one(q, k, v, 2.0, flags=RC).clone()
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    sa.pool(k, v, kpool=r.kpool, vmean=r.vmean)
+    r.plan(q, 2.0)
+    out = r(q, k, v, 2.0, flags=RC | sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
