@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     SOL_F_ROW_CORRECTION,
     SOL_OK,
     SOL_ROUTE_GAUSS,
+    SOL_ROUTE_GAUSS_DIAG,
     SOL_ROUTE_ROWMAX,
     SolAttnError,
     lib,

@@ -20,6 +20,7 @@ SOL_F_ROW_CORRECTION = 1 << 3
 
 SOL_ROUTE_ROWMAX = 0
 SOL_ROUTE_GAUSS = 1
+SOL_ROUTE_GAUSS_DIAG = 2
 
 SOL_ATTN_MAX_N = 4096 * 64
 

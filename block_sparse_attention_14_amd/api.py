@@ -112,10 +112,11 @@ class SolAttention:
 
     def __call__(self, q, k, v, tau: float, flags: int = 0, out: Optional[torch.Tensor] = None,
                  stats: bool = True, bitmap: Optional[torch.Tensor] = None, beta: Optional[float] = None,
-                 sinks: Optional[Tuple[int, int]] = None) -> torch.Tensor:
+                 sinks: Optional[Tuple[int, int]] = None, diag: bool = False) -> torch.Tensor:
         """Forward on the current stream. ``tau`` is the row-max offset; with
         ``beta`` set, the Gaussian-calibrated rule (mean + beta * std of each
-        proxy row) routes instead and ``tau`` is ignored. ``sinks`` =
+        proxy row) routes instead and ``tau`` is ignored; ``diag`` selects its
+        diagonal estimator from the pooled-key statistics. ``sinks`` =
         (first, count) key blocks that are always kept."""
         shape = (self.B, self.H, self.N, self.d)
         _check_qkv("q", q, shape)
@@ -134,8 +135,10 @@ class SolAttention:
                 raise ValueError(f"bitmap must be a contiguous int32 tensor of shape {bs} on {self.device}")
             bm_ptr = _ptr(bitmap)
         if beta is not None or sinks is not None:
+            rule = _lib.SOL_ROUTE_ROWMAX if beta is None else (
+                _lib.SOL_ROUTE_GAUSS_DIAG if diag else _lib.SOL_ROUTE_GAUSS)
             route = _lib.sol_attn_route(
-                _lib.SOL_ROUTE_GAUSS if beta is not None else _lib.SOL_ROUTE_ROWMAX,
+                rule,
                 float(tau) if beta is None else 0.0, 0.0 if beta is None else float(beta),
                 0 if sinks is None else int(sinks[0]), 0 if sinks is None else int(sinks[1]))
             rc = lib().sol_attn_forward_ex(

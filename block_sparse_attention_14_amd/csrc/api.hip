@@ -14,7 +14,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: [header words | item costs | item order | pooled queries].
 struct WsLayout {
-  size_t cost, perm, qpool, khi16, klo16, vbar16, total;
+  size_t cost, perm, qpool, khi16, klo16, vbar16, kstats, total;
 };
 
 WsLayout ws_layout(int BH, int N, int d) {
@@ -27,7 +27,8 @@ WsLayout ws_layout(int BH, int N, int d) {
   w.khi16 = round_up(w.qpool + (size_t)BH * Nq * (size_t)d * 4, 256);
   w.klo16 = round_up(w.khi16 + (size_t)BH * Nq * (size_t)d * 2, 256);
   w.vbar16 = round_up(w.klo16 + (size_t)BH * Nq * (size_t)d * 2, 256);
-  w.total = round_up(w.vbar16 + (size_t)BH * Nq * (size_t)d * 2, 256);
+  w.kstats = round_up(w.vbar16 + (size_t)BH * Nq * (size_t)d * 2, 256);
+  w.total = round_up(w.kstats + (size_t)BH * 2 * (size_t)d * 4, 256);
   return w;
 }
 
@@ -89,7 +90,7 @@ hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d
 int check_route(const sol_attn_route& r, int N, int Bk) {
   if (r.rule == SOL_ROUTE_ROWMAX) {
     if (check_tau(r.tau) != SOL_OK) return SOL_EINVAL;
-  } else if (r.rule == SOL_ROUTE_GAUSS) {
+  } else if (r.rule == SOL_ROUTE_GAUSS || r.rule == SOL_ROUTE_GAUSS_DIAG) {
     if (!isfinite(r.beta)) return SOL_EINVAL;
   } else {
     return SOL_EINVAL;
@@ -158,6 +159,11 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
     e = sol::launch_to_bf16(kpool, khi16, klo16, vmean, vbar16, (size_t)BH * Nk * d, s);
     if (e != hipSuccess) return SOL_EHIP;
   }
+  float* kstats = reinterpret_cast<float*>(wsb + w.kstats);
+  if (route.rule == SOL_ROUTE_GAUSS_DIAG) {
+    e = sol::launch_kstats(kpool, kstats, BH, Nk, d, s);
+    if (e != hipSuccess) return SOL_EHIP;
+  }
 
   sol::FwdParams p;
   p.q = q16;
@@ -177,7 +183,8 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   p.nwords = (Nk + 31) / 32;
   p.rule = route.rule;
   p.tau = route.rule == SOL_ROUTE_ROWMAX ? route.tau : 0.f;
-  p.beta = route.rule == SOL_ROUTE_GAUSS ? route.beta : 0.f;
+  p.beta = route.rule != SOL_ROUTE_ROWMAX ? route.beta : 0.f;
+  p.kstats = kstats;
   p.sink_lo = route.sink_count > 0 ? route.sink_first : 0;
   p.sink_hi = route.sink_count > 0 ? route.sink_first + route.sink_count : 0;
   p.proxy_scale = (float)(1.0 / sqrt((double)d));
@@ -250,6 +257,7 @@ int sol_attn_mask_threshold(const void* q, const float* kpool, int B, int H, int
   int rc = check_mask(q, kpool, B, H, N, d, Bq, Bk, kept_bitmap);
   if (rc != SOL_OK) return rc;
   if (!route || check_route(*route, N, Bk) != SOL_OK) return SOL_EINVAL;
+  if (route->rule == SOL_ROUTE_GAUSS_DIAG) return SOL_EUNSUPPORTED;
   sol::MaskParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.kpool = kpool;

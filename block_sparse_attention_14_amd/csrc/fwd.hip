@@ -348,7 +348,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     // beta * std of the row (population statistics over the key blocks; the
     // row is on chip, so both come exactly from it in two passes)
     float thA = MA - p.tau, thB = MB - p.tau;
-    if (p.rule == SOL_ROUTE_GAUSS) {
+    if (p.rule == SOL_ROUTE_GAUSS_DIAG) {
+      // mean and (diagonal-estimate) variance of the rows from the pooled-key
+      // statistics of the head: known without the rows themselves
+      float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;
+      if (tid < D) {
+        const rsrc_t rs = make_rsrc(p.kstats + (size_t)bh * 2 * D, 2 * D * 4);
+        const float mu = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, 0, 0));
+        const float var = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (D + tid) * 4, 0, 0));
+        const float x0 = sm.qbar[0][tid], x1 = sm.qbar[1][tid];
+        a0 = x0 * mu;
+        b0 = x0 * x0 * var;
+        a1 = x1 * mu;
+        b1 = x1 * x1 * var;
+      }
+      a0 = wave_sum(a0);
+      b0 = wave_sum(b0);
+      a1 = wave_sum(a1);
+      b1 = wave_sum(b1);
+      if (lane == 0) {
+        sm.gred[0][wid] = a0;
+        sm.gred[0][4 + wid] = b0;
+        sm.gred[1][wid] = a1;
+        sm.gred[1][4 + wid] = b1;
+      }
+      __syncthreads();
+      const float inv_d = p.proxy_scale * p.proxy_scale;
+      thA = ((sm.gred[0][0] + sm.gred[0][1]) + (sm.gred[0][2] + sm.gred[0][3])) * p.proxy_scale +
+            p.beta * sqrtf(((sm.gred[0][4] + sm.gred[0][5]) + (sm.gred[0][6] + sm.gred[0][7])) * inv_d);
+      thB = ((sm.gred[1][0] + sm.gred[1][1]) + (sm.gred[1][2] + sm.gred[1][3])) * p.proxy_scale +
+            p.beta * sqrtf(((sm.gred[1][4] + sm.gred[1][5]) + (sm.gred[1][6] + sm.gred[1][7])) * inv_d);
+    } else if (p.rule == SOL_ROUTE_GAUSS) {
       float sA = 0.f, sB = 0.f;
       for (int j = tid; j < Nk; j += kThreads) {
         sA += wrow0[j];

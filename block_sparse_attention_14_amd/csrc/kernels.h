@@ -53,6 +53,7 @@ struct FwdParams {
   const uint16_t* khi16;   // bf16 [BH][Nk][d] pooled keys, high part (row_corr)
   const uint16_t* klo16;   // bf16 [BH][Nk][d] pooled keys, the remainder (row_corr)
   const uint16_t* vbar16;  // bf16 [BH][Nk][d] pooled values (row_corr)
+  const float* kstats;     // fp32 [BH][2][d]: mean and variance of the pooled keys (GAUSS_DIAG)
 };
 
 // Up to three bf16 [BH][N][d] tensors pooled per 64-token block into fp32
@@ -71,6 +72,10 @@ hipError_t launch_pool(const PoolSet& set, int BH, int N, int Nk, int d, unsigne
 // carries about 16 significant bits) and b16 = bf16(b), for n values each.
 hipError_t launch_to_bf16(const float* a, uint16_t* a_hi, uint16_t* a_lo, const float* b, uint16_t* b16, size_t n,
                           hipStream_t stream);
+
+// stats[bh][0][c] = mean_j kpool[bh][j][c], stats[bh][1][c] = population
+// variance over j (two passes), one workgroup per head.
+hipError_t launch_kstats(const float* kpool, float* stats, int BH, int Nk, int d, hipStream_t stream);
 
 // Resets the workspace header words (one small kernel).
 hipError_t launch_reset(unsigned* hdr, hipStream_t stream);

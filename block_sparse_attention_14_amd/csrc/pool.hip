@@ -78,6 +78,49 @@ hipError_t launch_to_bf16(const float* a, uint16_t* a_hi, uint16_t* a_lo, const 
   return hipGetLastError();
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void kstats_kernel(const float* __restrict__ kpool, float* __restrict__ stats, int Nk) {
+  constexpr int G = 256 / D;  // row groups
+  __shared__ float part[G][D];
+  __shared__ float mean[D];
+  const int tid = threadIdx.x, c = tid % D, rg = tid / D;
+  const float* kp = kpool + (size_t)blockIdx.x * Nk * D;
+  float s = 0.f;
+  for (int j = rg; j < Nk; j += G) s += kp[(size_t)j * D + c];
+  part[rg][c] = s;
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) t += part[g][tid];
+    mean[tid] = t / (float)Nk;
+  }
+  __syncthreads();
+  const float m = mean[c];
+  float v = 0.f;
+  for (int j = rg; j < Nk; j += G) {
+    const float x = kp[(size_t)j * D + c] - m;
+    v += x * x;
+  }
+  part[rg][c] = v;
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) t += part[g][tid];
+    stats[(size_t)blockIdx.x * 2 * D + tid] = mean[tid];
+    stats[(size_t)blockIdx.x * 2 * D + D + tid] = t / (float)Nk;
+  }
+}
+
+hipError_t launch_kstats(const float* kpool, float* stats, int BH, int Nk, int d, hipStream_t stream) {
+  if (d == 128)
+    hipLaunchKernelGGL(kstats_kernel<128>, dim3(BH), dim3(256), 0, stream, kpool, stats, Nk);
+  else
+    hipLaunchKernelGGL(kstats_kernel<64>, dim3(BH), dim3(256), 0, stream, kpool, stats, Nk);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void reset_kernel(unsigned* hdr) {
   for (int w = threadIdx.x; w < kHdrWords; w += 256) hdr[w] = w == kHdrMin ? 0xffffffffu : 0u;
 }

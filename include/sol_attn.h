@@ -94,7 +94,13 @@ enum {
    * over the key blocks of the row; they equal the pooled-key first and
    * second moment form of App. B "Threshold variance derivation", and are
    * computed here from the proxy row, which stays on chip) */
-  SOL_ROUTE_GAUSS = 1
+  SOL_ROUTE_GAUSS = 1,
+  /* the same threshold with the diagonal estimator of App. B "Diagonal
+   * threshold estimator": mean_j s_ij = qbar_i . m_K / sqrt(d) and
+   * var_j s_ij ~= sum_c qbar_ic^2 v_Kc / d, from the mean m_K and the
+   * per-dimension (population) variance v_K of the head's pooled keys, so the
+   * threshold is known before the proxy row is formed. Forward only. */
+  SOL_ROUTE_GAUSS_DIAG = 2
 };
 
 /* Routing of sol_attn_forward_ex, read from HOST memory during the call. */
@@ -124,8 +130,9 @@ typedef struct sol_attn_stats {
 /* Bytes of device workspace sol_attn_forward and sol_attn_plan need: the
  * work-queue and stats words, one cost and one order slot per work item (a
  * pair of query blocks), the fp32 pooled queries [B][H][Nq][d] of the
- * planning stage, and bf16 copies of the pooled keys and values
- * [B][H][Nk][d] for SOL_F_ROW_CORRECTION. Returns 0 for unsupported sizes. */
+ * planning stage, bf16 copies of the pooled keys and values [B][H][Nk][d]
+ * for SOL_F_ROW_CORRECTION, and the pooled-key statistics [B][H][2][d] of
+ * SOL_ROUTE_GAUSS_DIAG. Returns 0 for unsupported sizes. */
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
 
 /*
@@ -211,7 +218,9 @@ int sol_attn_forward_ex(const void* q, const void* k, const void* v, float* out,
  * Sparsification" compares their cost with on-chip threshold routing).
  *   q          bf16 [B][H][N][d]; kpool fp32 [B][H][Nk][d] (sol_attn_pool)
  *   kept_bitmap device uint32 [B][H][Nq][ceil(Nk/32)], written in full
- * Errors as for sol_attn_forward; SOL_EUNSUPPORTED also when B * H > 65535.
+ * Errors as for sol_attn_forward; SOL_EUNSUPPORTED also when B * H > 65535,
+ * and for SOL_ROUTE_GAUSS_DIAG (its statistics live in the forward's
+ * workspace).
  *
  * sol_attn_mask_threshold: the forward's own routing (pooled queries from the
  * Q tiles, both proxy rows of a pair of query blocks in LDS, the rule and

@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 import block_sparse_attention_14_amd as sa
-from oracle import attend_head, block_means, gauss_threshold, proxy_scores, route
+from oracle import attend_head, block_means, gauss_threshold, gauss_threshold_diag, proxy_scores, route
 from workloads import bf16_bits_to_f64
 
 BITMAP_TIE = 1e-3
@@ -31,19 +31,19 @@ def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 def run_gpu(qb, kb, vb, tau, flags=0, runner: Optional[sa.SolAttention] = None, device="cuda", beta=None,
-            sinks=None):
+            sinks=None, diag=False):
     """Returns (out fp32 numpy, keep bool [B,H,Nq,Nk], stats dict)."""
     B, H, N, d = qb.shape
     q, k, v = (to_device_bf16(x, device) for x in (qb, kb, vb))
     runner = runner or sa.SolAttention(B, H, N, d, device)
     bm = torch.zeros(sa.bitmap_shape(B, H, N), dtype=torch.int32, device=device)
-    out = runner(q, k, v, tau, flags=flags, bitmap=bm, beta=beta, sinks=sinks)
+    out = runner(q, k, v, tau, flags=flags, bitmap=bm, beta=beta, sinks=sinks, diag=diag)
     torch.cuda.synchronize()
     keep = sa.unpack_bitmap(bm, -(-N // 64))
     return out.cpu().numpy(), keep, runner.read_stats()
 
 
-def oracle_route(q, k, tau, beta=None, sinks=None):
+def oracle_route(q, k, tau, beta=None, sinks=None, diag=False):
     """fp64 proxy scores, thresholds, keep mask and the forced-sink mask of one head."""
     d = q.shape[1]
     qbar, _ = block_means(q, 64)
@@ -53,7 +53,7 @@ def oracle_route(q, k, tau, beta=None, sinks=None):
         M, keep = route(s, tau)
         theta = M - tau
     else:
-        theta = gauss_threshold(qbar, kbar, d, beta)
+        theta = (gauss_threshold_diag if diag else gauss_threshold)(qbar, kbar, d, beta)
         keep = s >= theta[:, None]
     forced = np.zeros_like(keep)
     if sinks is not None and sinks[1] > 0:
@@ -79,10 +79,10 @@ def check_bitmap(gpu_keep: np.ndarray, s: np.ndarray, theta: np.ndarray, keep: n
 
 
 def check_head(qb, kb, vb, out_gpu, keep_gpu, tau, query_blocks: Optional[Iterable[int]] = None, where="",
-               beta=None, sinks=None, row_correction=False):
+               beta=None, sinks=None, row_correction=False, diag=False):
     """Bitmap on every query block of the head; outputs on `query_blocks` (all if None)."""
     q, k, v = (bf16_bits_to_f64(x) for x in (qb, kb, vb))
-    s, theta, keep, forced = oracle_route(q, k, tau, beta, sinks)
+    s, theta, keep, forced = oracle_route(q, k, tau, beta, sinks, diag)
     check_bitmap(keep_gpu, s, theta, keep, forced, beta is None, where)
     r = attend_head(q, k, v, 64, 64, tau, keep_override=keep_gpu, query_blocks=query_blocks,
                     row_correction=row_correction)

@@ -151,7 +151,7 @@ def fwd_ex(route, bitmap=None, **over):
 
 @pytest.mark.parametrize("route,bitmap,code", [
     (None, None, sa.SOL_EINVAL),
-    ((2, 1.0, 0.0, 0, 0), None, sa.SOL_EINVAL),                       # unknown rule
+    ((7, 1.0, 0.0, 0, 0), None, sa.SOL_EINVAL),                       # unknown rule
     ((0, -1.0, 0.0, 0, 0), None, sa.SOL_EINVAL),                      # negative tau
     ((0, math.nan, 0.0, 0, 0), None, sa.SOL_EINVAL),
     ((1, 0.0, math.inf, 0, 0), None, sa.SOL_EINVAL),                  # beta not finite
@@ -204,3 +204,10 @@ def test_mask_builders_reject_bad_route_bitmap_workspace():
     assert L.sol_attn_mask_topk(*a, 4, P, P + 64, 1 << 40, None) == sa.SOL_EINVAL
     assert L.sol_attn_mask_topk(*a, 4, P, P, 64, None) == sa.SOL_EWORKSPACE
     assert L.sol_attn_mask_topp(*a, ctypes.c_float(math.nan), P, P, 1 << 40, None) == sa.SOL_EINVAL
+
+
+def test_forward_ex_accepts_diag_rule_arguments():
+    # a valid diagonal-estimator route passes validation (the tiny workspace fails next)
+    assert fwd_ex((2, 0.0, 1.0, 0, 0)) == sa.SOL_EWORKSPACE
+    assert fwd_ex((2, 0.0, math.inf, 0, 0)) == sa.SOL_EINVAL
+    assert fwd_ex((3, 0.0, 1.0, 0, 0)) == sa.SOL_EINVAL

@@ -33,13 +33,13 @@ def _report(name, tag, err):
 
 
 def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, seed=0, beta=None, sinks=None,
-                 flags=0):
+                 flags=0, diag=False):
     x = inputs or make_inputs(wl)
-    out, keep, stats = run_gpu(x["q"], x["k"], x["v"], tau, beta=beta, sinks=sinks, flags=flags)
+    out, keep, stats = run_gpu(x["q"], x["k"], x["v"], tau, beta=beta, sinks=sinks, flags=flags, diag=diag)
     check_stats(stats, keep, wl.N)
     rng = np.random.default_rng(seed)
     worst = 0.0
-    tag = f"tau={tau}" if beta is None else f"beta={beta}"
+    tag = f"tau={tau}" if beta is None else f"beta={beta}" + (" diag" if diag else "")
     if sinks is not None:
         tag += f" sinks={sinks}"
     rowc = bool(flags & sa.SOL_F_ROW_CORRECTION)
@@ -50,7 +50,7 @@ def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, see
             qbs = None if query_blocks_per_head is None else sample_blocks(wl.Nq, rng, query_blocks_per_head)
             worst = max(worst, check_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], out[b, h], keep[b, h],
                                           tau, qbs, where=f"{wl.name} b={b} h={h} {tag}", beta=beta, sinks=sinks,
-                                          row_correction=rowc))
+                                          row_correction=rowc, diag=diag))
     _report(wl.name, tag, worst)
     return out, keep, stats
 
@@ -329,3 +329,39 @@ def test_row_correction_planned_matches_one_shot():
     out = r(q, k, v, 2.0, flags=RC | sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# Gaussian threshold with the diagonal estimator (threshold from pooled-key
+# statistics, known before the proxy row)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("beta", [-0.5, 0.5, 2.0])
+def test_gauss_diag_rule_tiny(beta):
+    _full_parity(get_workload("tiny_fp32"), 0.0, beta=beta, diag=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 130, 1000])
+def test_gauss_diag_rule_ragged(N, d):
+    _full_parity(_custom(N, d, H=2, seed=N + d + 13), 0.0, beta=1.0, diag=True)
+
+
+def test_gauss_diag_rule_video(video32k):
+    _full_parity(get_workload("image_dit_4k"), 0.0, beta=1.5, diag=True)
+    _full_parity(get_workload("video_dit_32k"), 0.0, video32k, query_blocks_per_head=2, seed=9, beta=3.0, diag=True,
+                 sinks=(0, 1), flags=sa.SOL_F_ROW_CORRECTION)
+
+
+def test_mask_threshold_rejects_diag():
+    wl = _custom(1000, 128, H=1)
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    kp, _ = sa.pool(k, v)
+    import ctypes
+    from block_sparse_attention_14_amd import _lib
+    route = _lib.sol_attn_route(sa.SOL_ROUTE_GAUSS_DIAG, 0.0, 1.0, 0, 0)
+    bm = torch.zeros(sa.bitmap_shape(1, 1, 1000), dtype=torch.int32, device=q.device)
+    rc = sa.lib().sol_attn_mask_threshold(q.data_ptr(), kp.data_ptr(), 1, 1, 1000, 128, 64, 64, ctypes.byref(route),
+                                          bm.data_ptr(), None)
+    assert rc == sa.SOL_EUNSUPPORTED
