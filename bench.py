@@ -5,8 +5,8 @@
 A step is one full pass of the hot path over the video-DiT layer
 (B=1, H=12, 21x30x52 grid -> N=32760, d=128, bf16 inputs resident in HBM):
 the pooling pre-pass plus the fused routing / exact / correction kernel, one
-C-ABI call. The optional planning stage (sol_attn_plan) is timed alongside
-under "planned" for every tau. The headline tau is 8; taus 2, 4 and +inf (the same kernel run
+C-ABI call; for a finite tau it includes the planning kernels (item costs
+and queue order, sol_attn_plan), which are also timed on their own. The headline tau is 8; taus 2, 4 and +inf (the same kernel run
 dense) are reported alongside. Prints ONE JSON line.
 
 value = dense-equivalent TFLOP/s = 4*B*H*N^2*d / (seconds per call).
@@ -137,32 +137,32 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         r["call_flushed"] = elapsed(ev)
-        # per-kernel split of the same call: the pool pass (k, v), then the
-        # fused kernel on the pooled buffers (after its one-workgroup header reset)
-        ev1, ev2 = events(steps), events(steps)
-        for (a, b), (c, e) in zip(ev1, ev2):
+        # per-kernel split of the same call: the pool pass (k, v), the planning
+        # kernels (item costs, queue order), then the fused kernel alone
+        ev1, ev2, ev3 = events(steps), events(steps), events(steps)
+        for (a, b), (c, e), (f, g) in zip(ev1, ev2, ev3):
             a.record(stream)
             sa.pool(k, v, kpool=runner.kpool, vmean=runner.vmean)
             b.record(stream)
             c.record(stream)
-            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED)
-            e.record(stream)
-        torch.cuda.synchronize()
-        r["pool"], r["fwd"] = elapsed(ev1), elapsed(ev2)
-        stats = runner.read_stats()
-        # the optional planning stage (pooled q, item costs, outliers first),
-        # then the fused kernel on the planned order
-        n = max(3, steps // 2)
-        ev1, ev2 = events(n), events(n)
-        for (a, b), (c, e) in zip(ev1, ev2):
-            a.record(stream)
             runner.plan(q, tau)
-            b.record(stream)
-            c.record(stream)
-            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
             e.record(stream)
+            f.record(stream)
+            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+            g.record(stream)
         torch.cuda.synchronize()
-        r["plan"], r["fwd_planned"] = elapsed(ev1), elapsed(ev2)
+        r["pool"], r["plan"], r["fwd"] = elapsed(ev1), elapsed(ev2), elapsed(ev3)
+        stats = runner.read_stats()
+        # the fused kernel with its items in sequence (the identity order)
+        n = max(3, steps // 2)
+        runner.plan(q, math.inf)
+        ev = events(n)
+        for a, b in ev:
+            a.record(stream)
+            runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+            b.record(stream)
+        torch.cuda.synchronize()
+        r["fwd_sequence_order"] = elapsed(ev)
         # the whole call with the token-to-block (per-row) correction
         ev = events(n)
         for a, b in ev:
@@ -204,8 +204,7 @@ def main():
         steps = args.steps if tau == args.tau else max(3, args.steps // 2)
         r, wall, stats = measure(tau, steps, args.warmup if tau == args.tau else 2)
         ms_call = float(np.mean(r["call"]))
-        ms_pool, ms_fwd = float(np.median(r["pool"])), float(np.median(r["fwd"]))
-        ms_plan, ms_fwd_planned = float(np.median(r["plan"])), float(np.median(r["fwd_planned"]))
+        ms_pool, ms_plan, ms_fwd = (float(np.median(r[x])) for x in ("pool", "plan", "fwd"))
         flops, nbytes = fwd_algorithmic(tau, stats)
         t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
         t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
@@ -217,8 +216,8 @@ def main():
             "ms_pool": round(ms_pool, 4),
             "ms_fwd": round(ms_fwd, 4),
             "fwd_ms": pct(r["fwd"]),
-            "planned": {"ms_plan": round(ms_plan, 4), "ms_fwd": round(ms_fwd_planned, 4),
-                        "ms_per_call": round(ms_pool + ms_plan + ms_fwd_planned, 4)},
+            "ms_plan": round(ms_plan, 4),
+            "fwd_ms_items_in_sequence": round(float(np.median(r["fwd_sequence_order"])), 4),
             "row_correction_ms_per_call": round(float(np.median(r["call_row_correction"])), 4),
             "dense_equiv_tflops": round(dense / (ms_call * 1e-3) / 1e12, 1),
             "kept_block_pct": round(kept_pct, 3),
@@ -347,12 +346,13 @@ def main():
         "ms_per_call": round(ms_call, 4),
         "kept_block_pct": round(kept_pct, 3),
         "ms_pool": round(ms_pool, 4),
+        "ms_plan": round(per_tau["inf" if math.isinf(args.tau) else f"{args.tau:g}"]["ms_plan"], 4),
         "ms_fwd": round(ms_fwd, 4),
         "pool_gbs": per_tau["inf" if math.isinf(args.tau) else f"{args.tau:g}"]["pool_gbs"],
         "device_copy_gbs": round(copy_gbs, 1),
         "roofline": {
             "kernel": "fwd_kernel<128> (fused routing + kept MFMA + correction); HIP events around the "
-                      "fused launch and its one-workgroup header reset",
+                      "fused launch alone (planned workspace)",
             "bound": bound,
             "achieved": round(achieved, 1),
             "peak": peak,

@@ -12,9 +12,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: [header words | item costs | item order | pooled queries].
+// Workspace: [header words | item costs | item order | pooled-key copies and
+// statistics of the optional modes].
 struct WsLayout {
-  size_t cost, perm, qpool, khi16, klo16, vbar16, kstats, total;
+  size_t cost, perm, khi16, klo16, vbar16, kstats, total;
 };
 
 WsLayout ws_layout(int BH, int N, int d) {
@@ -23,8 +24,7 @@ WsLayout ws_layout(int BH, int N, int d) {
   WsLayout w;
   w.cost = sol::kHdrWords * 4;
   w.perm = round_up(w.cost + 4 * items, 256);
-  w.qpool = round_up(w.perm + 4 * items, 256);
-  w.khi16 = round_up(w.qpool + (size_t)BH * Nq * (size_t)d * 4, 256);
+  w.khi16 = round_up(w.perm + 4 * items, 256);
   w.klo16 = round_up(w.khi16 + (size_t)BH * Nq * (size_t)d * 2, 256);
   w.vbar16 = round_up(w.klo16 + (size_t)BH * Nq * (size_t)d * 2, 256);
   w.kstats = round_up(w.vbar16 + (size_t)BH * Nq * (size_t)d * 2, 256);
@@ -37,6 +37,12 @@ WsLayout ws_layout(int BH, int N, int d) {
 constexpr int kMaxOrderedItems = 1 << 20;
 
 bool use_order(float tau, int nitems) { return !isinf(tau) && nitems > 1 && nitems <= kMaxOrderedItems; }
+
+// The forward plans its work order by itself from this tau on (row-max rule):
+// below it the budgets of the query blocks are close enough that items in
+// sequence finish together (measured on video-DiT layers: planning costs
+// about 20 us a call and pays back only from tau ~ 6 up).
+constexpr float kPlanMinTau = 6.f;
 
 // Largest B * H of the launches whose grid has one row per head (plan, masks).
 constexpr int kMaxGridHeads = 65535;
@@ -64,26 +70,20 @@ sol_attn_route rowmax_route(float tau) {
   return r;
 }
 
-// Planning: pooled queries into the workspace with a clean header, then (for
-// finite tau) the item costs and the order of each queue, else the identity
-// order.
-hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d, float tau, void* ws, hipStream_t s) {
+// Planning: per-item costs and the order of each queue into the workspace
+// (row-max rule, finite tau, sizes the sort handles), else the identity
+// order, which every later planned forward may still read.
+hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d, float tau, void* ws, hipStream_t s,
+                     bool* ordered) {
   const WsLayout w = ws_layout(BH, N, d);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   const int Nq = (N + 63) / 64, Nk = Nq;
-  sol::PoolSet set;
-  set.src[0] = q;
-  set.dst[0] = reinterpret_cast<float*>(wsb + w.qpool);
-  set.n = 1;
-  hipError_t e = sol::launch_pool(set, BH, N, Nk, d, static_cast<unsigned*>(ws), s);
-  if (e != hipSuccess) return e;
   unsigned* perm = reinterpret_cast<unsigned*>(wsb + w.perm);
   const int nitems = sol::forward_items(BH, Nq);
-  if (use_order(tau, nitems) && BH <= kMaxGridHeads)
-    return sol::launch_plan(reinterpret_cast<const float*>(wsb + w.qpool), kpool,
-                            reinterpret_cast<unsigned*>(wsb + w.cost), perm, BH, Nq, Nk, d, tau,
+  *ordered = use_order(tau, nitems) && BH <= kMaxGridHeads;
+  if (*ordered)
+    return sol::launch_plan(q, kpool, reinterpret_cast<unsigned*>(wsb + w.cost), perm, BH, N, Nq, Nk, d, tau,
                             (float)(1.0 / sqrt((double)d)), s);
-  // a valid order even so: a planned forward at another tau may still read it
   return sol::launch_identity_order(perm, nitems, s);
 }
 
@@ -140,16 +140,27 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   if (flags & SOL_F_PLANNED) {
     // the workspace holds a valid order from sol_attn_plan(), as a previous call left it
     perm = reinterpret_cast<const unsigned*>(wsb + w.perm);
-  } else if (flags & SOL_F_POOLED) {
-    e = sol::launch_reset(static_cast<unsigned*>(ws), s);
   } else {
-    sol::PoolSet set;
-    set.src[0] = k16;
-    set.dst[0] = kpool;
-    set.src[1] = v16;
-    set.dst[1] = vmean;
-    set.n = 2;
-    e = sol::launch_pool(set, BH, N, Nk, d, static_cast<unsigned*>(ws), s);
+    if (flags & SOL_F_POOLED) {
+      e = sol::launch_reset(static_cast<unsigned*>(ws), s);
+    } else {
+      sol::PoolSet set;
+      set.src[0] = k16;
+      set.dst[0] = kpool;
+      set.src[1] = v16;
+      set.dst[1] = vmean;
+      set.n = 2;
+      e = sol::launch_pool(set, BH, N, Nk, d, static_cast<unsigned*>(ws), s);
+    }
+    // row-max routing with a large finite tau, where per-block budgets spread
+    // widely: plan the order of the work (elsewhere the items go in sequence;
+    // the order never changes the result)
+    if (e == hipSuccess && route.rule == SOL_ROUTE_ROWMAX && route.tau >= kPlanMinTau &&
+        use_order(route.tau, nitems) && BH <= kMaxGridHeads) {
+      bool ordered = false;
+      e = plan_impl(q16, kpool, BH, N, d, route.tau, ws, s, &ordered);
+      perm = reinterpret_cast<const unsigned*>(wsb + w.perm);
+    }
   }
   if (e != hipSuccess) return SOL_EHIP;
   uint16_t* khi16 = reinterpret_cast<uint16_t*>(wsb + w.khi16);
@@ -316,8 +327,10 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
   const int rc = check_sizes(B, H, N, d, Bq, Bk);
   if (rc != SOL_OK) return rc;
   if (workspace_bytes < sol_attn_workspace_bytes(B, H, N, d, Bq, Bk)) return SOL_EWORKSPACE;
-  const hipError_t e = plan_impl(static_cast<const uint16_t*>(q), kpool, B * H, N, d, tau, workspace,
-                                 reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = sol::launch_reset(static_cast<unsigned*>(workspace), s);
+  bool ordered = false;
+  if (e == hipSuccess) e = plan_impl(static_cast<const uint16_t*>(q), kpool, B * H, N, d, tau, workspace, s, &ordered);
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 

@@ -589,11 +589,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         for (int kt = 0; kt < 4; ++kt) {
           st[0][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
           st[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // K operands one step ahead of the MFMAs that use them
+        auto kread = [&](int i) {
+          return as_bf16x8(*reinterpret_cast<const uint4*>(stage + 16 * (i / NDS) * G::RB + koff[i % NDS]));
+        };
+        bf16x8 kcur = kread(0);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
           for (int ds = 0; ds < NDS; ++ds) {
-            const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(stage + 16 * kt * G::RB + koff[ds]));
+            const int i = kt * NDS + ds;
+            const bf16x8 a = kcur;
+            if (i + 1 < 4 * NDS) kcur = kread(i + 1);
+            __builtin_amdgcn_sched_barrier(0);
             st[0][kt] = mfma16x16x32(a, qop[0][ds], st[0][kt]);
             st[1][kt] = mfma16x16x32(a, qop[1][ds], st[1][kt]);
+            __builtin_amdgcn_sched_barrier(0);
             if (kPooled) {  // the remainder part of the pooled keys, one tile further on
               const bf16x8 b =
                   as_bf16x8(*reinterpret_cast<const uint4*>(stage + G::TILE + 16 * kt * G::RB + koff[ds]));
@@ -688,16 +700,30 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         // 32ks + 4g + e and 32ks + 16 + 4g + e give exactly the keys of the P^T
         // slots; each V^T operand serves both query tiles
         const unsigned char* vstage = kPooled ? stB : stage;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        // V^T operands of the next 16 rows of d read while this slice's MFMAs run
+        auto vread = [&](int dt, uint2 (&o)[4]) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const uint2 lo = ld_tr(vstage + voff[dt] + 32 * ks * G::RB);
-            const uint2 hi = ld_tr(vstage + voff[dt] + (32 * ks + 16) * G::RB);
-            const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+            o[2 * ks] = ld_tr(vstage + voff[dt] + 32 * ks * G::RB);
+            o[2 * ks + 1] = ld_tr(vstage + voff[dt] + (32 * ks + 16) * G::RB);
+          }
+        };
+        uint2 vc[4], vn[4];
+        vread(0, vc);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          if (dt + 1 < NDT) vread(dt + 1, vn);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 a = as_bf16x8(make_uint4(vc[2 * ks].x, vc[2 * ks].y, vc[2 * ks + 1].x, vc[2 * ks + 1].y));
             acc[0][dt] = mfma16x16x32(a, pb[0][ks], acc[0][dt]);
             acc[1][dt] = mfma16x16x32(a, pb[1][ks], acc[1][dt]);
           }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) vc[e2] = vn[e2];
+        }
       };
 
       // Every barrier below is preceded by an explicit wait for all of this

@@ -81,10 +81,10 @@ hipError_t launch_kstats(const float* kpool, float* stats, int BH, int Nk, int d
 hipError_t launch_reset(unsigned* hdr, hipStream_t stream);
 
 // Per-item cost estimates (union of the kept sets of each pair of query
-// blocks) and the order of each queue's range: items above twice the queue's
-// mean cost first, longest first, then the rest in sequence.
+// blocks, from sampled query means) and the order of each queue's range:
+// head-major, then its last third heaviest first.
 // perm[rank] = item, with rank and item in the same queue range.
-hipError_t launch_plan(const float* qpool, const float* kpool, unsigned* cost, unsigned* perm, int BH, int Nq,
+hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, int BH, int N, int Nq,
                        int Nk, int d, float tau, float proxy_scale, hipStream_t stream);
 
 // perm[i] = i for every item (the order of a plan that does not sort).

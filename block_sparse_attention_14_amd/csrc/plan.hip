@@ -1,4 +1,4 @@
-// Work ordering for the fused kernel: outliers first.
+// Work ordering for the fused kernel: the tail of each queue heaviest first.
 //
 // The per-query-block budgets of threshold routing vary by two orders of
 // magnitude (page "Sol-Attn: Accelerating Video Generation Inference via
@@ -6,12 +6,12 @@
 // routing": dynamic, query-dependent budgets). A persistent grid that takes
 // items in sequence order ends with a few workgroups finishing the heaviest
 // items while the rest idle. These two small kernels estimate every item's
-// cost (the size of the union of its two blocks' kept lists) and move the
-// outliers of each XCD queue to its front, longest first, so the heavy items
-// start early while the rest keep their head-major order.
+// cost (the size of the union of its two blocks' kept lists) and order each
+// XCD queue: head-major first, then its last third heaviest first, so the
+// queue ends on light items.
 //
-// The estimate uses bf16 MFMA products of the pooled queries and keys: it
-// only orders work. The fused kernel routes every item itself, in fp32, and
+// The estimate uses bf16 MFMA products of sampled query means and the pooled
+// keys: it only orders work. The fused kernel routes every item itself, in fp32, and
 // nothing here influences which blocks it keeps. Only one count per item is
 // written to device memory; no proxy scores or block indices are.
 #include <math.h>
@@ -25,11 +25,14 @@ namespace {
 
 // Score tiles a wave keeps in registers between the max pass and the count
 // pass; tiles beyond these are recomputed in the count pass.
-constexpr int kCached = 8;
-constexpr int kBatch = 4;  // tiles whose loads are in flight together
+constexpr int kCached = 4;
+constexpr int kBatch = 2;       // tiles whose loads are in flight together
+constexpr int kPlanWaves = 8;   // waves per planning workgroup, splitting the key tiles
+constexpr int kPlanQ = 32;      // query blocks per workgroup: two 16-column tiles per wave
+constexpr int kSampleStride = 4;  // every 4th row of a query block enters its estimated mean
 
-// Loads (pass 1) of one 16x16 S^T tile of pooled vectors: lane (g, c16)
-// fetches pooled key jt0 + c16, columns 32 ds + 8 g .. +7 (zero past Nk).
+// Loads of one 16x16 S^T tile of pooled keys: lane (g, c16) fetches pooled
+// key jt0 + c16, columns 32 ds + 8 g .. +7 (zero past Nk).
 template <int D>
 __device__ __forceinline__ void tile_load(const float* kp, int Nk, int jt0, int c16, int g, float4 (&x)[D / 16]) {
   const int j = jt0 + c16;
@@ -45,139 +48,187 @@ __device__ __forceinline__ void tile_load(const float* kp, int Nk, int jt0, int 
   }
 }
 
-// S^T tile = K̄ Q̄^T in bf16 MFMA from the loaded pooled keys.
+// The two S^T column tiles (query blocks 0-15 and 16-31 of the workgroup)
+// against one tile of pooled keys, in bf16 MFMA.
 template <int D>
-__device__ __forceinline__ f32x4 tile_mma(const float4 (&x)[D / 16], const bf16x8 (&qop)[D / 32]) {
-  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void tile_mma(const float4 (&x)[D / 16], const bf16x8 (&qop)[2][D / 32], f32x4 (&s)[2]) {
+  s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) {
     const float4 a = x[2 * ds], b = x[2 * ds + 1];
-    const uint4 u = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                               pack_bf16x2(b.z, b.w));
-    s = mfma16x16x32(as_bf16x8(u), qop[ds], s);
+    const bf16x8 k = as_bf16x8(make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                                          pack_bf16x2(b.z, b.w)));
+    s[0] = mfma16x16x32(k, qop[0][ds], s[0]);
+    s[1] = mfma16x16x32(k, qop[1][ds], s[1]);
   }
-  return s;
 }
 
-// grid (ceil(Nq / 16), BH), 256 threads. All four waves serve the same 16
-// query blocks (lane column c16); wave w takes key tiles w, w + 4, ...
-// Pass 1 finds each block's maximum, pass 2 counts, per pair of blocks, the
-// key blocks that either block keeps. Both reductions meet in LDS.
+// grid (ceil(Nq / 32), BH), 512 threads. The workgroup estimates the pooled
+// query of each of its 32 query blocks from every 4th row (a scheduling
+// estimate: the forward pools all rows itself), then all eight waves serve
+// the same 32 query blocks, wave w taking key tiles w, w + 8, ... Pass 1 finds
+// each block's maximum, pass 2 counts, per pair of blocks, the key blocks
+// that either block keeps. Both reductions meet in LDS.
 template <int D>
-__global__ __launch_bounds__(256) void plan_kernel(const float* __restrict__ qpool, const float* __restrict__ kpool,
-                                                   unsigned* __restrict__ cost, int Nq, int Nk, float tau,
+__global__ __launch_bounds__(64 * kPlanWaves) void plan_kernel(const uint16_t* __restrict__ q,
+                                                                const float* __restrict__ kpool,
+                                                   unsigned* __restrict__ cost, int N, int Nq, int Nk, float tau,
                                                    float proxy_scale) {
-  __shared__ float red[4][16];
-  __shared__ unsigned cred[4][16];
-  const int bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int q = 16 * blockIdx.x + c16;  // this lane's query block (column of S^T)
-  const float* kp = kpool + (size_t)bh * Nk * D;
+  constexpr int TPB = 64 * kPlanWaves / kPlanQ;  // threads per query block
+  constexpr int CPT = D / TPB;                   // columns per thread
+  __shared__ float qs[kPlanQ][D];
+  __shared__ float red[kPlanWaves][kPlanQ];
+  __shared__ unsigned cred[kPlanWaves][kPlanQ];
+  const int bh = blockIdx.y, q0 = kPlanQ * blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 
-  bf16x8 qop[D / 32];
+  // sampled means: thread t covers block t / TPB, columns (t % TPB) * CPT .. +CPT-1
+  {
+    const int b = tid / TPB, c0 = (tid % TPB) * CPT, qb = q0 + b;
+    const int nb = qb < Nq ? min(kBlk, N - qb * kBlk) : 0;
+    float acc[CPT];
 #pragma unroll
-  for (int ds = 0; ds < D / 32; ++ds) {
-    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-    if (q < Nq) {
-      const float4* row = reinterpret_cast<const float4*>(qpool + ((size_t)bh * Nq + q) * D + 32 * ds + 8 * g);
-      x0 = row[0];
-      x1 = row[1];
+    for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+    const uint16_t* rows = q + ((size_t)bh * N + (size_t)qb * kBlk) * D + c0;
+#pragma unroll
+    for (int r = 0; r < kBlk; r += kSampleStride) {
+      if (r < nb) {
+        if constexpr (CPT == 8) {
+          const uint4 u = *reinterpret_cast<const uint4*>(rows + (size_t)r * D);
+          acc[0] += bf16lo(u.x); acc[1] += bf16hi(u.x);
+          acc[2] += bf16lo(u.y); acc[3] += bf16hi(u.y);
+          acc[4] += bf16lo(u.z); acc[5] += bf16hi(u.z);
+          acc[6] += bf16lo(u.w); acc[7] += bf16hi(u.w);
+        } else {
+          static_assert(CPT == 4, "8 or 4 columns per thread");
+          const uint2 u = *reinterpret_cast<const uint2*>(rows + (size_t)r * D);
+          acc[0] += bf16lo(u.x); acc[1] += bf16hi(u.x);
+          acc[2] += bf16lo(u.y); acc[3] += bf16hi(u.y);
+        }
+      }
     }
-    qop[ds] = as_bf16x8(make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
-                                   pack_bf16x2(x1.z, x1.w)));
+    const float inv = nb > 0 ? 1.f / (float)((nb + kSampleStride - 1) / kSampleStride) : 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) qs[b][c0 + c] = acc[c] * inv;
   }
+  __syncthreads();
+
+  const int g = lane >> 4, c16 = lane & 15;
+  const float* kp = kpool + (size_t)bh * Nk * D;
+  bf16x8 qop[2][D / 32];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      const float* r = &qs[16 * ct + c16][32 * ds + 8 * g];
+      qop[ct][ds] = as_bf16x8(make_uint4(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                                         pack_bf16x2(r[6], r[7])));
+    }
   const int njt = (Nk + 15) / 16;
   auto valid = [&](int jt, int i) { return 16 * jt + 4 * g + i < Nk; };
 
   // pass 1: maxima; the first kCached tiles of this wave stay in registers
-  float mx = -INFINITY;
-  f32x4 sc[kCached];
+  float mx[2] = {-INFINITY, -INFINITY};
+  f32x4 sc[kCached][2];
 #pragma unroll
   for (int c0 = 0; c0 < kCached; c0 += kBatch) {
     float4 x[kBatch][D / 16];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) tile_load<D>(kp, Nk, 16 * (wid + 4 * (c0 + u)), c16, g, x[u]);
+    for (int u = 0; u < kBatch; ++u) tile_load<D>(kp, Nk, 16 * (wid + kPlanWaves * (c0 + u)), c16, g, x[u]);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int jt = wid + 4 * (c0 + u);
-      sc[c0 + u] = tile_mma<D>(x[u], qop);
+      const int jt = wid + kPlanWaves * (c0 + u);
+      tile_mma<D>(x[u], qop, sc[c0 + u]);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (jt < njt && valid(jt, i)) mx[ct] = fmaxf(mx[ct], sc[c0 + u][ct][i]);
+    }
+  }
+  for (int jt = wid + kPlanWaves * kCached; jt < njt; jt += kPlanWaves) {
+    float4 x[D / 16];
+    tile_load<D>(kp, Nk, 16 * jt, c16, g, x);
+    f32x4 s[2];
+    tile_mma<D>(x, qop, s);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (jt < njt && valid(jt, i)) mx = fmaxf(mx, sc[c0 + u][i]);
-    }
+        if (valid(jt, i)) mx[ct] = fmaxf(mx[ct], s[ct][i]);
   }
-  for (int jt = wid + 4 * kCached; jt < njt; jt += 4) {
-    float4 x[D / 16];
-    tile_load<D>(kp, Nk, 16 * jt, c16, g, x);
-    const f32x4 s = tile_mma<D>(x, qop);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (valid(jt, i)) mx = fmaxf(mx, s[i]);
+  for (int ct = 0; ct < 2; ++ct) {
+    mx[ct] = fmaxf(mx[ct], __shfl_xor(mx[ct], 16));
+    mx[ct] = fmaxf(mx[ct], __shfl_xor(mx[ct], 32));
+    if (g == 0) red[wid][16 * ct + c16] = mx[ct];
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  if (g == 0) red[wid][c16] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0][c16], red[1][c16]), fmaxf(red[2][c16], red[3][c16]));
-  const float thr = mx * proxy_scale - tau;
+  float thr[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int col = 16 * ct + c16;
+    float m = red[0][col];
+#pragma unroll
+    for (int w = 1; w < kPlanWaves; ++w) m = fmaxf(m, red[w][col]);
+    thr[ct] = m * proxy_scale - tau;
+  }
 
   // pass 2: size of the union of the kept sets of blocks c16 and c16 ^ 1
-  unsigned cnt = 0;
-  auto count = [&](const f32x4& s, int jt) {
+  unsigned cnt[2] = {0u, 0u};
+  auto count = [&](const f32x4 (&s)[2], int jt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool keep = q < Nq && jt < njt && valid(jt, i) && s[i] * proxy_scale >= thr;
-      const bool other = __shfl_xor((int)keep, 1) != 0;
-      cnt += (keep || other) ? 1u : 0u;
-    }
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool keep = q0 + 16 * ct + c16 < Nq && jt < njt && valid(jt, i) && s[ct][i] * proxy_scale >= thr[ct];
+        const bool other = dpp<kDppXor1>((int)keep) != 0;  // the pair's other block (lane c16 ^ 1)
+        cnt[ct] += (keep || other) ? 1u : 0u;
+      }
   };
 #pragma unroll
-  for (int c = 0; c < kCached; ++c) count(sc[c], wid + 4 * c);
-  for (int jt = wid + 4 * kCached; jt < njt; jt += 4) {
+  for (int c = 0; c < kCached; ++c) count(sc[c], wid + kPlanWaves * c);
+  for (int jt = wid + kPlanWaves * kCached; jt < njt; jt += kPlanWaves) {
     float4 x[D / 16];
     tile_load<D>(kp, Nk, 16 * jt, c16, g, x);
-    count(tile_mma<D>(x, qop), jt);
+    f32x4 s[2];
+    tile_mma<D>(x, qop, s);
+    count(s, jt);
   }
-  cnt += __shfl_xor(cnt, 16);
-  cnt += __shfl_xor(cnt, 32);
-  if (g == 0) cred[wid][c16] = cnt;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    cnt[ct] += __shfl_xor(cnt[ct], 16);
+    cnt[ct] += __shfl_xor(cnt[ct], 32);
+    if (g == 0) cred[wid][16 * ct + c16] = cnt[ct];
+  }
   __syncthreads();
   const int npairs = (Nq + 1) / 2;
-  if (wid == 0 && g == 0 && (c16 & 1) == 0 && q < Nq)
-    cost[(size_t)bh * npairs + q / 2] = cred[0][c16] + cred[1][c16] + cred[2][c16] + cred[3][c16];
+  if (tid < kPlanQ && (tid & 1) == 0 && q0 + tid < Nq) {
+    unsigned c = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) c += cred[w][tid];
+    cost[(size_t)bh * npairs + (q0 + tid) / 2] = c;
+  }
 }
 
-// One workgroup per queue. Items whose cost exceeds twice the queue's mean
-// go first, by decreasing cost (a counting sort; equal costs in no particular
-// order); all other items follow in their natural, head-major order. Taking
-// only the outliers out of sequence starts them early enough to keep them off
-// the end of the queue, while neighbouring query blocks, whose kept key
-// blocks overlap, still run side by side and share those tiles in L2.
+// One workgroup per queue. The first two thirds of the queue's range keep
+// their natural, head-major order, so the workgroups of an XCD work on
+// neighbouring query blocks, whose kept key blocks overlap, and share those
+// tiles in L2. The last third is sorted by decreasing cost (a counting sort;
+// equal costs in no particular order), so the queue ends on its lightest
+// items and no workgroup starts a heavy one when the others are about to
+// finish.
 __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict__ cost, unsigned* __restrict__ perm,
                                                      int nitems, int Nk) {
-  extern __shared__ unsigned hist[];  // [Nk + 1] counts of the outliers, then running offsets
+  extern __shared__ unsigned hist[];  // [Nk + 1] counts, then running offsets
   __shared__ unsigned part[1024];
-  __shared__ unsigned long long wsum[16];
-  __shared__ unsigned nheavy;
   const int tid = threadIdx.x, nt = blockDim.x;
-  const int lo = queue_begin(blockIdx.x, nitems), hi = queue_begin(blockIdx.x + 1, nitems), n = hi - lo;
-
-  // total cost of the queue
-  unsigned long long sum = 0;
-  for (int i = lo + tid; i < hi; i += nt) sum += cost[i];
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  if ((tid & 63) == 0) wsum[tid >> 6] = sum;
+  const int lo = queue_begin(blockIdx.x, nitems), hi = queue_begin(blockIdx.x + 1, nitems);
+  const int t0 = hi - (hi - lo) / 3;  // first item of the sorted tail
+  for (int i = lo + tid; i < t0; i += nt) perm[i] = (unsigned)i;
   for (int b = tid; b <= Nk; b += nt) hist[b] = 0u;
   __syncthreads();
-  unsigned long long total = 0;
-  for (int w = 0; w < nt / 64; ++w) total += wsum[w];
-  auto heavy = [&](unsigned c) { return (unsigned long long)c * (unsigned long long)n > 2ull * total; };
-
-  for (int i = lo + tid; i < hi; i += nt) {
-    const unsigned c = min(cost[i], (unsigned)Nk);
-    if (heavy(c)) atomicAdd(&hist[c], 1u);
-  }
+  for (int i = t0 + tid; i < hi; i += nt) atomicAdd(&hist[min(cost[i], (unsigned)Nk)], 1u);
   __syncthreads();
   // exclusive offsets with the highest cost first: position p is bucket Nk - p;
   // thread t owns positions [t*C, (t+1)*C)
@@ -195,8 +246,7 @@ __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict_
     part[tid] += v;
     __syncthreads();
   }
-  if (tid == nt - 1) nheavy = part[tid];
-  unsigned run = (unsigned)lo + part[tid] - local;  // exclusive, offset to the queue's range
+  unsigned run = (unsigned)t0 + part[tid] - local;  // exclusive, offset to the tail's first rank
   for (int k = 0; k < C; ++k) {
     const int pos = tid * C + k;
     if (pos <= Nk) {
@@ -206,28 +256,7 @@ __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict_
     }
   }
   __syncthreads();
-  for (int i = lo + tid; i < hi; i += nt) {
-    const unsigned c = min(cost[i], (unsigned)Nk);
-    if (heavy(c)) perm[atomicAdd(&hist[c], 1u)] = (unsigned)i;
-  }
-
-  // the rest in natural order: thread t owns items [lo + t*CI, lo + (t+1)*CI)
-  const int CI = (n + nt - 1) / nt;
-  const int i0 = lo + tid * CI, i1 = min(hi, i0 + CI);
-  unsigned light = 0;
-  for (int i = i0; i < i1; ++i) light += heavy(min(cost[i], (unsigned)Nk)) ? 0u : 1u;
-  __syncthreads();  // every reader of part is done
-  part[tid] = light;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    const unsigned v = tid >= off ? part[tid - off] : 0u;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  unsigned dst = (unsigned)lo + nheavy + part[tid] - light;
-  for (int i = i0; i < i1; ++i)
-    if (!heavy(min(cost[i], (unsigned)Nk))) perm[dst++] = (unsigned)i;
+  for (int i = t0 + tid; i < hi; i += nt) perm[atomicAdd(&hist[min(cost[i], (unsigned)Nk)], 1u)] = (unsigned)i;
 }
 
 __global__ __launch_bounds__(256) void iota_kernel(unsigned* __restrict__ perm, int nitems) {
@@ -242,13 +271,15 @@ hipError_t launch_identity_order(unsigned* perm, int nitems, hipStream_t stream)
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const float* qpool, const float* kpool, unsigned* cost, unsigned* perm, int BH, int Nq, int Nk,
-                       int d, float tau, float proxy_scale, hipStream_t stream) {
-  const dim3 grid((Nq + 15) / 16, BH);
+hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, int BH, int N, int Nq,
+                       int Nk, int d, float tau, float proxy_scale, hipStream_t stream) {
+  const dim3 grid((Nq + kPlanQ - 1) / kPlanQ, BH);
   if (d == 128)
-    hipLaunchKernelGGL(plan_kernel<128>, grid, dim3(256), 0, stream, qpool, kpool, cost, Nq, Nk, tau, proxy_scale);
+    hipLaunchKernelGGL(plan_kernel<128>, grid, dim3(64 * kPlanWaves), 0, stream, q, kpool, cost, N, Nq, Nk, tau,
+                       proxy_scale);
   else
-    hipLaunchKernelGGL(plan_kernel<64>, grid, dim3(256), 0, stream, qpool, kpool, cost, Nq, Nk, tau, proxy_scale);
+    hipLaunchKernelGGL(plan_kernel<64>, grid, dim3(64 * kPlanWaves), 0, stream, q, kpool, cost, N, Nq, Nk, tau,
+                       proxy_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nitems = forward_items(BH, Nq);

@@ -129,10 +129,9 @@ typedef struct sol_attn_stats {
 
 /* Bytes of device workspace sol_attn_forward and sol_attn_plan need: the
  * work-queue and stats words, one cost and one order slot per work item (a
- * pair of query blocks), the fp32 pooled queries [B][H][Nq][d] of the
- * planning stage, bf16 copies of the pooled keys and values [B][H][Nk][d]
- * for SOL_F_ROW_CORRECTION, and the pooled-key statistics [B][H][2][d] of
- * SOL_ROUTE_GAUSS_DIAG. Returns 0 for unsupported sizes. */
+ * pair of query blocks), bf16 copies of the pooled keys and values
+ * [B][H][Nk][d] for SOL_F_ROW_CORRECTION, and the pooled-key statistics
+ * [B][H][2][d] of SOL_ROUTE_GAUSS_DIAG. Returns 0 for unsupported sizes. */
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
 
 /*
@@ -147,15 +146,16 @@ int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean,
                   int B, int H, int N, int d, int Bk, void* stream);
 
 /*
- * Optional planning stage, for forwards called with SOL_F_PLANNED: pools q
- * per block into the workspace (the pooled queries of §2 "Block-Sparse
- * Attention"), and for finite tau estimates every work item's kept budget
- * (bf16 products of the pooled vectors) and moves the items far above their
- * work queue's mean budget to the front of that queue, heaviest first. It is
- * a scheduling aid only: the forward still routes every block itself, in
- * fp32, and nothing routing-related is written to device memory beyond one
- * count per item. For tau = +inf (and very large B*H*N) the order is the
- * identity. Resets the workspace's queue and stats words.
+ * The planning stage of the forward, callable on its own for forwards with
+ * SOL_F_PLANNED (e.g. one plan reused over several diffusion steps of a
+ * layer): for finite tau, estimates every work item's kept budget (bf16
+ * products of query means sampled from every 4th row and the pooled keys)
+ * and orders each work queue: its first two thirds in sequence (neighbouring
+ * query blocks keep overlapping key blocks and share them in L2), its last
+ * third heaviest first. A scheduling aid only: the forward still routes every
+ * block itself, in fp32, and nothing routing-related is written to device
+ * memory beyond one count per item. For tau = +inf (and very large B*H*N)
+ * the order is the identity. Resets the workspace's queue and stats words.
  *   q         bf16 [B][H][N][d]
  *   kpool     fp32 [B][H][Nk][d], sol_attn_pool() of k
  *   workspace as for sol_attn_forward
@@ -177,7 +177,9 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
  *             SOL_F_PLANNED is set. Every forward leaves its queue and stats
  *             words clean.
  * Launches the pooling pass of k and v (unless SOL_F_POOLED, which launches
- * a one-workgroup reset of the workspace words instead) and one fused kernel;
+ * a one-workgroup reset of the workspace words instead), the planning kernels
+ * of sol_attn_plan (row-max rule with 6 <= tau < +inf, where the per-block
+ * budgets spread widely enough for the order to pay) and one fused kernel;
  * with SOL_F_PLANNED only the fused kernel. The fused kernel's persistent
  * grid takes pairs of query blocks from eight atomic queues (one per XCD,
  * each over a contiguous range of items, stealing from the others once

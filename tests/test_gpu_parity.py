@@ -365,3 +365,21 @@ def test_mask_threshold_rejects_diag():
     rc = sa.lib().sol_attn_mask_threshold(q.data_ptr(), kp.data_ptr(), 1, 1, 1000, 128, 64, 64, ctypes.byref(route),
                                           bm.data_ptr(), None)
     assert rc == sa.SOL_EUNSUPPORTED
+
+
+def test_order_never_changes_the_result():
+    """The forward plans its own order at tau = 8; a planned workspace with the
+    identity order (a plan at tau = +inf) and one planned at tau = 2 give the
+    same bits."""
+    wl = get_workload("image_dit_4k")
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    ref = r(q, k, v, 8.0).clone()
+    st = r.read_stats()
+    for plan_tau in (INF, 2.0, 8.0):
+        r.plan(q, plan_tau)
+        out = r(q, k, v, 8.0, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), plan_tau
+        assert r.read_stats() == st
