@@ -32,19 +32,15 @@ constexpr int kPlanQ = 32;      // query blocks per workgroup: two 16-column til
 constexpr int kSampleStride = 4;  // every 4th row of a query block enters its estimated mean
 
 // Loads of one 16x16 S^T tile of pooled keys: lane (g, c16) fetches pooled
-// key jt0 + c16, columns 32 ds + 8 g .. +7 (zero past Nk).
+// key jt0 + c16, columns 32 ds + 8 g .. +7. Buffer loads: keys past Nk read
+// zero without a branch, so the loads of a batch are all in flight at once.
 template <int D>
-__device__ __forceinline__ void tile_load(const float* kp, int Nk, int jt0, int c16, int g, float4 (&x)[D / 16]) {
-  const int j = jt0 + c16;
+__device__ __forceinline__ void tile_load(rsrc_t rk, int jt0, int c16, int g, float4 (&x)[D / 16]) {
+  const uint32_t off = ((jt0 + c16) * D + 8 * g) * 4;
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) {
-    if (j < Nk) {
-      const float4* row = reinterpret_cast<const float4*>(kp + (size_t)j * D + 32 * ds + 8 * g);
-      x[2 * ds] = row[0];
-      x[2 * ds + 1] = row[1];
-    } else {
-      x[2 * ds] = x[2 * ds + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    x[2 * ds] = ld16f(rk, off + 128 * ds, 0);
+    x[2 * ds + 1] = ld16f(rk, off + 128 * ds + 16, 0);
   }
 }
 
@@ -80,31 +76,49 @@ __global__ __launch_bounds__(64 * kPlanWaves) void plan_kernel(const uint16_t* _
   __shared__ float red[kPlanWaves][kPlanQ];
   __shared__ unsigned cred[kPlanWaves][kPlanQ];
   const int bh = blockIdx.y, q0 = kPlanQ * blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
 
-  // sampled means: thread t covers block t / TPB, columns (t % TPB) * CPT .. +CPT-1
+  // sampled means: thread t covers block t / TPB, columns (t % TPB) * CPT .. +CPT-1;
+  // buffer loads over the block's valid rows read zero past them, so all of
+  // a thread's loads are issued before the first sum
   {
     const int b = tid / TPB, c0 = (tid % TPB) * CPT, qb = q0 + b;
     const int nb = qb < Nq ? min(kBlk, N - qb * kBlk) : 0;
     float acc[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
-    const uint16_t* rows = q + ((size_t)bh * N + (size_t)qb * kBlk) * D + c0;
+    // one resource per wave (wave-uniform, so no per-lane resource loop) over
+    // the rows of its consecutive query blocks, clamped to the sequence
+    constexpr int BPW = 64 / TPB;  // query blocks per wave
+    const int qw = q0 + wid * BPW;
+    const int rows_w = __builtin_amdgcn_readfirstlane(max(0, min(BPW * kBlk, N - qw * kBlk)));
+    const rsrc_t rq = make_rsrc(q + ((size_t)bh * N + (size_t)(rows_w > 0 ? qw : 0) * kBlk) * D, (uint32_t)rows_w * D * 2);
+    const uint32_t lane_off = (uint32_t)(((b - wid * BPW) * kBlk * D + c0) * 2);
+    constexpr int NS = kBlk / kSampleStride;
+    if constexpr (CPT == 8) {
+      uint4 u[NS];
 #pragma unroll
-    for (int r = 0; r < kBlk; r += kSampleStride) {
-      if (r < nb) {
-        if constexpr (CPT == 8) {
-          const uint4 u = *reinterpret_cast<const uint4*>(rows + (size_t)r * D);
-          acc[0] += bf16lo(u.x); acc[1] += bf16hi(u.x);
-          acc[2] += bf16lo(u.y); acc[3] += bf16hi(u.y);
-          acc[4] += bf16lo(u.z); acc[5] += bf16hi(u.z);
-          acc[6] += bf16lo(u.w); acc[7] += bf16hi(u.w);
-        } else {
-          static_assert(CPT == 4, "8 or 4 columns per thread");
-          const uint2 u = *reinterpret_cast<const uint2*>(rows + (size_t)r * D);
-          acc[0] += bf16lo(u.x); acc[1] += bf16hi(u.x);
-          acc[2] += bf16lo(u.y); acc[3] += bf16hi(u.y);
-        }
+      for (int r = 0; r < NS; ++r) u[r] = ld16(rq, lane_off + (uint32_t)(r * kSampleStride * D * 2), 0);
+#pragma unroll
+      for (int r = 0; r < NS; ++r) {
+        acc[0] += bf16lo(u[r].x); acc[1] += bf16hi(u[r].x);
+        acc[2] += bf16lo(u[r].y); acc[3] += bf16hi(u[r].y);
+        acc[4] += bf16lo(u[r].z); acc[5] += bf16hi(u[r].z);
+        acc[6] += bf16lo(u[r].w); acc[7] += bf16hi(u[r].w);
+      }
+    } else {
+      static_assert(CPT == 4, "8 or 4 columns per thread");
+      uint2 u[NS];
+#pragma unroll
+      for (int r = 0; r < NS; ++r) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(rq, (int)(lane_off + r * kSampleStride * D * 2), 0, 0);
+        u[r] = make_uint2(w[0], w[1]);
+      }
+#pragma unroll
+      for (int r = 0; r < NS; ++r) {
+        acc[0] += bf16lo(u[r].x); acc[1] += bf16hi(u[r].x);
+        acc[2] += bf16lo(u[r].y); acc[3] += bf16hi(u[r].y);
       }
     }
     const float inv = nb > 0 ? 1.f / (float)((nb + kSampleStride - 1) / kSampleStride) : 0.f;
@@ -114,7 +128,7 @@ __global__ __launch_bounds__(64 * kPlanWaves) void plan_kernel(const uint16_t* _
   __syncthreads();
 
   const int g = lane >> 4, c16 = lane & 15;
-  const float* kp = kpool + (size_t)bh * Nk * D;
+  const rsrc_t rk = make_rsrc(kpool + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
   bf16x8 qop[2][D / 32];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(64 * kPlanWaves) void plan_kernel(const uint16_t* _
   for (int c0 = 0; c0 < kCached; c0 += kBatch) {
     float4 x[kBatch][D / 16];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) tile_load<D>(kp, Nk, 16 * (wid + kPlanWaves * (c0 + u)), c16, g, x[u]);
+    for (int u = 0; u < kBatch; ++u) tile_load<D>(rk, 16 * (wid + kPlanWaves * (c0 + u)), c16, g, x[u]);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int jt = wid + kPlanWaves * (c0 + u);
@@ -148,7 +162,7 @@ __global__ __launch_bounds__(64 * kPlanWaves) void plan_kernel(const uint16_t* _
   }
   for (int jt = wid + kPlanWaves * kCached; jt < njt; jt += kPlanWaves) {
     float4 x[D / 16];
-    tile_load<D>(kp, Nk, 16 * jt, c16, g, x);
+    tile_load<D>(rk, 16 * jt, c16, g, x);
     f32x4 s[2];
     tile_mma<D>(x, qop, s);
 #pragma unroll
@@ -190,7 +204,7 @@ __global__ __launch_bounds__(64 * kPlanWaves) void plan_kernel(const uint16_t* _
   for (int c = 0; c < kCached; ++c) count(sc[c], wid + kPlanWaves * c);
   for (int jt = wid + kPlanWaves * kCached; jt < njt; jt += kPlanWaves) {
     float4 x[D / 16];
-    tile_load<D>(kp, Nk, 16 * jt, c16, g, x);
+    tile_load<D>(rk, 16 * jt, c16, g, x);
     f32x4 s[2];
     tile_mma<D>(x, qop, s);
     count(s, jt);
