@@ -38,14 +38,27 @@ constexpr int kMaxOrderedItems = 1 << 20;
 
 bool use_order(float tau, int nitems) { return !isinf(tau) && nitems > 1 && nitems <= kMaxOrderedItems; }
 
-// The forward plans its work order by itself from this tau on (row-max rule):
-// below it the budgets of the query blocks are close enough that items in
-// sequence finish together (measured on video-DiT layers: planning costs
-// about 20 us a call and pays back only from tau ~ 6 up).
-constexpr float kPlanMinTau = 6.f;
+// The forward plans its work order by itself only where the order was
+// measured to repay the planning kernels (about 25 us on the 32K-token video
+// layer, growing with B*H*Nq*Nk): row-max routing with tau >= 8, where the
+// budgets of the query blocks spread widest; at most about eight items per
+// workgroup of the persistent grid, where one heavy item started late sets
+// the finish (with more, the dynamic queues balance the work by themselves);
+// and at least 2^21 query-block x key-block pairs, so that the extra launches
+// are small against the call. Measured whole calls, planned vs in sequence:
+// 32K layer tau = 8 -4%, tau = 6 +1%; 119K layer tau = 8 +9%; 4K image layer
+// tau = 8 +12%.
+constexpr float kPlanMinTau = 8.f;
+constexpr int kPlanMaxItems = 4096;
+constexpr long long kPlanMinPairs = 1ll << 21;
 
 // Largest B * H of the launches whose grid has one row per head (plan, masks).
 constexpr int kMaxGridHeads = 65535;
+
+bool plan_by_default(const sol_attn_route& r, int BH, int Nq, int nitems) {
+  return r.rule == SOL_ROUTE_ROWMAX && r.tau >= kPlanMinTau && use_order(r.tau, nitems) &&
+         nitems <= kPlanMaxItems && (long long)BH * Nq * Nq >= kPlanMinPairs && BH <= kMaxGridHeads;
+}
 
 int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return SOL_EINVAL;
@@ -155,8 +168,7 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
     // row-max routing with a large finite tau, where per-block budgets spread
     // widely: plan the order of the work (elsewhere the items go in sequence;
     // the order never changes the result)
-    if (e == hipSuccess && route.rule == SOL_ROUTE_ROWMAX && route.tau >= kPlanMinTau &&
-        use_order(route.tau, nitems) && BH <= kMaxGridHeads) {
+    if (e == hipSuccess && plan_by_default(route, BH, Nq, nitems)) {
       bool ordered = false;
       e = plan_impl(q16, kpool, BH, N, d, route.tau, ws, s, &ordered);
       perm = reinterpret_cast<const unsigned*>(wsb + w.perm);

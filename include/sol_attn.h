@@ -178,8 +178,10 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
  *             words clean.
  * Launches the pooling pass of k and v (unless SOL_F_POOLED, which launches
  * a one-workgroup reset of the workspace words instead), the planning kernels
- * of sol_attn_plan (row-max rule with 6 <= tau < +inf, where the per-block
- * budgets spread widely enough for the order to pay) and one fused kernel;
+ * of sol_attn_plan where the order repays them (row-max rule with
+ * 8 <= tau < +inf, where the per-block budgets spread widest, at most 4096
+ * items and at least 2^21 query-block x key-block pairs in the call) and one
+ * fused kernel;
  * with SOL_F_PLANNED only the fused kernel. The fused kernel's persistent
  * grid takes pairs of query blocks from eight atomic queues (one per XCD,
  * each over a contiguous range of items, stealing from the others once

@@ -368,9 +368,8 @@ def test_mask_threshold_rejects_diag():
 
 
 def test_order_never_changes_the_result():
-    """The forward plans its own order at tau = 8; a planned workspace with the
-    identity order (a plan at tau = +inf) and one planned at tau = 2 give the
-    same bits."""
+    """The default call, a planned workspace with the identity order (a plan
+    at tau = +inf) and ones planned at tau = 2 and 8 give the same bits."""
     wl = get_workload("image_dit_4k")
     x = make_inputs(wl)
     q, k, v = (to_device_bf16(x[n]) for n in "qkv")
