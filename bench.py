@@ -171,6 +171,15 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         r["call_row_correction"] = elapsed(ev)
+        # the whole call with the output stored as bf16 (SOL_F_OUT_BF16)
+        out16 = torch.empty(out.shape, dtype=torch.bfloat16, device=out.device)
+        ev = events(n)
+        for a, b in ev:
+            a.record(stream)
+            runner(q, k, v, tau, out=out16)
+            b.record(stream)
+        torch.cuda.synchronize()
+        r["call_bf16_out"] = elapsed(ev)
         return r, wall, stats
 
     def pct(xs):
@@ -219,6 +228,7 @@ def main():
             "ms_plan": round(ms_plan, 4),
             "fwd_ms_items_in_sequence": round(float(np.median(r["fwd_sequence_order"])), 4),
             "row_correction_ms_per_call": round(float(np.median(r["call_row_correction"])), 4),
+            "bf16_out_ms_per_call": round(float(np.median(r["call_bf16_out"])), 4),
             "dense_equiv_tflops": round(dense / (ms_call * 1e-3) / 1e12, 1),
             "kept_block_pct": round(kept_pct, 3),
             "kept_token_pct": round(100.0 * stats["kept_pairs"] / (B * H * N * N), 3),

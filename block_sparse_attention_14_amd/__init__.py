@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     SOL_EUNSUPPORTED,
     SOL_EWORKSPACE,
     SOL_F_EXACT_ONLY,
+    SOL_F_OUT_BF16,
     SOL_F_PLANNED,
     SOL_F_POOLED,
     SOL_F_ROW_CORRECTION,

@@ -17,6 +17,7 @@ SOL_F_POOLED = 1 << 0
 SOL_F_EXACT_ONLY = 1 << 1
 SOL_F_PLANNED = 1 << 2
 SOL_F_ROW_CORRECTION = 1 << 3
+SOL_F_OUT_BF16 = 1 << 4
 
 SOL_ROUTE_ROWMAX = 0
 SOL_ROUTE_GAUSS = 1

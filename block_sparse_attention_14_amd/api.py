@@ -14,7 +14,7 @@ from typing import Dict, Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import SOL_F_EXACT_ONLY, SOL_F_PLANNED, SOL_F_POOLED, SOL_F_ROW_CORRECTION, check, lib  # noqa: F401
+from ._lib import SOL_F_EXACT_ONLY, SOL_F_OUT_BF16, SOL_F_PLANNED, SOL_F_POOLED, SOL_F_ROW_CORRECTION, check, lib  # noqa: F401
 
 STATS_WORDS = 4  # sol_attn_stats is 32 bytes
 
@@ -112,12 +112,14 @@ class SolAttention:
 
     def __call__(self, q, k, v, tau: float, flags: int = 0, out: Optional[torch.Tensor] = None,
                  stats: bool = True, bitmap: Optional[torch.Tensor] = None, beta: Optional[float] = None,
-                 sinks: Optional[Tuple[int, int]] = None, diag: bool = False) -> torch.Tensor:
+                 sinks: Optional[Tuple[int, int]] = None, diag: bool = False,
+                 out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
         """Forward on the current stream. ``tau`` is the row-max offset; with
         ``beta`` set, the Gaussian-calibrated rule (mean + beta * std of each
         proxy row) routes instead and ``tau`` is ignored; ``diag`` selects its
         diagonal estimator from the pooled-key statistics. ``sinks`` =
-        (first, count) key blocks that are always kept."""
+        (first, count) key blocks that are always kept. The output is fp32,
+        or bf16 (SOL_F_OUT_BF16) when ``out`` or ``out_dtype`` is bfloat16."""
         shape = (self.B, self.H, self.N, self.d)
         _check_qkv("q", q, shape)
         _check_qkv("k", k, shape)
@@ -125,8 +127,17 @@ class SolAttention:
         if q.device != self.device or k.device != self.device or v.device != self.device:
             raise ValueError(f"q, k, v must be on {self.device}")
         if out is None:
-            out = torch.empty(shape, dtype=torch.float32, device=self.device)
-        _check_f32("out", out, shape, self.device)
+            if out_dtype not in (torch.float32, torch.bfloat16):
+                raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+            out = torch.empty(shape, dtype=out_dtype, device=self.device)
+        if out.dtype == torch.bfloat16:
+            flags |= SOL_F_OUT_BF16
+            if not out.is_contiguous() or tuple(out.shape) != shape or out.device != self.device:
+                raise ValueError(f"out must be a contiguous tensor of shape {shape} on {self.device}")
+        else:
+            if flags & SOL_F_OUT_BF16:
+                raise ValueError("SOL_F_OUT_BF16 needs a bfloat16 out tensor")
+            _check_f32("out", out, shape, self.device)
         bm_ptr = None
         if bitmap is not None:
             bs = bitmap_shape(self.B, self.H, self.N, self.Bq, self.Bk)
@@ -177,10 +188,11 @@ class SolAttention:
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, Bq: int = 64, Bk: int = 64,
             flags: int = 0, return_bitmap: bool = False, return_stats: bool = False,
-            beta: Optional[float] = None, sinks: Optional[Tuple[int, int]] = None):
+            beta: Optional[float] = None, sinks: Optional[Tuple[int, int]] = None,
+            out_dtype: torch.dtype = torch.float32):
     """One-shot sparse attention forward (allocates its buffers).
 
-    Returns out (fp32), plus the kept-block bitmap [B, H, Nq, ceil(Nk/32)]
+    Returns out (fp32, or bf16 with ``out_dtype``), plus the kept-block bitmap [B, H, Nq, ceil(Nk/32)]
     (int32 words) and/or the stats dict when asked.
     """
     _check_qkv("q", q)
@@ -191,7 +203,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, Bq: i
     bm = None
     if return_bitmap:
         bm = torch.zeros(bitmap_shape(B, H, N, Bq, Bk), dtype=torch.int32, device=q.device)
-    out = runner(q, k, v, tau, flags=flags, bitmap=bm, beta=beta, sinks=sinks)
+    out = runner(q, k, v, tau, flags=flags, bitmap=bm, beta=beta, sinks=sinks, out_dtype=out_dtype)
     res = [out]
     if return_bitmap:
         res.append(bm)

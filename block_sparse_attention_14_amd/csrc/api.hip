@@ -116,7 +116,7 @@ int check_route(const sol_attn_route& r, int N, int Bk) {
   return SOL_OK;
 }
 
-int check_forward(const void* q, const void* k, const void* v, const float* out, int B, int H, int N,
+int check_forward(const void* q, const void* k, const void* v, const void* out, int B, int H, int N,
                   int d, int Bq, int Bk, const sol_attn_route& route, unsigned flags, const sol_attn_stats* stats,
                   const float* kpool, const float* vmean, const void* ws, size_t ws_bytes) {
   if (!q || !k || !v || !out || !kpool || !vmean || !ws) return SOL_EINVAL;
@@ -124,7 +124,8 @@ int check_forward(const void* q, const void* k, const void* v, const float* out,
       !aligned(kpool, 16) || !aligned(vmean, 16) || !aligned(ws, 256) || !aligned(stats, 8))
     return SOL_EINVAL;
   if (check_route(route, N, Bk) != SOL_OK) return SOL_EINVAL;
-  if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION)) return SOL_EINVAL;
+  if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION | SOL_F_OUT_BF16))
+    return SOL_EINVAL;
   if ((flags & SOL_F_EXACT_ONLY) && (flags & SOL_F_ROW_CORRECTION)) return SOL_EINVAL;
   if ((flags & SOL_F_PLANNED) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
   const int rc = check_sizes(B, H, N, d, Bq, Bk);
@@ -133,7 +134,7 @@ int check_forward(const void* q, const void* k, const void* v, const float* out,
   return SOL_OK;
 }
 
-int forward_impl(const void* q, const void* k, const void* v, float* out, int B, int H, int N, int d,
+int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
                  int Bq, int Bk, const sol_attn_route& route, unsigned flags, sol_attn_stats* stats, float* kpool,
                  float* vmean, void* ws, size_t ws_bytes, void* stream, uint32_t* bitmap) {
   const int rc = check_forward(q, k, v, out, B, H, N, d, Bq, Bk, route, flags, stats, kpool, vmean, ws, ws_bytes);
@@ -214,6 +215,7 @@ int forward_impl(const void* q, const void* k, const void* v, float* out, int B,
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
   p.exact_only = (flags & SOL_F_EXACT_ONLY) ? 1 : 0;
   p.row_corr = (flags & SOL_F_ROW_CORRECTION) ? 1 : 0;
+  p.out_bf16 = (flags & SOL_F_OUT_BF16) ? 1 : 0;
   p.khi16 = khi16;
   p.klo16 = klo16;
   p.vbar16 = vbar16;
@@ -346,14 +348,14 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 
-int sol_attn_forward(const void* q, const void* k, const void* v, float* out, int B, int H, int N, int d,
+int sol_attn_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
                      int Bq, int Bk, float tau, unsigned flags, sol_attn_stats* stats, float* kpool,
                      float* vmean, void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(q, k, v, out, B, H, N, d, Bq, Bk, rowmax_route(tau), flags, stats, kpool, vmean, workspace,
                       workspace_bytes, stream, nullptr);
 }
 
-int sol_attn_forward_ex(const void* q, const void* k, const void* v, float* out, int B, int H, int N, int d,
+int sol_attn_forward_ex(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
                         int Bq, int Bk, const sol_attn_route* route, unsigned flags, sol_attn_stats* stats,
                         float* kpool, float* vmean, void* workspace, size_t workspace_bytes, void* stream,
                         uint32_t* kept_bitmap) {
@@ -363,7 +365,7 @@ int sol_attn_forward_ex(const void* q, const void* k, const void* v, float* out,
                       workspace_bytes, stream, kept_bitmap);
 }
 
-int sol_attn_forward_debug(const void* q, const void* k, const void* v, float* out, int B, int H, int N,
+int sol_attn_forward_debug(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
                            int d, int Bq, int Bk, float tau, unsigned flags, sol_attn_stats* stats,
                            float* kpool, float* vmean, void* workspace, size_t workspace_bytes,
                            void* stream, uint32_t* kept_bitmap) {

@@ -779,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         const float inv = 1.f / (lt * fa + cden * fc);
         const int row = qrow0 + 16 * qt + c16;
         if (row < nmine) {
-          float* orow = p.out + hoff + (size_t)(rbase + row) * D;
+          const size_t orow = hoff + (size_t)(rbase + row) * D;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
             const int c = 16 * dt + 4 * g;
@@ -788,7 +788,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
             o.y = (acc[qt][dt][1] * fa + sm.cnum[qb][c + 1] * fc) * inv;
             o.z = (acc[qt][dt][2] * fa + sm.cnum[qb][c + 2] * fc) * inv;
             o.w = (acc[qt][dt][3] * fa + sm.cnum[qb][c + 3] * fc) * inv;
-            *reinterpret_cast<float4*>(orow + c) = o;
+            if (p.out_bf16)
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + c) =
+                  make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+            else
+              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + c) = o;
           }
         }
       }

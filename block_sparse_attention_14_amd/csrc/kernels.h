@@ -34,7 +34,7 @@ struct FwdParams {
   const uint16_t* q;     // bf16 [BH][N][d]
   const uint16_t* k;     // bf16 [BH][N][d]
   const uint16_t* v;     // bf16 [BH][N][d]
-  float* out;            // fp32 [BH][N][d]
+  void* out;             // [BH][N][d]: fp32, or bf16 when out_bf16
   const float* kpool;    // fp32 [BH][Nk][d]
   const float* vmean;    // fp32 [BH][Nk][d]
   const unsigned* perm;  // nullable: rank -> item, within each queue's range
@@ -50,6 +50,7 @@ struct FwdParams {
   float scale_log2;      // log2(e)/sqrt(d)
   int exact_only;        // skipped blocks dropped instead of corrected
   int row_corr;          // per-row (token-to-block) correction over the pooled tiles below
+  int out_bf16;          // store the output rounded to bf16
   const uint16_t* khi16;   // bf16 [BH][Nk][d] pooled keys, high part (row_corr)
   const uint16_t* klo16;   // bf16 [BH][Nk][d] pooled keys, the remainder (row_corr)
   const uint16_t* vbar16;  // bf16 [BH][Nk][d] pooled values (row_corr)

@@ -81,7 +81,10 @@ enum {
    * Routing stays block-level. Computed in bf16 MFMA tiles over the pooled
    * keys and values (bf16-rounded copies made in the workspace), in the same
    * online softmax as the kept blocks. Not with SOL_F_EXACT_ONLY. */
-  SOL_F_ROW_CORRECTION = 1u << 3
+  SOL_F_ROW_CORRECTION = 1u << 3,
+  /* `out` is bf16 [B][H][N][d] instead of fp32: the same fp32 result, rounded
+   * to nearest even as it is stored (half the output bytes). */
+  SOL_F_OUT_BF16 = 1u << 4
 };
 
 /* Routing rules of sol_attn_forward_ex (§3 "Dynamic threshold routing":
@@ -166,7 +169,7 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
 /*
  * Sparse attention forward with proxy correction (all sections cited above).
  *   q, k, v   bf16 [B][H][N][d] (read)
- *   out       fp32 [B][H][N][d] (written)
+ *   out       fp32 [B][H][N][d] (written), or bf16 with SOL_F_OUT_BF16
  *   tau       threshold offset in natural-log units, 0 <= tau <= +inf
  *   flags     SOL_F_* bits
  *   stats     device sol_attn_stats or NULL
@@ -191,7 +194,7 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
  * same accumulator. Two calls that share a workspace must not overlap in
  * time.
  */
-int sol_attn_forward(const void* q, const void* k, const void* v, float* out,
+int sol_attn_forward(const void* q, const void* k, const void* v, void* out,
                      int B, int H, int N, int d, int Bq, int Bk, float tau,
                      unsigned flags, sol_attn_stats* stats,
                      float* kpool, float* vmean,
@@ -207,7 +210,7 @@ int sol_attn_forward(const void* q, const void* k, const void* v, float* out,
  * 0 .. ceil(N/Bk) - 1. sol_attn_forward(..., tau, ...) is this call with
  * {SOL_ROUTE_ROWMAX, tau, 0, 0, 0}.
  */
-int sol_attn_forward_ex(const void* q, const void* k, const void* v, float* out,
+int sol_attn_forward_ex(const void* q, const void* k, const void* v, void* out,
                         int B, int H, int N, int d, int Bq, int Bk,
                         const sol_attn_route* route, unsigned flags, sol_attn_stats* stats,
                         float* kpool, float* vmean,
@@ -253,7 +256,7 @@ int sol_attn_mask_topp(const void* q, const float* kpool, int B, int H, int N, i
  *                j / 32 of row (b, h, i) is 1 iff key block j was kept for
  *                query block i. Must not be NULL.
  */
-int sol_attn_forward_debug(const void* q, const void* k, const void* v, float* out,
+int sol_attn_forward_debug(const void* q, const void* k, const void* v, void* out,
                            int B, int H, int N, int d, int Bq, int Bk, float tau,
                            unsigned flags, sol_attn_stats* stats,
                            float* kpool, float* vmean,

@@ -382,3 +382,31 @@ def test_order_never_changes_the_result():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), plan_tau
         assert r.read_stats() == st
+
+
+@pytest.mark.parametrize("case", [
+    ("tiny_fp32", None, 2.0, {}),
+    ("custom", (130, 64), 0.0, {}),
+    ("custom", (1000, 128), 4.0, dict(flags=sa.SOL_F_ROW_CORRECTION)),
+    ("custom", (1000, 128), 0.0, dict(beta=0.5, sinks=(0, 2))),
+    ("image_dit_4k", None, 8.0, {}),
+    ("image_dit_4k", None, INF, {}),
+])
+def test_bf16_output_is_the_fp32_output_rounded(case):
+    """SOL_F_OUT_BF16 stores the same fp32 result rounded to nearest even."""
+    name, arg, tau, kw = case
+    wl = get_workload(name) if arg is None else _custom(*arg)
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    ref = r(q, k, v, tau, **kw).clone()
+    st = r.read_stats()
+    out16 = torch.full(ref.shape, float("nan"), dtype=torch.bfloat16, device=ref.device)
+    got = r(q, k, v, tau, out=out16, **kw)
+    torch.cuda.synchronize()
+    assert got.dtype == torch.bfloat16
+    assert torch.equal(got.view(torch.int16), ref.to(torch.bfloat16).view(torch.int16))
+    assert r.read_stats() == st
+    with pytest.raises(ValueError):
+        r(q, k, v, tau, out=ref, flags=sa.SOL_F_OUT_BF16 | kw.get("flags", 0),
+          **{a: b for a, b in kw.items() if a != "flags"})
