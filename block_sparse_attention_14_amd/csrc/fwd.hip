@@ -496,15 +496,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int u = 0; u < U; ++u) x[u] = ld16f(rv, voff, (uint32_t)(j0 + u * JG) * D * 4);
         };
+        // all weights of a batch are read before any is used, with no branch
+        // in between, so their LDS round trips overlap (blocks past Nk get
+        // weight 0; their pooled values read as zero)
         auto use = [&](const float4 (&x)[U], int j0) {
+          float w0[U], w1[U];
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             const int j = j0 + u * JG + jg;
-            if (j < Nk) {
-              const float w0 = wrow0[j], w1 = wrow1[j];
-              a0.x += w0 * x[u].x; a0.y += w0 * x[u].y; a0.z += w0 * x[u].z; a0.w += w0 * x[u].w;
-              a1.x += w1 * x[u].x; a1.y += w1 * x[u].y; a1.z += w1 * x[u].z; a1.w += w1 * x[u].w;
-            }
+            const int jc = min(j, Nk - 1);
+            w0[u] = j < Nk ? wrow0[jc] : 0.f;
+            w1[u] = j < Nk ? wrow1[jc] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            a0.x += w0[u] * x[u].x; a0.y += w0[u] * x[u].y; a0.z += w0[u] * x[u].z; a0.w += w0[u] * x[u].w;
+            a1.x += w1[u] * x[u].x; a1.y += w1[u] * x[u].y; a1.z += w1[u] * x[u].z; a1.w += w1[u] * x[u].w;
           }
         };
         float4 x0[U], x1[U];
