@@ -114,6 +114,18 @@ def test_video_dit_119k(video119k, tau):
     _full_parity(get_workload("video_dit_119k"), tau, video119k, query_blocks_per_head=2, seed=int(tau))
 
 
+@pytest.mark.parametrize("d,tau", [(128, 2.0), (64, 4.0), (128, INF)])
+def test_maximum_length(d, tau):
+    """The longest supported head: N = SOL_ATTN_MAX_N - 1 = 262143 tokens on a
+    19 x 73 x 189 grid, 4096 key blocks, the last one ragged (63 tokens).
+    Bitmap on every query block, outputs on sampled blocks."""
+    N = sa.SOL_ATTN_MAX_N - 1
+    assert 19 * 73 * 189 == N
+    wl = Workload(name=f"max_N{N}_d{d}", B=1, H=1, grid=(19, 73, 189), d=d, dtype="bf16", taus=(), seed=2024 + d)
+    assert wl.Nk == 4096
+    _full_parity(wl, tau, query_blocks_per_head=3, seed=d)
+
+
 # ---------------------------------------------------------------------------
 # behaviour of the boundary
 # ---------------------------------------------------------------------------
