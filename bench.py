@@ -61,6 +61,7 @@ def parse():
     ap.add_argument("--profile-only", action="store_true", help="headline tau only, for profilers")
     ap.add_argument("--no-ablation", action="store_true", help="skip the correction ablation report")
     ap.add_argument("--no-routing-cost", action="store_true", help="skip the router comparison")
+    ap.add_argument("--no-rules", action="store_true", help="skip the Gaussian-rule and sink timings")
     ap.add_argument("--copy-ref-mib", type=int, default=512,
                     help="size of the plain device copy (reference rate, counter calibration, flush buffer)")
     return ap.parse_args()
@@ -322,6 +323,41 @@ def main():
         torch.cuda.empty_cache()
         return res
 
+    def rules_report(tau):
+        """Whole calls with the Gaussian-calibrated thresholds (moments of the
+        on-chip proxy row, and the diagonal estimator from pooled-key
+        statistics) at three cutoffs, and with the row-max rule plus four
+        forced sink blocks, on the same layer."""
+        def timed(fn, n=10):
+            fn()
+            torch.cuda.synchronize()
+            ev = events(n)
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median(elapsed(ev)))
+
+        res = {}
+        for diag in (False, True):
+            for beta in (1.0, 2.0, 3.0):
+                ms = timed(lambda: runner(q, k, v, 0.0, out=out, beta=beta, diag=diag))
+                st = runner.read_stats()
+                res[f"{'gauss_diag' if diag else 'gauss'}_beta{beta:g}"] = {
+                    "ms_per_call": round(ms, 4),
+                    "kept_block_pct": round(100.0 * st["kept_blocks"] / st["total_blocks"], 3)}
+        ms = timed(lambda: runner(q, k, v, tau, out=out, sinks=(0, 4)))
+        st = runner.read_stats()
+        res[f"rowmax_tau{tau:g}_sinks_0_4"] = {"ms_per_call": round(ms, 4),
+                                              "kept_block_pct": round(100.0 * st["kept_blocks"] / st["total_blocks"], 3)}
+        return res
+
+    rules = None
+    if not args.no_rules and not args.profile_only:
+        rules = rules_report(args.tau)
+        print(f"[bench] rules {json.dumps(rules)}", file=sys.stderr, flush=True)
+
     rcost = None
     if not args.no_routing_cost and not args.profile_only:
         rcost = routing_cost(args.tau, stats["kept_blocks"])
@@ -375,6 +411,7 @@ def main():
         "cpu_baseline": cpu,
         "correction_ablation": abl,
         "routing_cost": rcost,
+        "routing_rules": rules,
         "per_tau": per_tau,
         "context": {
             "pages_end_to_end_speedup_video_generation": "2.1x vs dense attention (hardware not stated)",
