@@ -174,8 +174,10 @@ class SolAttention:
         return out
 
     def plan(self, q: torch.Tensor, tau: float) -> None:
-        """Pooled queries and the longest-first item order into the workspace
-        (needs self.kpool to hold the pooled keys, e.g. from pool())."""
+        """Item costs and the planned order (per queue: first two thirds in
+        sequence, last third heaviest first) into the workspace, for forwards
+        with SOL_F_PLANNED (needs self.kpool to hold the pooled keys, e.g. from
+        pool())."""
         _check_qkv("q", q, (self.B, self.H, self.N, self.d))
         rc = lib().sol_attn_plan(_ptr(q), _ptr(self.kpool), self.B, self.H, self.N, self.d, self.Bq, self.Bk,
                                  ctypes.c_float(float(tau)), _ptr(self.workspace), self.workspace.numel() * 8,

@@ -166,9 +166,8 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
       set.n = 2;
       e = sol::launch_pool(set, BH, N, Nk, d, static_cast<unsigned*>(ws), s);
     }
-    // row-max routing with a large finite tau, where per-block budgets spread
-    // widely: plan the order of the work (elsewhere the items go in sequence;
-    // the order never changes the result)
+    // plan the order of the work where that was measured to pay (elsewhere
+    // the items go in sequence; the order never changes the result)
     if (e == hipSuccess && plan_by_default(route, BH, Nq, nitems)) {
       bool ordered = false;
       e = plan_impl(q16, kpool, BH, N, d, route.tau, ws, s, &ordered);

@@ -19,11 +19,12 @@
 // budgets differ by two orders of magnitude, so a static split would idle CUs.
 // There is one queue per XCD, each over a contiguous head-major range of items
 // (so an XCD's L2 holds the pooled keys and values of few heads at a time);
-// a workgroup whose queue is drained takes from the others. For finite tau
-// the tickets of a queue map to its items through an order computed by the
-// planning kernels: the few items far above the queue's mean cost first, the
-// rest in sequence, so no workgroup starts a heavy item late and neighbouring
-// blocks (which keep overlapping key blocks) still share K/V tiles in L2.
+// a workgroup whose queue is drained takes from the others. With a plan
+// (sol_attn_plan, or the forward's own where it pays) the tickets of a queue
+// map to its items through the planned order: the first two thirds in
+// sequence, so neighbouring blocks (which keep overlapping key blocks) share
+// K/V tiles in L2, the last third heaviest first, so no workgroup starts a
+// heavy item late.
 // Pairing halves the pooled-key / pooled-value traffic of routing and
 // correction (one read serves both rows) and lets one K/V tile in LDS serve
 // both blocks whenever both keep it, which neighbours usually do.
@@ -43,7 +44,7 @@
 //      lists (ascending, 2-bit owner mask) to LDS;
 //   4. the correction numerators sum_j w_j mean(v_j) of both rows, one pass
 //      over the pooled values, the next batch of loads in flight while one
-//      is used;
+//      is used and a batch's weights read from LDS together;
 //   5. for every union entry, the K and V tiles stream from HBM straight into
 //      LDS (buffer loads with an LDS destination, no registers involved),
 //      double-buffered in two stages, one barrier per tile, the next tile in
@@ -56,7 +57,7 @@
 //      ones operand, and O^T += V^T P^T with V^T operands read from the
 //      row-major V tile by transposing LDS reads (ds_read_b64_tr_b16);
 //   6. exact state and correction merge under a common maximum; rows are
-//      normalised and stored in fp32.
+//      normalised and stored in fp32 (or rounded to bf16 on request).
 #include <math.h>
 
 #include <algorithm>
