@@ -1,9 +1,11 @@
-"""Build libsolattn.so in-tree with hipcc for gfx950.
+"""Build libsolattn.so in-tree with hipcc for gfx950, and the plain C example.
 
     python -m block_sparse_attention_14_amd.build [-v]
 
 Every HIP source is compiled with packed-fp32 code generation disabled; the
-library links only the HIP runtime.
+library links only the HIP runtime. csrc/example_c.c, a C99 caller of the
+library's C ABI, is compiled with the host C compiler into sol_attn_example
+beside the library (found through an $ORIGIN run path).
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsolattn.so")
+EXAMPLE = os.path.join(PKG, "sol_attn_example")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 SOURCES = ["pool.hip", "plan.hip", "fwd.hip", "masks.hip", "api.hip"]
 ARCH = "gfx950"
 
@@ -69,7 +73,28 @@ def build(verbose: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stdout)
         os.replace(tmp_lib, LIB)
+    build_example(verbose)
     return LIB
+
+
+def build_example(verbose: bool = False) -> str:
+    """Compile the C example against the built library; return the binary's path."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no host C compiler found to build the C example")
+    tmp_bin = EXAMPLE + ".tmp"
+    cmd = [cc, "-O2", "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(ROCM, "include"),
+           os.path.join(CSRC, "example_c.c"), "-o", tmp_bin,
+           "-L", PKG, "-lsolattn", "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("C example build failed:\n" + r.stdout)
+    os.replace(tmp_bin, EXAMPLE)
+    return EXAMPLE
 
 
 if __name__ == "__main__":

@@ -211,3 +211,32 @@ def test_forward_ex_accepts_diag_rule_arguments():
     assert fwd_ex((2, 0.0, 1.0, 0, 0)) == sa.SOL_EWORKSPACE
     assert fwd_ex((2, 0.0, math.inf, 0, 0)) == sa.SOL_EINVAL
     assert fwd_ex((3, 0.0, 1.0, 0, 0)) == sa.SOL_EINVAL
+
+
+def test_header_is_plain_c():
+    """The header compiles as strict C99 and as C++ (no torch or HIP types needed)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    inc = os.path.dirname(HEADER)
+    for lang, std in (("c", "-std=c99"), ("c++", "-std=c++17")):
+        r = subprocess.run([gcc, "-x", lang, std, "-pedantic", "-Wall", "-Werror", "-fsyntax-only", "-I", inc, "-"],
+                           input='#include "sol_attn.h"\n', text=True, capture_output=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_c_example_links_against_the_library():
+    """The C example built beside the library resolves libsolattn through its run path."""
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(sa.LIB_PATH), "sol_attn_example")
+    if not os.path.exists(exe):
+        pytest.skip("C example not built")
+    r = subprocess.run(["ldd", exe], text=True, capture_output=True)
+    assert r.returncode == 0, r.stderr
+    assert "not found" not in r.stdout, r.stdout
+    line = [ln for ln in r.stdout.splitlines() if "libsolattn.so" in ln]
+    assert line and os.path.realpath(sa.LIB_PATH) in os.path.realpath(line[0].split("=>")[1].split()[0])
