@@ -598,18 +598,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
           st[0][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
           st[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        // K operands one step ahead of the MFMAs that use them
+        // K operands four steps ahead of the MFMAs that use them (one step
+        // ahead leaves each MFMA pair waiting on its LDS read)
         auto kread = [&](int i) {
           return as_bf16x8(*reinterpret_cast<const uint4*>(stage + 16 * (i / NDS) * G::RB + koff[i % NDS]));
         };
-        bf16x8 kcur = kread(0);
+        constexpr int KA = 4;
+        bf16x8 kop[4 * NDS];
+#pragma unroll
+        for (int i = 0; i < KA; ++i) kop[i] = kread(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
           for (int ds = 0; ds < NDS; ++ds) {
             const int i = kt * NDS + ds;
-            const bf16x8 a = kcur;
-            if (i + 1 < 4 * NDS) kcur = kread(i + 1);
+            const bf16x8 a = kop[i];
+            if (i + KA < 4 * NDS) kop[i + KA] = kread(i + KA);
             __builtin_amdgcn_sched_barrier(0);
             st[0][kt] = mfma16x16x32(a, qop[0][ds], st[0][kt]);
             st[1][kt] = mfma16x16x32(a, qop[1][ds], st[1][kt]);
