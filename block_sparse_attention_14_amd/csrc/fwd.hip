@@ -47,8 +47,10 @@
 //      is used and a batch's weights read from LDS together;
 //   5. for every union entry, the K and V tiles stream from HBM straight into
 //      LDS (buffer loads with an LDS destination, no registers involved),
-//      double-buffered in two stages, one barrier per tile, the next tile in
-//      flight while the current one is consumed. 16-byte chunks are
+//      double-buffered in two stages, one barrier per tile, the copy into
+//      one stage issued before the other stage is consumed (the compiler
+//      still makes the reads of stage A wait for a copy into stage B; the
+//      other workgroup on the CU covers that wait). 16-byte chunks are
 //      XOR-swizzled per row through the per-lane source addresses, so both
 //      operand reads below are bank-conflict free. Each wave whose block keeps
 //      the entry computes its 64x32 S^T with 16x16x32 bf16 MFMAs, the online
