@@ -23,6 +23,7 @@ import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -41,10 +42,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_traffic_video_dit_32k_tau8.js
 
 
 def kernel_hash() -> str:
+    """Hash of the fused kernel's code with comments and whitespace removed, so
+    that measured counters stay attached to it through comment-only edits."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
