@@ -765,6 +765,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         // pooled tiles, one at a time: each fills stage A and half of stage B
         const int npool = (Nk + kBlk - 1) / kBlk;
         for (int c = 0; c < npool; ++c) {
+          // a tile whose key blocks both rows keep holds only masked pooled
+          // keys (all of them, at tau = +inf): skipped, the same decision in
+          // every thread (kept bits in LDS), so the barriers stay matched
+          const int nv = min(kBlk, Nk - c * kBlk);
+          const uint64_t valid = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+          const uint64_t ka = (uint64_t)sm.kbits[0][2 * c] | ((uint64_t)sm.kbits[0][2 * c + 1] << 32);
+          const uint64_t kb = (uint64_t)sm.kbits[1][2 * c] | ((uint64_t)sm.kbits[1][2 * c + 1] << 32);
+          if ((valid & ~ka) == 0 && (!hasB || (valid & ~kb) == 0)) continue;
           dma_pooled(c);
           __builtin_amdgcn_s_waitcnt(0);
           __syncthreads();  // pooled tile c is in LDS
