@@ -329,6 +329,15 @@ def test_row_correction_with_gauss_and_sinks():
     _full_parity(_custom(1000, 128, H=2, seed=3), 1.0, sinks=(15, 1), flags=RC)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_row_correction_with_fully_kept_pooled_tiles(d):
+    """Sinks over key blocks 0-63 make the first pooled tile one that every
+    query block keeps whole (skipped by the kernel); the second tile and the
+    ragged one-block third tile still carry corrections."""
+    wl = _custom(8200, d, H=2, seed=21 + d)  # 129 key blocks: pooled tiles of 64, 64 and 1
+    _full_parity(wl, 1.0, sinks=(0, 64), flags=RC, query_blocks_per_head=6, seed=21)
+
+
 def test_row_correction_planned_matches_one_shot():
     wl = get_workload("image_dit_4k")
     x = make_inputs(wl)
