@@ -492,24 +492,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
       if (!RC && !p.exact_only && (nkA < Nk || (hasB && nkB < Nk))) {
         const rsrc_t rv = make_rsrc(p.vmean + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
-        const uint32_t voff = (jg * D + c4 * 4) * 4;
-        // two batches of U pooled values per lane: one in flight while the other is used
-        // (loads past Nk read zero and are never used)
+        const uint32_t voff = (jg * U * D + c4 * 4) * 4;
+        // two batches of U pooled values per lane (lane group jg takes U
+        // consecutive key blocks of each batch): one in flight while the
+        // other is used (loads past Nk read zero and are never used)
         auto load = [&](float4 (&x)[U], int j0) {
 #pragma unroll
-          for (int u = 0; u < U; ++u) x[u] = ld16f(rv, voff, (uint32_t)(j0 + u * JG) * D * 4);
+          for (int u = 0; u < U; ++u) x[u] = ld16f(rv, voff, (uint32_t)(j0 + u) * D * 4);
         };
         // all weights of a batch are read before any is used, with no branch
-        // in between, so their LDS round trips overlap (blocks past Nk get
-        // weight 0; their pooled values read as zero)
+        // in between (four 16-byte LDS reads), so their round trips overlap
+        // (blocks past Nk get weight 0; their pooled values read as zero)
         auto use = [&](const float4 (&x)[U], int j0) {
+          const int jb = j0 + jg * U;  // (reads up to Nk rounded to 64 stay in the stage)
           float w0[U], w1[U];
 #pragma unroll
+          for (int u = 0; u < U; u += 4) {
+            const float4 a = *reinterpret_cast<const float4*>(&wrow0[jb + u]);
+            const float4 b = *reinterpret_cast<const float4*>(&wrow1[jb + u]);
+            w0[u] = a.x; w0[u + 1] = a.y; w0[u + 2] = a.z; w0[u + 3] = a.w;
+            w1[u] = b.x; w1[u + 1] = b.y; w1[u + 2] = b.z; w1[u + 3] = b.w;
+          }
+#pragma unroll
           for (int u = 0; u < U; ++u) {
-            const int j = j0 + u * JG + jg;
-            const int jc = min(j, Nk - 1);
-            w0[u] = j < Nk ? wrow0[jc] : 0.f;
-            w1[u] = j < Nk ? wrow1[jc] : 0.f;
+            w0[u] = jb + u < Nk ? w0[u] : 0.f;
+            w1[u] = jb + u < Nk ? w1[u] : 0.f;
           }
 #pragma unroll
           for (int u = 0; u < U; ++u) {
