@@ -59,7 +59,10 @@
 //      ones operand, and O^T += V^T P^T with V^T operands read from the
 //      row-major V tile by transposing LDS reads (ds_read_b64_tr_b16);
 //   6. exact state and correction merge under a common maximum; rows are
-//      normalised and stored in fp32 (or rounded to bf16 on request).
+//      normalised and stored in fp32 (or rounded to bf16 on request). The
+//      next item's ticket is resolved before the stores and the item
+//      boundary waits for LDS only, so the stores drain while the next item
+//      starts (nothing in the kernel reads the output).
 #include <math.h>
 
 #include <algorithm>
@@ -74,6 +77,16 @@ namespace sol {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Workgroup barrier for LDS reuse only: this wave's LDS operations complete
+// (lgkmcnt 0; vmcnt and expcnt left at their maxima), no wait for its global
+// stores; the memory clobbers keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 constexpr int kThreads = 256;
 // A row's running max is raised only when a tile's max exceeds it by more than
 // this (base-2 units); until then probabilities may reach 2^8, which fp32 and
@@ -789,9 +802,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       }
     }
 
-    // The next ticket is drawn now, so its round trip overlaps the stores
-    // below; drawing it earlier would tie an item to this workgroup while it
-    // may still spend long on this one, which others could have taken.
+    // The next ticket is drawn now, so its round trip overlaps the fold
+    // below (it is resolved before this wave's stores); drawing it earlier
+    // would tie an item to this workgroup while it may still spend long on
+    // this one, which others could have taken.
     unsigned next_ticket = 0;
     if (tid == 0) next_ticket = ticket();
 
@@ -807,22 +821,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         const float fa = __builtin_amdgcn_exp2f(m[qt] - mf);
         const float fc = p.exact_only ? 0.f : __builtin_amdgcn_exp2f(M2 - mf);
         const float inv = 1.f / (lt * fa + cden * fc);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int c = 16 * dt + 4 * g;
+          acc[qt][dt][0] = (acc[qt][dt][0] * fa + sm.cnum[qb][c + 0] * fc) * inv;
+          acc[qt][dt][1] = (acc[qt][dt][1] * fa + sm.cnum[qb][c + 1] * fc) * inv;
+          acc[qt][dt][2] = (acc[qt][dt][2] * fa + sm.cnum[qb][c + 2] * fc) * inv;
+          acc[qt][dt][3] = (acc[qt][dt][3] * fa + sm.cnum[qb][c + 3] * fc) * inv;
+        }
+      }
+      // the next item, resolved before this wave's stores, so that waiting
+      // for the ticket never waits for them
+      if (tid == 0) sm.item = item_of(take(next_ticket));
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
         const int row = qrow0 + 16 * qt + c16;
         if (row < nmine) {
           const size_t orow = hoff + (size_t)(rbase + row) * D;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
             const int c = 16 * dt + 4 * g;
-            float4 o;
-            o.x = (acc[qt][dt][0] * fa + sm.cnum[qb][c + 0] * fc) * inv;
-            o.y = (acc[qt][dt][1] * fa + sm.cnum[qb][c + 1] * fc) * inv;
-            o.z = (acc[qt][dt][2] * fa + sm.cnum[qb][c + 2] * fc) * inv;
-            o.w = (acc[qt][dt][3] * fa + sm.cnum[qb][c + 3] * fc) * inv;
+            const f32x4 o = acc[qt][dt];
             if (p.out_bf16)
               *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + c) =
-                  make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+                  make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             else
-              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + c) = o;
+              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + c) = make_float4(o[0], o[1], o[2], o[3]);
           }
         }
       }
@@ -844,9 +868,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         st_max = max(st_max, (unsigned)nkB);
       }
     }
-    __syncthreads();  // LDS is rewritten by the next item
-    if (tid == 0) sm.item = item_of(take(next_ticket));
-    __syncthreads();
+    lds_barrier();  // the next item is in sm.item; LDS is rewritten by it (output stores may still be in flight)
   }
 
   // Each workgroup adds its stats once; the last one to finish publishes
