@@ -193,6 +193,38 @@ def test_concurrent_calls_on_two_streams():
         assert torch.equal(o2.view(torch.int32), ref2.view(torch.int32))
 
 
+@pytest.mark.parametrize("wlname", ["image_dit_4k", "video_dit_32k"])
+def test_hip_graph_capture_and_replay(wlname, request):
+    """The whole default call (pool pass, planning where it runs, fused
+    kernel: kernels only, no memsets or allocations) captured in a graph and
+    replayed several times, with eager calls on the same workspace in
+    between, gives the eager result bit for bit on every replay."""
+    wl = get_workload(wlname)
+    x = request.getfixturevalue("video32k") if wlname == "video_dit_32k" else make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    tau = 8.0
+    ref = r(q, k, v, tau).clone()  # eager (also sets up the library's per-device state)
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        r(q, k, v, tau, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        r(q, k, v, tau, out=out)
+    for _ in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+        eager = r(q, k, v, tau)
+        torch.cuda.synchronize()
+        assert torch.equal(eager.view(torch.int32), ref.view(torch.int32))
+
+
 def test_exact_only_ablation():
     wl = _custom(1000, 128, H=2, seed=9)
     x = make_inputs(wl)
