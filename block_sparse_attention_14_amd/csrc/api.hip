@@ -46,8 +46,8 @@ bool use_order(float tau, int nitems) { return !isinf(tau) && nitems > 1 && nite
 // the finish (with more, the dynamic queues balance the work by themselves);
 // and at least 2^21 query-block x key-block pairs, so that the extra launches
 // are small against the call. Measured whole calls, planned vs in sequence:
-// 32K layer tau = 8 -4%, tau = 6 +1%; 119K layer tau = 8 +9%; 4K image layer
-// tau = 8 +12%.
+// 32K layer tau = 8 -8%, tau = 16 -5%, tau = 6 +1%; 119K layer tau = 8 +9%;
+// 4K image layer tau = 8 +12%.
 constexpr float kPlanMinTau = 8.f;
 constexpr int kPlanMaxItems = 4096;
 constexpr long long kPlanMinPairs = 1ll << 21;
