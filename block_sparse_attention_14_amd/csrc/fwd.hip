@@ -211,6 +211,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   const int npairs = (p.Nq + 1) >> 1;
   const int nlast = N - (Nk - 1) * kBlk;
   const float csc = p.scale_log2;
+  // per-row correction: log2(n_j) of a full and of the ragged last key block
+  // in raw dot-product units, formed once (per element they would become a
+  // branch around a division)
+  const float pbias = RC ? 6.f / csc : 0.f;
+  const float pbias_last = RC ? __log2f((float)nlast) / csc : 0.f;
 
   // Queues: the workgroup starts on its own XCD's queue (workgroups are
   // dispatched to the XCDs round-robin) and, when that is drained, takes
@@ -660,16 +665,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
           uint64_t off = (uint64_t)kb[2 * e] | ((uint64_t)kb[2 * e + 1] << 32);
           if (valid < kBlk) off |= ~0ull << valid;
           off >>= 4 * g;
-          const float bias = 6.f / csc;
           const int last = Nk - 1 - e * kBlk - 4 * g;  // lane position of the last block, if here
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const bool masked = (off >> (16 * kt + i)) & 1ull;
-              const float b = 16 * kt + i == last ? __log2f((float)nlast) / csc : bias;
-              st[0][kt][i] = masked ? -INFINITY : st[0][kt][i] + b;
-              st[1][kt][i] = masked ? -INFINITY : st[1][kt][i] + b;
+              const float b = masked ? -INFINITY : 16 * kt + i == last ? pbias_last : pbias;
+              st[0][kt][i] += b;
+              st[1][kt][i] += b;
             }
         } else if (nj < kBlk) {
 #pragma unroll
