@@ -114,6 +114,14 @@ def test_video_dit_119k(video119k, tau):
     _full_parity(get_workload("video_dit_119k"), tau, video119k, query_blocks_per_head=2, seed=int(tau))
 
 
+def test_row_correction_video_dit_119k(video119k):
+    """Per-row correction at the 119K layer's size: every row scored against
+    1857 pooled keys in 29 pooled tiles, the last key block ragged (16
+    tokens); outputs on sampled query blocks."""
+    _full_parity(get_workload("video_dit_119k"), 2.0, video119k, query_blocks_per_head=2, seed=12,
+                 flags=sa.SOL_F_ROW_CORRECTION)
+
+
 @pytest.mark.parametrize("d,tau", [(128, 2.0), (64, 4.0), (128, INF)])
 def test_maximum_length(d, tau):
     """The longest supported head: N = SOL_ATTN_MAX_N - 1 = 262143 tokens on a
@@ -124,6 +132,14 @@ def test_maximum_length(d, tau):
     wl = Workload(name=f"max_N{N}_d{d}", B=1, H=1, grid=(19, 73, 189), d=d, dtype="bf16", taus=(), seed=2024 + d)
     assert wl.Nk == 4096
     _full_parity(wl, tau, query_blocks_per_head=3, seed=d)
+
+
+def test_maximum_length_row_correction():
+    """The longest head with the per-row correction: 64 pooled tiles per item,
+    the last one holding the ragged 63-token block."""
+    N = sa.SOL_ATTN_MAX_N - 1
+    wl = Workload(name=f"max_N{N}_d128", B=1, H=1, grid=(19, 73, 189), d=128, dtype="bf16", taus=(), seed=2152)
+    _full_parity(wl, 2.0, query_blocks_per_head=3, seed=5, flags=sa.SOL_F_ROW_CORRECTION)
 
 
 # ---------------------------------------------------------------------------
