@@ -127,6 +127,9 @@ int check_forward(const void* q, const void* k, const void* v, const void* out, 
   if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION | SOL_F_OUT_BF16))
     return SOL_EINVAL;
   if ((flags & SOL_F_EXACT_ONLY) && (flags & SOL_F_ROW_CORRECTION)) return SOL_EINVAL;
+  // exact-only under a Gaussian threshold: a query block whose threshold lies
+  // above its best block would keep nothing, and its rows would have no terms
+  if ((flags & SOL_F_EXACT_ONLY) && route.rule != SOL_ROUTE_ROWMAX && route.sink_count == 0) return SOL_EINVAL;
   if ((flags & SOL_F_PLANNED) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
   const int rc = check_sizes(B, H, N, d, Bq, Bk);
   if (rc != SOL_OK) return rc;
@@ -378,7 +381,8 @@ const char* sol_attn_strerror(int code) {
     case SOL_OK: return "success";
     case SOL_EINVAL:
       return "invalid argument (null/misaligned pointer, size <= 0, tau NaN or negative, beta not finite, "
-             "unknown rule, sink range out of bounds, unknown or inconsistent flags)";
+             "unknown rule, sink range out of bounds, unknown or inconsistent flags, exact-only under a "
+             "Gaussian rule without sinks)";
     case SOL_EUNSUPPORTED: return "unsupported configuration (d must be 64 or 128, Bq = Bk = 64, N <= SOL_ATTN_MAX_N)";
     case SOL_EWORKSPACE: return "workspace smaller than sol_attn_workspace_bytes()";
     case SOL_EHIP: return "HIP runtime error during launch";

@@ -818,12 +818,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       const float M2 = (qb ? MB : MA) * kLog2e;
       const float cden = sm.cden[qb];
       const int rbase = (qA + qb) * kBlk;
+      // with no correction mass (exact-only, the per-row mode, every block
+      // kept, or every skipped weight zero) the exact state alone is
+      // normalised: a common maximum with M2 could underflow it to zero
+      const bool corr = !p.exact_only && cden > 0.f;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         const float lt = lsum[qt][0];
-        const float mf = p.exact_only ? m[qt] : fmaxf(m[qt], M2);
+        const float mf = corr ? fmaxf(m[qt], M2) : m[qt];
         const float fa = __builtin_amdgcn_exp2f(m[qt] - mf);
-        const float fc = p.exact_only ? 0.f : __builtin_amdgcn_exp2f(M2 - mf);
+        const float fc = corr ? __builtin_amdgcn_exp2f(M2 - mf) : 0.f;
         const float inv = 1.f / (lt * fa + cden * fc);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {

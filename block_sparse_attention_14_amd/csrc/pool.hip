@@ -7,8 +7,9 @@
 // One workgroup per (block j, head) and tensor (grid x = head * Nk + j, grid y
 // = tensor). Each thread streams 16-byte chunks of rows, the partial sums meet
 // in LDS, and thread c writes column c. The pass is a pure HBM stream: every
-// input byte is read once. The forward also pools q here (the pooled queries
-// of the routing step, computed once instead of once per work item).
+// input byte is read once. The forward pools k and v here; its pooled queries
+// are summed inside the fused kernel from the Q tiles it loads anyway. The
+// top-k / top-p mask builders pool q with this kernel.
 #include "common.h"
 #include "kernels.h"
 

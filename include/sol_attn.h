@@ -64,7 +64,10 @@ enum {
 enum {
   /* kpool/vmean already hold sol_attn_pool() of these k and v: skip that pass. */
   SOL_F_POOLED = 1u << 0,
-  /* Ablation: drop skipped blocks instead of correcting them (keep-or-drop). */
+  /* Ablation: drop skipped blocks instead of correcting them (keep-or-drop).
+   * With SOL_ROUTE_GAUSS or SOL_ROUTE_GAUSS_DIAG it needs a sink range
+   * (SOL_EINVAL otherwise): a Gaussian threshold above a query block's best
+   * proxy keeps nothing, which leaves that block's rows without any term. */
   SOL_F_EXACT_ONLY = 1u << 1,
   /* The workspace holds the result of sol_attn_plan() (for these shapes;
    * ideally for these q, kpool and tau), possibly followed by other forwards
@@ -207,7 +210,8 @@ int sol_attn_forward(const void* q, const void* k, const void* v, void* out,
  * All other arguments, the launches and the errors are those of
  * sol_attn_forward; in addition SOL_EINVAL for an unknown rule, a NaN or
  * negative tau (ROWMAX), a non-finite beta (GAUSS), or a sink range outside
- * 0 .. ceil(N/Bk) - 1. sol_attn_forward(..., tau, ...) is this call with
+ * 0 .. ceil(N/Bk) - 1, and for SOL_F_EXACT_ONLY under a Gaussian rule with
+ * sink_count = 0. sol_attn_forward(..., tau, ...) is this call with
  * {SOL_ROUTE_ROWMAX, tau, 0, 0, 0}.
  */
 int sol_attn_forward_ex(const void* q, const void* k, const void* v, void* out,

@@ -105,6 +105,42 @@ def check_stats(stats, keep_all: np.ndarray, N: int):
     assert stats["kept_pairs"] == int(pairs.sum())
 
 
+QUEUES = 8  # the fused kernel's work queues, one per XCD, each over a contiguous range of items
+
+
+def stratified_blocks(B: int, H: int, Nq: int, rng: np.random.Generator, per_queue: int = 3):
+    """Query blocks to check on a layer too large for the oracle to run whole,
+    chosen where scheduling could go wrong: in each of the eight queue ranges
+    of work items (an item is a pair of neighbouring query blocks, numbered
+    head-major), the first two and last two items (where workgroups begin and
+    where stealing from a drained queue starts), the item that opens the last
+    third (where a planned order switches to heaviest first), and `per_queue`
+    random items of that last third and of the first two thirds; plus the
+    first and the ragged last query block of every head.
+    Returns {(b, h): sorted list of query blocks}."""
+    npairs = (Nq + 1) // 2
+    nitems = B * H * npairs
+    items = set()
+    for x in range(QUEUES):
+        lo, hi = x * nitems // QUEUES, (x + 1) * nitems // QUEUES
+        if hi <= lo:
+            continue
+        tail = lo + 2 * (hi - lo) // 3
+        items.update(i for i in (lo, lo + 1, hi - 2, hi - 1, tail) if lo <= i < hi)
+        if hi > tail:
+            items.update(rng.integers(tail, hi, size=per_queue).tolist())
+        if tail > lo:
+            items.update(rng.integers(lo, tail, size=per_queue).tolist())
+    picks = {(b, h): {0, Nq - 1} for b in range(B) for h in range(H)}
+    for it in items:
+        bh, p = divmod(it, npairs)
+        blocks = picks[(bh // H, bh % H)]
+        blocks.add(2 * p)
+        if 2 * p + 1 < Nq:
+            blocks.add(2 * p + 1)
+    return {key: sorted(v) for key, v in picks.items()}
+
+
 def sample_blocks(Nq: int, rng: np.random.Generator, k: int = 6) -> Sequence[int]:
     """First, last (ragged) and a few random query blocks."""
     picks = {0, Nq - 1}

@@ -206,6 +206,21 @@ def test_mask_builders_reject_bad_route_bitmap_workspace():
     assert L.sol_attn_mask_topp(*a, ctypes.c_float(math.nan), P, P, 1 << 40, None) == sa.SOL_EINVAL
 
 
+@pytest.mark.parametrize("rule", [1, 2])
+def test_exact_only_under_a_gaussian_rule_needs_sinks(rule):
+    """A Gaussian threshold above a query block's best proxy keeps nothing;
+    without the correction such a block's rows would have no term at all, so
+    exact-only is refused there unless sink blocks guarantee a kept block."""
+    EO = sa.SOL_F_EXACT_ONLY
+    assert fwd_ex((rule, 0.0, 50.0, 0, 0), flags=EO) == sa.SOL_EINVAL
+    assert fwd_ex((rule, 0.0, 0.0, 0, 0), flags=EO) == sa.SOL_EINVAL
+    # with a sink range (or the correction) the same route passes validation
+    assert fwd_ex((rule, 0.0, 50.0, 3, 1), flags=EO) == sa.SOL_EWORKSPACE
+    assert fwd_ex((rule, 0.0, 50.0, 0, 0)) == sa.SOL_EWORKSPACE
+    # the row-max rule always keeps its best block
+    assert fwd_ex((0, 0.0, 0.0, 0, 0), flags=EO) == sa.SOL_EWORKSPACE
+
+
 def test_forward_ex_accepts_diag_rule_arguments():
     # a valid diagonal-estimator route passes validation (the tiny workspace fails next)
     assert fwd_ex((2, 0.0, 1.0, 0, 0)) == sa.SOL_EWORKSPACE

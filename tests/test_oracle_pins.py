@@ -132,6 +132,34 @@ def test_routing_monotone_in_tau_and_argmax_kept():
     assert (keep.sum(axis=1) == 1).all()
 
 
+@pytest.mark.parametrize("N,d,Bq,Bk", [(37, 3, 8, 5), (40, 4, 16, 8), (23, 2, 4, 23), (61, 5, 7, 12), (64, 3, 64, 16)])
+@pytest.mark.parametrize("tau", [0.0, 0.4, 2.0, math.inf])
+def test_route_head_matches_brute_force_and_attend_head(N, d, Bq, Bk, tau):
+    """route_head (the routing-only entry of the oracle) against the
+    pure-Python brute force (§2 "Block-Sparse Attention": means of the query
+    and key blocks, one score per block pair) and against attend_head's own
+    routing. Unequal block sizes on both sides, with ragged last blocks, make
+    a swapped Bq/Bk fail; non-centred inputs (a common offset) make a sum
+    taken for a mean change every score."""
+    from oracle import route_head
+
+    rng = np.random.default_rng(31 * N + 7 * d + Bq + Bk)
+    q = rand(rng, N, d, scale=1.5) + 0.7
+    k = rand(rng, N, d, scale=1.5) - 0.4
+    v = rand(rng, N, d)
+    s, M, keep = route_head(q, k, Bq, Bk, tau)
+    _, s_b, keep_b = brute_head(q.tolist(), k.tolist(), v.tolist(), Bq, Bk, tau)
+    s_b = np.array(s_b)
+    assert s.shape == (-(-N // Bq), -(-N // Bk))
+    np.testing.assert_allclose(s, s_b, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(M, s_b.max(axis=1), rtol=0, atol=1e-12)
+    assert (keep == np.array(keep_b)).all()
+    r = attend_head(q, k, v, Bq, Bk, tau)
+    np.testing.assert_allclose(s, r["s"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(M, r["M"], rtol=0, atol=1e-12)
+    assert (keep == r["keep"]).all()
+
+
 def test_route_rejects_negative_or_nan_tau():
     s = np.zeros((2, 2))
     for bad in (-1e-9, -1.0, float("nan")):
