@@ -9,8 +9,10 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     SOL_ATTN_MAX_N,
+    SOL_ATTN_SCRATCH_BYTES,
     SOL_EHIP,
     SOL_EINVAL,
+    SOL_ESCRATCH,
     SOL_EUNSUPPORTED,
     SOL_EWORKSPACE,
     SOL_F_EXACT_ONLY,
@@ -31,6 +33,8 @@ from .api import (  # noqa: F401
     SolAttention,
     bitmap_shape,
     forward,
+    forward_noalloc,
+    new_stats,
     pool,
     pooled_shape,
     read_stats,

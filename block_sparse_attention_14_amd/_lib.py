@@ -12,6 +12,7 @@ SOL_EINVAL = -1
 SOL_EUNSUPPORTED = -2
 SOL_EWORKSPACE = -3
 SOL_EHIP = -4
+SOL_ESCRATCH = -5
 
 SOL_F_POOLED = 1 << 0
 SOL_F_EXACT_ONLY = 1 << 1
@@ -24,6 +25,7 @@ SOL_ROUTE_GAUSS = 1
 SOL_ROUTE_GAUSS_DIAG = 2
 
 SOL_ATTN_MAX_N = 4096 * 64
+SOL_ATTN_SCRATCH_BYTES = 96 << 20
 
 EXPORTS = (
     "sol_attn_workspace_bytes",
@@ -36,6 +38,7 @@ EXPORTS = (
     "sol_attn_mask_threshold",
     "sol_attn_mask_topk",
     "sol_attn_mask_topp",
+    "sol_attn_forward_noalloc",
     "sol_attn_strerror",
 )
 
@@ -111,6 +114,9 @@ def lib() -> ctypes.CDLL:
                 L.sol_attn_mask_topp.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp, _vp,
                                                  ctypes.c_size_t, _vp]
                 L.sol_attn_mask_topp.restype = _i
+                L.sol_attn_forward_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                                       ctypes.POINTER(sol_attn_route), ctypes.c_uint, _vp, _vp, _vp]
+                L.sol_attn_forward_noalloc.restype = _i
                 L.sol_attn_strerror.argtypes = [_i]
                 L.sol_attn_strerror.restype = ctypes.c_char_p
                 _lib = L

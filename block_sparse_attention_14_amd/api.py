@@ -214,6 +214,45 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, Bq: i
     return res[0] if len(res) == 1 else tuple(res)
 
 
+def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, tau: float = 0.0,
+                    flags: int = 0, stats: Optional[torch.Tensor] = None, bitmap: Optional[torch.Tensor] = None,
+                    beta: Optional[float] = None, sinks: Optional[Tuple[int, int]] = None,
+                    diag: bool = False) -> torch.Tensor:
+    """sol_attn_forward_noalloc: the forward with its pooled buffers and
+    workspace in the library's static device scratch array, so nothing is
+    allocated, by torch or the library (the caller passes ``out`` and, if
+    wanted, ``stats`` (new_stats()) and ``bitmap``). Routing as for
+    SolAttention.__call__. Calls that overlap on one GPU race."""
+    _check_qkv("q", q)
+    shape = tuple(q.shape)
+    _check_qkv("k", k, shape)
+    _check_qkv("v", v, shape)
+    B, H, N, d = shape
+    if k.device != q.device or v.device != q.device or out.device != q.device:
+        raise ValueError("q, k, v and out must be on one device")
+    if not out.is_contiguous() or tuple(out.shape) != shape:
+        raise ValueError(f"out must be a contiguous tensor of shape {shape}")
+    if out.dtype == torch.bfloat16:
+        flags |= SOL_F_OUT_BF16
+    elif out.dtype != torch.float32:
+        raise ValueError("out must be float32 or bfloat16")
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() != STATS_WORDS or stats.device != q.device):
+        raise ValueError("stats must come from new_stats() on the inputs' device")
+    if bitmap is not None:
+        bs = bitmap_shape(B, H, N)
+        if bitmap.dtype != torch.int32 or tuple(bitmap.shape) != bs or not bitmap.is_contiguous() \
+                or bitmap.device != q.device:
+            raise ValueError(f"bitmap must be a contiguous int32 tensor of shape {bs} on {q.device}")
+    rule = _lib.SOL_ROUTE_ROWMAX if beta is None else (_lib.SOL_ROUTE_GAUSS_DIAG if diag else _lib.SOL_ROUTE_GAUSS)
+    route = _lib.sol_attn_route(rule, float(tau) if beta is None else 0.0, 0.0 if beta is None else float(beta),
+                                0 if sinks is None else int(sinks[0]), 0 if sinks is None else int(sinks[1]))
+    rc = lib().sol_attn_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, 64, 64,
+                                        ctypes.byref(route), ctypes.c_uint(flags), _ptr(stats),
+                                        _stream(q.device), _ptr(bitmap))
+    check(rc, "sol_attn_forward_noalloc")
+    return out
+
+
 def unpack_bitmap(words: torch.Tensor, Nk: int):
     """[..., nwords] int32 words -> [..., Nk] bool numpy array (host)."""
     import numpy as np

@@ -3,10 +3,39 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "sol_attn.h"
 
 namespace {
+
+// Device memory of sol_attn_forward_noalloc: the pooled keys and values and
+// the forward's workspace of one call, for callers that cannot allocate. One
+// copy per GPU, at its own address, held until the process ends. In host
+// code `scratch` names a host-side stand-in: its device address on the
+// current GPU comes from hipGetSymbolAddress (scratch_base below), and only
+// that address is ever handed to a kernel or a runtime call.
+__device__ __align__(256) unsigned char scratch[SOL_ATTN_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {nullptr};
+
+// The device address of `scratch` on the current GPU, looked up once per
+// device with that device current; SOL_EHIP if the runtime refuses.
+int scratch_base(void** base) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SOL_EHIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SOL_EHIP;
+    scratch_dev[dev] = p;
+  }
+  *base = scratch_dev[dev];
+  return SOL_OK;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -116,12 +145,11 @@ int check_route(const sol_attn_route& r, int N, int Bk) {
   return SOL_OK;
 }
 
-int check_forward(const void* q, const void* k, const void* v, const void* out, int B, int H, int N,
-                  int d, int Bq, int Bk, const sol_attn_route& route, unsigned flags, const sol_attn_stats* stats,
-                  const float* kpool, const float* vmean, const void* ws, size_t ws_bytes) {
-  if (!q || !k || !v || !out || !kpool || !vmean || !ws) return SOL_EINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(kpool, 16) || !aligned(vmean, 16) || !aligned(ws, 256) || !aligned(stats, 8))
+// Everything of a forward but the caller's pooled buffers and workspace.
+int check_args(const void* q, const void* k, const void* v, const void* out, int B, int H, int N, int d, int Bq,
+               int Bk, const sol_attn_route& route, unsigned flags, const sol_attn_stats* stats) {
+  if (!q || !k || !v || !out) return SOL_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(stats, 8))
     return SOL_EINVAL;
   if (check_route(route, N, Bk) != SOL_OK) return SOL_EINVAL;
   if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION | SOL_F_OUT_BF16))
@@ -131,7 +159,15 @@ int check_forward(const void* q, const void* k, const void* v, const void* out, 
   // above its best block would keep nothing, and its rows would have no terms
   if ((flags & SOL_F_EXACT_ONLY) && route.rule != SOL_ROUTE_ROWMAX && route.sink_count == 0) return SOL_EINVAL;
   if ((flags & SOL_F_PLANNED) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
-  const int rc = check_sizes(B, H, N, d, Bq, Bk);
+  return check_sizes(B, H, N, d, Bq, Bk);
+}
+
+int check_forward(const void* q, const void* k, const void* v, const void* out, int B, int H, int N,
+                  int d, int Bq, int Bk, const sol_attn_route& route, unsigned flags, const sol_attn_stats* stats,
+                  const float* kpool, const float* vmean, const void* ws, size_t ws_bytes) {
+  if (!kpool || !vmean || !ws) return SOL_EINVAL;
+  if (!aligned(kpool, 16) || !aligned(vmean, 16) || !aligned(ws, 256)) return SOL_EINVAL;
+  const int rc = check_args(q, k, v, out, B, H, N, d, Bq, Bk, route, flags, stats);
   if (rc != SOL_OK) return rc;
   if (ws_bytes < sol_attn_workspace_bytes(B, H, N, d, Bq, Bk)) return SOL_EWORKSPACE;
   return SOL_OK;
@@ -376,6 +412,28 @@ int sol_attn_forward_debug(const void* q, const void* k, const void* v, void* ou
                       workspace_bytes, stream, kept_bitmap);
 }
 
+int sol_attn_forward_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
+                             int Bq, int Bk, const sol_attn_route* route, unsigned flags, sol_attn_stats* stats,
+                             void* stream, uint32_t* kept_bitmap) {
+  if (!route) return SOL_EINVAL;
+  if (kept_bitmap && !aligned(kept_bitmap, 4)) return SOL_EINVAL;
+  // the pooled buffers and the plan live in the shared scratch array, which
+  // the previous call on this GPU may have overwritten: always pool afresh
+  if (flags & (SOL_F_POOLED | SOL_F_PLANNED)) return SOL_EINVAL;
+  const int rc = check_args(q, k, v, out, B, H, N, d, Bq, Bk, *route, flags, stats);
+  if (rc != SOL_OK) return rc;
+  // scratch layout: [workspace | kpool | vmean], each 256-byte aligned
+  const size_t ws = sol_attn_workspace_bytes(B, H, N, d, Bq, Bk);
+  const size_t pooled = round_up((size_t)B * H * (size_t)((N + Bk - 1) / Bk) * (size_t)d * 4, 256);
+  if (ws + 2 * pooled > (size_t)SOL_ATTN_SCRATCH_BYTES) return SOL_ESCRATCH;
+  void* base = nullptr;
+  const int rc3 = scratch_base(&base);
+  if (rc3 != SOL_OK) return rc3;
+  unsigned char* b = static_cast<unsigned char*>(base);
+  return forward_impl(q, k, v, out, B, H, N, d, Bq, Bk, *route, flags, stats, reinterpret_cast<float*>(b + ws),
+                      reinterpret_cast<float*>(b + ws + pooled), b, ws, stream, kept_bitmap);
+}
+
 const char* sol_attn_strerror(int code) {
   switch (code) {
     case SOL_OK: return "success";
@@ -386,6 +444,8 @@ const char* sol_attn_strerror(int code) {
     case SOL_EUNSUPPORTED: return "unsupported configuration (d must be 64 or 128, Bq = Bk = 64, N <= SOL_ATTN_MAX_N)";
     case SOL_EWORKSPACE: return "workspace smaller than sol_attn_workspace_bytes()";
     case SOL_EHIP: return "HIP runtime error during launch";
+    case SOL_ESCRATCH:
+      return "problem too large for sol_attn_forward_noalloc (needs more than SOL_ATTN_SCRATCH_BYTES of scratch)";
     default: return "unknown error code";
   }
 }

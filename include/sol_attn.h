@@ -57,7 +57,8 @@ enum {
   SOL_EINVAL = -1,       /* null or misaligned pointer, size <= 0, tau NaN or < 0, bad flag */
   SOL_EUNSUPPORTED = -2, /* d not in {64, 128}, Bq != 64, Bk != 64, or N too large */
   SOL_EWORKSPACE = -3,   /* workspace smaller than sol_attn_workspace_bytes() */
-  SOL_EHIP = -4          /* the HIP runtime refused a launch or a query */
+  SOL_EHIP = -4,         /* the HIP runtime refused a launch or a query */
+  SOL_ESCRATCH = -5      /* sol_attn_forward_noalloc: the problem needs more than SOL_ATTN_SCRATCH_BYTES */
 };
 
 /* Flags of sol_attn_forward. */
@@ -266,6 +267,38 @@ int sol_attn_forward_debug(const void* q, const void* k, const void* v, void* ou
                            float* kpool, float* vmean,
                            void* workspace, size_t workspace_bytes, void* stream,
                            uint32_t* kept_bitmap);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * sol_attn_forward_ex with the pooled keys and values and the workspace taken
+ * from a static device array of the library instead of the caller. The
+ * caller passes only inputs and outputs; the call makes no allocation, free
+ * or allocating library call.
+ *   arguments    as for sol_attn_forward_ex, without kpool, vmean and the
+ *                workspace
+ *   scratch      SOL_ATTN_SCRATCH_BYTES of device memory per GPU, reserved
+ *                when the library is loaded and held until the process ends,
+ *                laid out as [workspace | kpool | vmean]: a problem needs
+ *                sol_attn_workspace_bytes() + 2 * round_up(B*H*ceil(N/Bk)*d*4,
+ *                256) bytes of it (about 76 MiB for B*H = 24 heads of 118800
+ *                tokens at d = 128)
+ * Errors: those of sol_attn_forward_ex; SOL_EINVAL also for SOL_F_POOLED or
+ * SOL_F_PLANNED (the array holds whatever the previous call on this GPU left,
+ * so every call pools afresh); SOL_ESCRATCH, before any launch, when the
+ * problem needs more than SOL_ATTN_SCRATCH_BYTES; SOL_EHIP if the runtime
+ * cannot resolve the array's address on the current GPU (looked up once per
+ * device, on the first call made with that device current).
+ * Every call on one GPU uses that GPU's one array (one per process): two
+ * calls of one process that overlap in time on the same GPU (different
+ * streams or threads) race and may both return wrong results. Calls on one
+ * stream are ordered and safe.
+ */
+#define SOL_ATTN_SCRATCH_BYTES (96u << 20)
+int sol_attn_forward_noalloc(const void* q, const void* k, const void* v, void* out,
+                             int B, int H, int N, int d, int Bq, int Bk,
+                             const sol_attn_route* route, unsigned flags, sol_attn_stats* stats,
+                             void* stream, uint32_t* kept_bitmap);
 
 /* Static description of a return code. */
 const char* sol_attn_strerror(int code);

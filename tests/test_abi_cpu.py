@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_strerror():
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert sa.strerror(code) and sa.strerror(code) != sa.strerror(-99)
 
 
@@ -219,6 +219,44 @@ def test_exact_only_under_a_gaussian_rule_needs_sinks(rule):
     assert fwd_ex((rule, 0.0, 50.0, 0, 0)) == sa.SOL_EWORKSPACE
     # the row-max rule always keeps its best block
     assert fwd_ex((0, 0.0, 0.0, 0, 0), flags=EO) == sa.SOL_EWORKSPACE
+
+
+def fwd_noalloc(route=(0, 2.0, 0.0, 0, 0), bitmap=None, **over):
+    a = dict(q=P, k=P, v=P, out=P, B=1, H=2, N=1000, d=128, Bq=64, Bk=64, flags=0, stats=None, stream=None)
+    a.update(over)
+    rp = None if route is None else ctypes.byref(_lib.sol_attn_route(*route))
+    return sa.lib().sol_attn_forward_noalloc(a["q"], a["k"], a["v"], a["out"], a["B"], a["H"], a["N"], a["d"],
+                                             a["Bq"], a["Bk"], rp, ctypes.c_uint(a["flags"]), a["stats"],
+                                             a["stream"], bitmap)
+
+
+@pytest.mark.parametrize("route,over,code", [
+    (None, {}, sa.SOL_EINVAL),
+    ((0, -1.0, 0.0, 0, 0), {}, sa.SOL_EINVAL),
+    ((0, 2.0, 0.0, 0, 0), dict(q=None), sa.SOL_EINVAL),
+    ((0, 2.0, 0.0, 0, 0), dict(out=P + 4), sa.SOL_EINVAL),
+    ((0, 2.0, 0.0, 0, 0), dict(flags=sa.SOL_F_POOLED), sa.SOL_EINVAL),
+    ((0, 2.0, 0.0, 0, 0), dict(flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED), sa.SOL_EINVAL),
+    ((1, 0.0, 1.0, 0, 0), dict(flags=sa.SOL_F_EXACT_ONLY), sa.SOL_EINVAL),
+    ((0, 2.0, 0.0, 0, 0), dict(d=96), sa.SOL_EUNSUPPORTED),
+    # 64 heads of 118800 tokens need about 190 MiB of pooled buffers: beyond the array
+    ((0, 2.0, 0.0, 0, 0), dict(H=64, N=118800), sa.SOL_ESCRATCH),
+    ((0, 2.0, 0.0, 0, 0), dict(H=1, N=sa.SOL_ATTN_MAX_N, B=40), sa.SOL_ESCRATCH),
+])
+def test_noalloc_rejects_before_launch(route, over, code):
+    assert fwd_noalloc(route, **over) == code
+
+
+def test_noalloc_scratch_limit():
+    """The array's size is the header's constant; the 119K-token layer (24
+    heads, d = 128) fits in it in every mode."""
+    assert sa.SOL_ATTN_SCRATCH_BYTES == 96 << 20
+    text = open(HEADER).read()
+    assert "#define SOL_ATTN_SCRATCH_BYTES (96u << 20)" in text
+    L = sa.lib()
+    ws = L.sol_attn_workspace_bytes(1, 24, 118800, 128, 64, 64)
+    pooled = -(-(24 * 1857 * 128 * 4) // 256) * 256
+    assert ws + 2 * pooled <= sa.SOL_ATTN_SCRATCH_BYTES
 
 
 def test_forward_ex_accepts_diag_rule_arguments():
