@@ -16,6 +16,9 @@ from ._lib import (  # noqa: F401
     SOL_EUNSUPPORTED,
     SOL_EWORKSPACE,
     SOL_F_EXACT_ONLY,
+    SOL_F_GROUP2,
+    SOL_F_GROUP4,
+    SOL_F_GROUP8,
     SOL_F_OUT_BF16,
     SOL_F_PLANNED,
     SOL_F_POOLED,

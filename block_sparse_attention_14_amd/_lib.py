@@ -19,13 +19,16 @@ SOL_F_EXACT_ONLY = 1 << 1
 SOL_F_PLANNED = 1 << 2
 SOL_F_ROW_CORRECTION = 1 << 3
 SOL_F_OUT_BF16 = 1 << 4
+SOL_F_GROUP2 = 1 << 5
+SOL_F_GROUP4 = 2 << 5
+SOL_F_GROUP8 = 3 << 5
 
 SOL_ROUTE_ROWMAX = 0
 SOL_ROUTE_GAUSS = 1
 SOL_ROUTE_GAUSS_DIAG = 2
 
 SOL_ATTN_MAX_N = 4096 * 64
-SOL_ATTN_SCRATCH_BYTES = 96 << 20
+SOL_ATTN_SCRATCH_BYTES = 128 << 20
 
 EXPORTS = (
     "sol_attn_workspace_bytes",
@@ -107,7 +110,8 @@ def lib() -> ctypes.CDLL:
                 L.sol_attn_mask_workspace_bytes.argtypes = [_i] * 6
                 L.sol_attn_mask_workspace_bytes.restype = ctypes.c_size_t
                 L.sol_attn_mask_threshold.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i,
-                                                      ctypes.POINTER(sol_attn_route), _vp, _vp]
+                                                      ctypes.POINTER(sol_attn_route), _vp, _vp, ctypes.c_size_t,
+                                                      _vp]
                 L.sol_attn_mask_threshold.restype = _i
                 L.sol_attn_mask_topk.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, ctypes.c_size_t, _vp]
                 L.sol_attn_mask_topk.restype = _i

@@ -14,9 +14,18 @@ from typing import Dict, Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import SOL_F_EXACT_ONLY, SOL_F_OUT_BF16, SOL_F_PLANNED, SOL_F_POOLED, SOL_F_ROW_CORRECTION, check, lib  # noqa: F401
+from ._lib import (SOL_F_EXACT_ONLY, SOL_F_GROUP2, SOL_F_GROUP4, SOL_F_GROUP8, SOL_F_OUT_BF16,  # noqa: F401
+                   SOL_F_PLANNED, SOL_F_POOLED, SOL_F_ROW_CORRECTION, check, lib)
 
 STATS_WORDS = 4  # sol_attn_stats is 32 bytes
+
+
+def group_flag(group: int) -> int:
+    """The SOL_F_GROUP* bits for 2, 4 or 8 query blocks per work item (0: automatic)."""
+    try:
+        return {0: 0, 2: SOL_F_GROUP2, 4: SOL_F_GROUP4, 8: SOL_F_GROUP8}[int(group)]
+    except KeyError:
+        raise ValueError("group must be 0, 2, 4 or 8") from None
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -113,13 +122,16 @@ class SolAttention:
     def __call__(self, q, k, v, tau: float, flags: int = 0, out: Optional[torch.Tensor] = None,
                  stats: bool = True, bitmap: Optional[torch.Tensor] = None, beta: Optional[float] = None,
                  sinks: Optional[Tuple[int, int]] = None, diag: bool = False,
-                 out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+                 out_dtype: torch.dtype = torch.float32, group: int = 0) -> torch.Tensor:
         """Forward on the current stream. ``tau`` is the row-max offset; with
         ``beta`` set, the Gaussian-calibrated rule (mean + beta * std of each
         proxy row) routes instead and ``tau`` is ignored; ``diag`` selects its
         diagonal estimator from the pooled-key statistics. ``sinks`` =
         (first, count) key blocks that are always kept. The output is fp32,
-        or bf16 (SOL_F_OUT_BF16) when ``out`` or ``out_dtype`` is bfloat16."""
+        or bf16 (SOL_F_OUT_BF16) when ``out`` or ``out_dtype`` is bfloat16.
+        ``group`` (2, 4 or 8; 0 = the library's choice) sets the query
+        blocks per work item (SOL_F_GROUP*)."""
+        flags |= group_flag(group)
         shape = (self.B, self.H, self.N, self.d)
         _check_qkv("q", q, shape)
         _check_qkv("k", k, shape)
@@ -281,14 +293,12 @@ class MaskBuilder:
         _check_f32("kpool", kpool, pooled_shape(self.B, self.H, self.N, self.d, self.Bk), self.device)
         return (_ptr(q), _ptr(kpool), self.B, self.H, self.N, self.d, self.Bq, self.Bk)
 
-    def threshold(self, q, kpool, tau: float = 0.0, beta: Optional[float] = None,
-                  sinks: Optional[Tuple[int, int]] = None) -> torch.Tensor:
-        route = _lib.sol_attn_route(
-            _lib.SOL_ROUTE_GAUSS if beta is not None else _lib.SOL_ROUTE_ROWMAX,
-            float(tau) if beta is None else 0.0, 0.0 if beta is None else float(beta),
-            0 if sinks is None else int(sinks[0]), 0 if sinks is None else int(sinks[1]))
+    def threshold(self, q, kpool, tau: float = 0.0, sinks: Optional[Tuple[int, int]] = None) -> torch.Tensor:
+        """The forward's own routing (row-max rule, optional sinks), bitmap only."""
+        route = _lib.sol_attn_route(_lib.SOL_ROUTE_ROWMAX, float(tau), 0.0,
+                                    0 if sinks is None else int(sinks[0]), 0 if sinks is None else int(sinks[1]))
         rc = lib().sol_attn_mask_threshold(*self._common(q, kpool), ctypes.byref(route), _ptr(self.bitmap),
-                                           _stream(self.device))
+                                           _ptr(self.workspace), self.workspace.numel() * 8, _stream(self.device))
         check(rc, "sol_attn_mask_threshold")
         return self.bitmap
 

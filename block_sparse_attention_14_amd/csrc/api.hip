@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kernels.h"
@@ -42,23 +43,72 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: [header words | item costs | item order | pooled-key copies and
-// statistics of the optional modes].
+// statistics of the optional modes]. The cost and order slots are sized for
+// items of two query blocks, the most items any group size gives.
 struct WsLayout {
-  size_t cost, perm, khi16, klo16, vbar16, kstats, total;
+  size_t cost, perm, kh, km, kl, vt, vbar16, kstats, kmom, total;
 };
+
+// Key blocks per head in the tiled operand planes: Nk rounded up to 256 (the
+// padding is written as zeros, so no read of a plane needs a bound).
+int padded_blocks(int Nk) { return (Nk + 255) / 256 * 256; }
 
 WsLayout ws_layout(int BH, int N, int d) {
   const size_t Nq = (size_t)(N + 63) / 64;
-  const size_t items = (size_t)sol::forward_items(BH, (int)Nq);
+  const size_t items = (size_t)sol::forward_items(BH, (int)Nq, 2);
+  const size_t plane = round_up((size_t)BH * Nq * (size_t)d * 2, 256);
+  const size_t tplane = round_up((size_t)BH * (size_t)d * (size_t)padded_blocks((int)Nq) * 2, 256);
   WsLayout w;
   w.cost = sol::kHdrWords * 4;
   w.perm = round_up(w.cost + 4 * items, 256);
-  w.khi16 = round_up(w.perm + 4 * items, 256);
-  w.klo16 = round_up(w.khi16 + (size_t)BH * Nq * (size_t)d * 2, 256);
-  w.vbar16 = round_up(w.klo16 + (size_t)BH * Nq * (size_t)d * 2, 256);
-  w.kstats = round_up(w.vbar16 + (size_t)BH * Nq * (size_t)d * 2, 256);
-  w.total = round_up(w.kstats + (size_t)BH * 2 * (size_t)d * 4, 256);
+  w.kh = round_up(w.perm + 4 * items, 256);
+  w.km = w.kh + tplane;
+  w.kl = w.km + tplane;
+  w.vt = w.kl + tplane;
+  w.vbar16 = w.vt + tplane;
+  w.kstats = w.vbar16 + plane;
+  w.kmom = round_up(w.kstats + (size_t)BH * 2 * (size_t)d * 4, 256);
+  w.total = round_up(w.kmom + (size_t)BH * (size_t)(d + 1) * (size_t)d * 4, 256);
   return w;
+}
+
+// Query blocks per work item of the fused kernel. Larger groups read the
+// head's pooled keys and values once for more query blocks (the routing
+// pass's traffic falls as 1/G), smaller ones give the persistent grid more
+// items to balance; a group is taken only while the call keeps at least 16
+// items per CU (about eight per workgroup), and eight blocks only up to 2048
+// key blocks (their kept bits and kept list must fit the workgroup's LDS).
+// A flag may ask for a size; 0 there means this automatic choice.
+std::mutex cu_mu;
+int cu_count[64] = {0};
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(cu_mu);
+  if (cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    cu_count[dev] = n;
+  }
+  return cu_count[dev];
+}
+
+int auto_group(int BH, int Nq) {
+  const long long target = 6ll * device_cus();
+  if (Nq <= sol::kMaxKeyBlocksG8 && (long long)sol::forward_items(BH, Nq, 8) >= target) return 8;
+  if ((long long)sol::forward_items(BH, Nq, 4) >= target) return 4;
+  return 2;
+}
+
+// The group size a flag field asks for (0: automatic), or 0 if unsupported.
+int group_of(unsigned flags, int BH, int Nq) {
+  switch ((flags & SOL_F_GROUP_MASK) >> SOL_F_GROUP_SHIFT) {
+    case 1: return 2;
+    case 2: return 4;
+    case 3: return Nq <= sol::kMaxKeyBlocksG8 ? 8 : 0;
+    default: return auto_group(BH, Nq);
+  }
 }
 
 // Items beyond this are taken in sequence order (the one-workgroup sort
@@ -84,8 +134,8 @@ constexpr long long kPlanMinPairs = 1ll << 21;
 // Largest B * H of the launches whose grid has one row per head (plan, masks).
 constexpr int kMaxGridHeads = 65535;
 
-bool plan_by_default(const sol_attn_route& r, int BH, int Nq, int nitems) {
-  return r.rule == SOL_ROUTE_ROWMAX && r.tau >= kPlanMinTau && use_order(r.tau, nitems) &&
+bool plan_by_default(const sol_attn_route& r, int BH, int Nq, int nitems, int group) {
+  return group == 2 && r.rule == SOL_ROUTE_ROWMAX && r.tau >= kPlanMinTau && use_order(r.tau, nitems) &&
          nitems <= kPlanMaxItems && (long long)BH * Nq * Nq >= kPlanMinPairs && BH <= kMaxGridHeads;
 }
 
@@ -95,7 +145,6 @@ int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
   if (Bq != 64 || Bk != 64) return SOL_EUNSUPPORTED;
   if (N > SOL_ATTN_MAX_N) return SOL_EUNSUPPORTED;
   const long long nq = (N + 63) / 64;
-  if (nq > sol::forward_max_blocks(d)) return SOL_EUNSUPPORTED;
   if ((long long)B * H * nq > (1ll << 30)) return SOL_EUNSUPPORTED;  // ticket space
   return SOL_OK;
 }
@@ -113,16 +162,18 @@ sol_attn_route rowmax_route(float tau) {
 }
 
 // Planning: per-item costs and the order of each queue into the workspace
-// (row-max rule, finite tau, sizes the sort handles), else the identity
-// order, which every later planned forward may still read.
+// (row-max rule, finite tau, items of two query blocks, sizes the sort
+// handles), else the identity order, which every later planned forward may
+// still read. The items are those of the automatic group size.
 hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d, float tau, void* ws, hipStream_t s,
                      bool* ordered) {
   const WsLayout w = ws_layout(BH, N, d);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   const int Nq = (N + 63) / 64, Nk = Nq;
   unsigned* perm = reinterpret_cast<unsigned*>(wsb + w.perm);
-  const int nitems = sol::forward_items(BH, Nq);
-  *ordered = use_order(tau, nitems) && BH <= kMaxGridHeads;
+  const int group = auto_group(BH, Nq);
+  const int nitems = sol::forward_items(BH, Nq, group);
+  *ordered = group == 2 && use_order(tau, nitems) && BH <= kMaxGridHeads;
   if (*ordered)
     return sol::launch_plan(q, kpool, reinterpret_cast<unsigned*>(wsb + w.cost), perm, BH, N, Nq, Nk, d, tau,
                             (float)(1.0 / sqrt((double)d)), s);
@@ -152,14 +203,22 @@ int check_args(const void* q, const void* k, const void* v, const void* out, int
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(stats, 8))
     return SOL_EINVAL;
   if (check_route(route, N, Bk) != SOL_OK) return SOL_EINVAL;
-  if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION | SOL_F_OUT_BF16))
+  if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION | SOL_F_OUT_BF16 |
+                          SOL_F_GROUP_MASK))
     return SOL_EINVAL;
+  // a plan orders the items of the automatic group size
+  if ((flags & SOL_F_PLANNED) && (flags & SOL_F_GROUP_MASK)) return SOL_EINVAL;
   if ((flags & SOL_F_EXACT_ONLY) && (flags & SOL_F_ROW_CORRECTION)) return SOL_EINVAL;
   // exact-only under a Gaussian threshold: a query block whose threshold lies
   // above its best block would keep nothing, and its rows would have no terms
   if ((flags & SOL_F_EXACT_ONLY) && route.rule != SOL_ROUTE_ROWMAX && route.sink_count == 0) return SOL_EINVAL;
   if ((flags & SOL_F_PLANNED) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
-  return check_sizes(B, H, N, d, Bq, Bk);
+  const int rc = check_sizes(B, H, N, d, Bq, Bk);
+  if (rc != SOL_OK) return rc;
+  // eight query blocks per item only up to kMaxKeyBlocksG8 key blocks
+  if (((flags & SOL_F_GROUP_MASK) >> SOL_F_GROUP_SHIFT) == 3 && (N + 63) / 64 > sol::kMaxKeyBlocksG8)
+    return SOL_EUNSUPPORTED;
+  return SOL_OK;
 }
 
 int check_forward(const void* q, const void* k, const void* v, const void* out, int B, int H, int N,
@@ -186,7 +245,8 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   const WsLayout w = ws_layout(BH, N, d);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
-  const int nitems = sol::forward_items(BH, Nq);
+  const int group = group_of(flags, BH, Nq);
+  const int nitems = sol::forward_items(BH, Nq, group);
 
   const unsigned* perm = nullptr;
   hipError_t e = hipSuccess;
@@ -207,23 +267,31 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
     }
     // plan the order of the work where that was measured to pay (elsewhere
     // the items go in sequence; the order never changes the result)
-    if (e == hipSuccess && plan_by_default(route, BH, Nq, nitems)) {
+    if (e == hipSuccess && plan_by_default(route, BH, Nq, nitems, group)) {
       bool ordered = false;
       e = plan_impl(q16, kpool, BH, N, d, route.tau, ws, s, &ordered);
       perm = reinterpret_cast<const unsigned*>(wsb + w.perm);
     }
   }
   if (e != hipSuccess) return SOL_EHIP;
-  uint16_t* khi16 = reinterpret_cast<uint16_t*>(wsb + w.khi16);
-  uint16_t* klo16 = reinterpret_cast<uint16_t*>(wsb + w.klo16);
+  // bf16 operand planes of the routing pass (and of the per-row correction)
+  uint16_t* kh = reinterpret_cast<uint16_t*>(wsb + w.kh);
+  uint16_t* km = reinterpret_cast<uint16_t*>(wsb + w.km);
+  uint16_t* kl = reinterpret_cast<uint16_t*>(wsb + w.kl);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(wsb + w.vt);
   uint16_t* vbar16 = reinterpret_cast<uint16_t*>(wsb + w.vbar16);
-  if (flags & SOL_F_ROW_CORRECTION) {
-    e = sol::launch_to_bf16(kpool, khi16, klo16, vmean, vbar16, (size_t)BH * Nk * d, s);
-    if (e != hipSuccess) return SOL_EHIP;
-  }
+  const int Nkp = padded_blocks(Nk);
+  e = sol::launch_prep(kpool, vmean, kh, km, kl, vt, (flags & SOL_F_ROW_CORRECTION) ? vbar16 : nullptr, BH, Nk, Nkp,
+                       d, s);
+  if (e != hipSuccess) return SOL_EHIP;
   float* kstats = reinterpret_cast<float*>(wsb + w.kstats);
   if (route.rule == SOL_ROUTE_GAUSS_DIAG) {
     e = sol::launch_kstats(kpool, kstats, BH, Nk, d, s);
+    if (e != hipSuccess) return SOL_EHIP;
+  }
+  float* kmom = reinterpret_cast<float*>(wsb + w.kmom);
+  if (route.rule == SOL_ROUTE_GAUSS) {
+    e = sol::launch_kmom(kpool, kmom, BH, Nk, d, s);
     if (e != hipSuccess) return SOL_EHIP;
   }
 
@@ -243,6 +311,11 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   p.Nk = Nk;
   p.nitems = nitems;
   p.nwords = (Nk + 31) / 32;
+  p.group = group;
+  p.ngroups = (Nq + group - 1) / group;
+  p.route_only = 0;
+  p.static_grid = 0;
+  p.kmom = kmom;
   p.rule = route.rule;
   p.tau = route.rule == SOL_ROUTE_ROWMAX ? route.tau : 0.f;
   p.beta = route.rule != SOL_ROUTE_ROWMAX ? route.beta : 0.f;
@@ -254,14 +327,18 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   p.exact_only = (flags & SOL_F_EXACT_ONLY) ? 1 : 0;
   p.row_corr = (flags & SOL_F_ROW_CORRECTION) ? 1 : 0;
   p.out_bf16 = (flags & SOL_F_OUT_BF16) ? 1 : 0;
-  p.khi16 = khi16;
-  p.klo16 = klo16;
+  p.khi16 = kh;
+  p.klo16 = km;
+  p.klo2 = kl;
+  p.vt = vt;
+  p.Nkp = Nkp;
   p.vbar16 = vbar16;
   e = sol::launch_forward(p, d, s);
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 
-// Workspace of the top-k / top-p mask builders: pooled queries, then the map.
+// Workspace of the mask builders: top-k / top-p use [pooled queries | map];
+// the threshold router uses [three bf16 planes of the pooled keys].
 struct MaskWs {
   size_t map, total;
 };
@@ -270,7 +347,8 @@ MaskWs mask_ws(int BH, int N, int d) {
   const size_t Nq = (size_t)(N + 63) / 64;
   MaskWs w;
   w.map = round_up((size_t)BH * Nq * (size_t)d * 4, 256);
-  w.total = round_up(w.map + (size_t)BH * Nq * Nq * 4, 256);
+  const size_t planes = 3 * round_up((size_t)BH * padded_blocks((int)Nq) * (size_t)d * 2, 256);
+  w.total = std::max(round_up(w.map + (size_t)BH * Nq * Nq * 4, 256), planes);
   return w;
 }
 
@@ -316,26 +394,52 @@ size_t sol_attn_mask_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk)
 }
 
 int sol_attn_mask_threshold(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk,
-                            const sol_attn_route* route, uint32_t* kept_bitmap, void* stream) {
+                            const sol_attn_route* route, uint32_t* kept_bitmap, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   int rc = check_mask(q, kpool, B, H, N, d, Bq, Bk, kept_bitmap);
   if (rc != SOL_OK) return rc;
   if (!route || check_route(*route, N, Bk) != SOL_OK) return SOL_EINVAL;
-  if (route->rule == SOL_ROUTE_GAUSS_DIAG) return SOL_EUNSUPPORTED;
-  sol::MaskParams p;
+  // the Gaussian rules take their statistics from the forward's workspace
+  if (route->rule != SOL_ROUTE_ROWMAX) return SOL_EUNSUPPORTED;
+  if (!workspace || !aligned(workspace, 256)) return SOL_EINVAL;
+  const int BH = B * H, Nq = (N + 63) / 64;
+  if (workspace_bytes < mask_ws(BH, N, d).total) return SOL_EWORKSPACE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // the score operands (the pooled keys in three bf16 parts), as the forward makes them
+  const size_t plane = round_up((size_t)BH * padded_blocks(Nq) * (size_t)d * 2, 256);
+  uint16_t* kh = static_cast<uint16_t*>(workspace);
+  uint16_t* km = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) + plane);
+  uint16_t* kl = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) + 2 * plane);
+  hipError_t e = sol::launch_prep(kpool, nullptr, kh, km, kl, nullptr, nullptr, BH, Nq, padded_blocks(Nq), d, s);
+  if (e != hipSuccess) return SOL_EHIP;
+  // the forward's own fused kernel, stopped after its routing: one workgroup
+  // per item, no work queues, no correction sums; only the bitmap is written
+  sol::FwdParams p = {};
   p.q = static_cast<const uint16_t*>(q);
   p.kpool = kpool;
+  p.vmean = kpool;  // not read: no correction sums are formed
+  p.khi16 = kh;
+  p.klo16 = km;
+  p.klo2 = kl;
+  p.Nkp = padded_blocks(Nq);
   p.bitmap = kept_bitmap;
   p.N = N;
-  p.Nq = (N + 63) / 64;
-  p.Nk = p.Nq;
-  p.nwords = (p.Nk + 31) / 32;
-  p.rule = route->rule;
-  p.tau = route->rule == SOL_ROUTE_ROWMAX ? route->tau : 0.f;
-  p.beta = route->rule == SOL_ROUTE_GAUSS ? route->beta : 0.f;
-  p.proxy_scale = (float)(1.0 / sqrt((double)d));
+  p.Nq = Nq;
+  p.Nk = Nq;
+  p.nwords = (Nq + 31) / 32;
+  p.group = auto_group(BH, Nq);
+  p.ngroups = (Nq + p.group - 1) / p.group;
+  p.nitems = sol::forward_items(BH, Nq, p.group);
+  p.route_only = 1;
+  p.static_grid = 1;
+  p.rule = SOL_ROUTE_ROWMAX;
+  p.tau = route->tau;
   p.sink_lo = route->sink_count > 0 ? route->sink_first : 0;
   p.sink_hi = route->sink_count > 0 ? route->sink_first + route->sink_count : 0;
-  const hipError_t e = sol::launch_mask_threshold(p, d, B * H, reinterpret_cast<hipStream_t>(stream));
+  p.proxy_scale = (float)(1.0 / sqrt((double)d));
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+  p.exact_only = 1;
+  e = sol::launch_forward(p, d, s);
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 

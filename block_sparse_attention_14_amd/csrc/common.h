@@ -89,6 +89,11 @@ __device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// 8-byte load; bytes at or beyond the resource's size read as zero.
+__device__ __forceinline__ uint2 ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+  return make_uint2(v[0], v[1]);
+}
 __device__ __forceinline__ float4 ld16f(rsrc_t r, uint32_t voff, uint32_t soff) {
   const uint4 u = ld16(r, voff, soff);
   return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
@@ -102,6 +107,12 @@ __device__ __forceinline__ float colsum_rows(float x) {
   if (CH == 8) x += dpp<kDppRor8>(x);
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Sum of a value over lanes l and l ^ 32 (every lane gets it).
+__device__ __forceinline__ float sum_half32(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }

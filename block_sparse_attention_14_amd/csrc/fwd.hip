@@ -4,53 +4,60 @@
 // Method (page "Sol-Attn: Accelerating Video Generation Inference via
 // On-the-Fly Attention Sparsification", paperlayer.ai summary):
 //   §2 "Block-Sparse Attention"      proxy s_ij = mean(q_i).mean(k_j)/sqrt(d)
-//   §3 "Dynamic threshold routing"   keep j iff s_ij >= max_j s_ij - tau
-//   §3 "On-the-fly sparsification"   proxy rows and kept lists live in LDS
-//                                    only; nothing routing-related is written
-//                                    to device memory
+//   §3 "Dynamic threshold routing"   keep j iff s_ij >= max_j s_ij - tau, or the
+//                                    Gaussian-calibrated mean + beta std of the
+//                                    row, from pooled-key moments
+//   §3 "On-the-fly sparsification"   scores are consumed chunk by chunk as
+//                                    they are produced; nothing routing-related
+//                                    is written to device memory
 //   §3 "Approximate correction"      skipped j adds n_j e^{s_ij} mean(v_j) to the
 //                                    numerator and n_j e^{s_ij} to the denominator
 //   §3 "Unified execution"           one online-softmax state per row holds the
 //                                    exact and the corrected terms
 //
-// Work decomposition. A work item is a PAIR of neighbouring 64-row query
-// blocks (b, h, 2p) and (b, h, 2p+1). A persistent grid of 256-thread
+// Work decomposition. A work item is a GROUP of G consecutive 64-row query
+// blocks of one head (G = 2, 4 or 8, chosen by the host so that there are
+// enough items to balance the grid). A persistent grid of 256-thread
 // workgroups (two per CU) takes items from atomic ticket counters: per-block
 // budgets differ by two orders of magnitude, so a static split would idle CUs.
 // There is one queue per XCD, each over a contiguous head-major range of items
-// (so an XCD's L2 holds the pooled keys and values of few heads at a time);
-// a workgroup whose queue is drained takes from the others. With a plan
+// (so an XCD's L2 holds the pooled keys and values of few heads at a time); a
+// workgroup whose queue is drained takes from the others. With a plan
 // (sol_attn_plan, or the forward's own where it pays) the tickets of a queue
-// map to its items through the planned order: the first two thirds in
-// sequence, so neighbouring blocks (which keep overlapping key blocks) share
-// K/V tiles in L2, the last third heaviest first, so no workgroup starts a
-// heavy item late.
-// Pairing halves the pooled-key / pooled-value traffic of routing and
-// correction (one read serves both rows) and lets one K/V tile in LDS serve
-// both blocks whenever both keep it, which neighbours usually do.
+// map to its items through the planned order.
 //
 // Per item:
-//   1. both Q tiles arrive through buffer loads (rows past the sequence read
-//      as zero) and pass through LDS once to become, per wave, the B operand
-//      of S^T = K Q^T (waves 0-1 own block A, waves 2-3 block B, 32 rows
-//      each); the pooled queries are summed from the same registers;
-//   2. the two fp32 proxy rows are built in LDS from pooled keys, eight lanes
-//      per key block (their partial dot products meet through DPP moves), a
-//      batch of loads in flight before any use;
-//   3. per row: max, threshold (max - tau, or the Gaussian-calibrated
-//      mean + beta std of the row, §3 "Dynamic threshold routing"), forced
-//      sink blocks (App. A), skipped scores turned into correction weights
-//      n_j e^{s_j - M}; a ballot/prefix pass writes the UNION of the two kept
-//      lists (ascending, 2-bit owner mask) to LDS;
-//   4. the correction numerators sum_j w_j mean(v_j) of both rows, one pass
-//      over the pooled values, the next batch of loads in flight while one
-//      is used and a batch's weights read from LDS together;
-//   5. for every union entry, the K and V tiles stream from HBM straight into
+//   A. the pooled queries of the G blocks, from their rows (buffer loads; rows
+//      past the sequence read as zero), and, for the Gaussian rules, each
+//      block's threshold from the head's pooled-key moments (known before any
+//      score exists);
+//   R. one streaming pass over the head's pooled keys and pooled values, in
+//      chunks of 256 key blocks, starting at the chunk of the group's own
+//      blocks and moving outwards. Per chunk:
+//        R1 the proxy scores of all G blocks: eight lanes per key block, each
+//           with 16 (d = 128) or 8 columns of every pooled query in
+//           registers; the eight partial dot products of a key block are
+//           reduced so that lane g of the eight ends with block g's score;
+//        R2 per block: the running row maximum, the threshold (running
+//           maximum - tau, or the fixed Gaussian one), keep or skip, the
+//           weight n_j e^{s - M} of each skipped block against the running
+//           maximum (earlier weights rescaled when it rises), kept bits;
+//        R3 the correction numerators sum_j w_j vbar_j of all G blocks
+//           (rescaled with the running maximum), each pooled value read once
+//           for the whole group;
+//      so the group reads the pooled keys and values once: G/2 times less
+//      than pairs of blocks would, which is what long sequences need;
+//   R4. row-max rule only: a block kept against a running maximum that later
+//      rose by more than its margin is rechecked against the final maximum
+//      and, if below it, moved to the correction; the group's bits are final;
+//   then for each PAIR of blocks of the group:
+//   1. both Q tiles through LDS into registers, the B operand of S^T = K Q^T
+//      (waves 0-1 own block A, waves 2-3 block B, 32 rows each);
+//   2. the union of the two kept lists (ascending, 2-bit owner mask) from the
+//      kept bits;
+//   3. for every union entry, the K and V tiles stream from HBM straight into
 //      LDS (buffer loads with an LDS destination, no registers involved),
-//      double-buffered in two stages, one barrier per tile, the copy into
-//      one stage issued before the other stage is consumed (the compiler
-//      still makes the reads of stage A wait for a copy into stage B; the
-//      other workgroup on the CU covers that wait). 16-byte chunks are
+//      double-buffered in two stages, one barrier per tile. 16-byte chunks are
 //      XOR-swizzled per row through the per-lane source addresses, so both
 //      operand reads below are bank-conflict free. Each wave whose block keeps
 //      the entry computes its 64x32 S^T with 16x16x32 bf16 MFMAs, the online
@@ -58,11 +65,11 @@
 //      two permlane swaps reduce a row), the row sums as an MFMA against a
 //      ones operand, and O^T += V^T P^T with V^T operands read from the
 //      row-major V tile by transposing LDS reads (ds_read_b64_tr_b16);
-//   6. exact state and correction merge under a common maximum; rows are
-//      normalised and stored in fp32 (or rounded to bf16 on request). The
-//      next item's ticket is resolved before the stores and the item
-//      boundary waits for LDS only, so the stores drain while the next item
-//      starts (nothing in the kernel reads the output).
+//   4. exact state and correction merge under a common maximum; rows are
+//      normalised and stored in fp32 (or rounded to bf16 on request). After
+//      the last pair the next item's ticket is resolved before the stores and
+//      the item boundary waits for LDS only, so the stores drain while the
+//      next item starts (nothing in the kernel reads the output).
 #include <math.h>
 
 #include <algorithm>
@@ -92,7 +99,6 @@ constexpr int kThreads = 256;
 // this (base-2 units); until then probabilities may reach 2^8, which fp32 and
 // bf16 carry as exactly (relatively) as values below 1.
 constexpr float kLazyRescale = 8.0f;
-constexpr int kMaxKeyWords = (SOL_ATTN_MAX_N / kBlk + 31) / 32;
 // max over the four lanes l, l^16, l^32, l^48 that share one query row
 __device__ __forceinline__ float rowmax4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -101,11 +107,17 @@ __device__ __forceinline__ float rowmax4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Words of kept bits per query block: groups of eight blocks are used up to
+// 2048 key blocks, smaller groups up to the longest supported head.
+template <int G>
+constexpr int key_words() {
+  return G == 8 ? kMaxKeyBlocksG8 / 32 : (SOL_ATTN_MAX_N / kBlk) / 32;
+}
+
 // LDS geometry. A K or V tile is 64 rows of 2d bytes, stored unpadded with
 // the 16-byte chunks of each row XOR-swizzled (kslot / vslot below); a stage
 // holds one K tile and one V tile. Before the kept loop the two stages also
-// hold the staged Q tiles (padded rows), the routing rows and the reduction
-// scratch.
+// hold the routing buffers of the group and the staged Q tiles.
 template <int D>
 struct Geom {
   static constexpr int RB = 2 * D;           // bytes per K / V row
@@ -145,12 +157,15 @@ __device__ __forceinline__ uint2 ld_tr(const unsigned char* p) {
 // swizzles depend on row bits the chunk index does not touch), so only a
 // scalar offset changes between the copies.
 // One 64-row tile into dst, chunks placed as K rows (kslot) or V rows (vslot).
-template <int D, bool KROWS>
+// The source is row-major (row r's chunk c at r * RB + 16 c) or, TILED, in
+// 16-row tiles stored chunk by chunk (at (r / 16) * 16 RB + (16 c + r % 16) * 16).
+template <int D, bool KROWS, bool TILED = false>
 __device__ __forceinline__ void dma_one(unsigned char* dst, rsrc_t r, int wid, int lane) {
   using G = Geom<D>;
   constexpr int LPR = G::RB / 16;
   const int row = (1024 * wid) / G::RB + lane / LPR, sl = lane % LPR;
-  const uint32_t o = row * G::RB + 16 * (KROWS ? kslot<D>(row, sl) : vslot<D>(row, sl));
+  const int c = KROWS ? kslot<D>(row, sl) : vslot<D>(row, sl);
+  const uint32_t o = TILED ? (row >> 4) * 16 * G::RB + (16 * c + (row & 15)) * 16 : row * G::RB + 16 * c;
 #pragma unroll
   for (int u = 0; u < G::NCH / 4; ++u)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 1024 * (wid + 4 * u)), 16, o, 4096 * u, 0, 0);
@@ -171,46 +186,69 @@ __device__ __forceinline__ void dma_tile(unsigned char* stage, rsrc_t rk, rsrc_t
   }
 }
 
-template <int D>
+// State of one group that outlives its routing pass (the kept loops of its
+// pairs read it), plus the workgroup's small scratch.
+template <int D, int G>
 struct alignas(16) Small {
-  float qbar[2][D];  // pooled queries of blocks A and B
-  float cnum[2][D];  // correction numerators
-  float wred[2][8];
-  float gred[2][8];  // row sums, then squared deviations (Gaussian threshold)
-  uint32_t kbits[2][kMaxKeyWords];  // kept-block bits of blocks A and B
-  float cden[2];
+  float cnum[G][D];                 // correction numerators
+  float cden[G];                    // correction denominators
+  float M[G];                       // row maxima of the proxy scores (natural units)
+  float theta[G];                   // Gaussian thresholds
+  float wmax[4][16];                // per wave and column: maximum over the wave's first step
+  float wfin[4][16];                // per wave and column: the wave's final maximum
+  float wden[4][16];                // per wave and column: the wave's correction denominator
+  uint32_t kbits[G][key_words<G>()];  // kept-block bits
   int cnt[3][4];
   int lastkept[2];
   int item;  // the item of the next iteration (-1: none left)
   int last;  // this workgroup finished last
 };
 
+// The k-th step of the outward order that starts at step cs: cs, cs+1,
+// cs-1, cs+2, ... (steps outside 0 .. nch-1 are left out).
+__device__ __forceinline__ int chunk_at(int k, int cs, int nch) {
+  // the k-th valid entry: first the symmetric part, then the longer side
+  const int below = cs, above = nch - 1 - cs, sym = min(below, above);
+  if (k <= 2 * sym) return k == 0 ? cs : ((k & 1) ? cs + (k + 1) / 2 : cs - k / 2);
+  const int rest = k - 2 * sym;  // 1, 2, ... on the longer side
+  return above > below ? cs + sym + rest : cs - sym - rest;
+}
+
 // RC: the per-row (token-to-block) correction replaces the block-level one.
-template <int D, bool RC>
+template <int D, int G, bool RC>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
-  using G = Geom<D>;
+  using GM = Geom<D>;
   // Two separate LDS objects for the two stages, so that reads of one stage
   // never wait for copies still landing in the other.
-  __shared__ __attribute__((aligned(16))) unsigned char stA[G::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char stB[G::STAGE];
-  __shared__ Small<D> sm;
+  __shared__ __attribute__((aligned(16))) unsigned char stA[GM::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char stB[GM::STAGE];
+  __shared__ Small<D, G> sm;
   extern __shared__ __align__(16) unsigned char dyn[];
   uint16_t* ulist = reinterpret_cast<uint16_t*>(dyn);  // [Nk] union of kept lists: j | A<<14 | B<<15
-  const int Nk = p.Nk, N = p.N;
-  float* wrow0 = reinterpret_cast<float*>(stA);  // [Nk] block A: scores, then weights (before the kept loop)
-  float* wrow1 = reinterpret_cast<float*>(stB);  // [Nk] block B
+  constexpr int KW = key_words<G>();
+  // routing buffers in the stages (before any pair's kept loop):
+  //   stA: qbar[G][D] pooled queries
+  //   stB: [4][G][D] per-wave partial sums (pooled queries, Gaussian
+  //        statistics, correction numerators)
+  static_assert(G * D * 4 <= GM::STAGE, "routing buffers exceed stage A");
+  static_assert(4 * G * D * 4 <= GM::STAGE, "routing buffers exceed stage B");
+  float* qbar = reinterpret_cast<float*>(stA);
+  float* part = reinterpret_cast<float*>(stB);  // [4 waves][G][D]
 
+  const int Nk = p.Nk, N = p.N, Nq = p.Nq;
   constexpr int NDS = D / 32;  // k-steps of S^T along d
   constexpr int NDT = D / 16;  // 16-row tiles of O^T along d
   constexpr int CH = D / 8;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int g = lane >> 4, c16 = lane & 15;
-  const int qb = wid >> 1;           // which block of the pair this wave serves
+  const int g16 = lane >> 4, c16 = lane & 15;
+  const int qb = wid >> 1;           // which block of a pair this wave serves
   const int qrow0 = 32 * (wid & 1);  // first of its 32 rows in that block
-  const int npairs = (p.Nq + 1) >> 1;
   const int nlast = N - (Nk - 1) * kBlk;
   const float csc = p.scale_log2;
+  const bool rowmax = p.rule == SOL_ROUTE_ROWMAX;
+  // block-level correction sums are formed (not in the per-row or exact-only modes)
+  const bool corr = !RC && !p.exact_only;
   // per-row correction: log2(n_j) of a full and of the ragged last key block
   // in raw dot-product units, formed once (per element they would become a
   // branch around a division)
@@ -244,248 +282,538 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     const unsigned it = rank < 0 ? ~0u : (p.perm ? p.perm[rank] : (unsigned)rank);
     return it < (unsigned)p.nitems ? (int)it : -1;
   };
-  if (tid == 0) sm.item = item_of(take(ticket()));
+  if (tid == 0) sm.item = p.static_grid ? (int)blockIdx.x : item_of(take(ticket()));
   __syncthreads();
   for (;;) {
     const int item = sm.item;
     if (item < 0) break;
-    const int bh = item / npairs;  // head-major: neighbouring pairs are consecutive tickets
-    const int qA = 2 * (item - bh * npairs);
-    const bool hasB = qA + 1 < p.Nq;
+    const int bh = item / p.ngroups;  // head-major: neighbouring groups are consecutive tickets
+    const int g0 = G * (item - bh * p.ngroups);
     const size_t hoff = (size_t)bh * N * D;
-    const int nA = min(kBlk, N - qA * kBlk);
-    const int nB = hasB ? min(kBlk, N - (qA + 1) * kBlk) : 0;
-    const int nmine = qb ? nB : nA;
+    // The thread index passes through an empty asm statement, so that the
+    // per-lane offsets of the routing pass are formed for each item instead
+    // of being hoisted out of the item loop and held (or spilled) through the
+    // kept loops.
+    int tid_i = tid;
+    asm volatile("" : "+v"(tid_i));
+    const int tid = tid_i, lane = tid_i & 63;
 
-    // ---- 1. Q tiles -> LDS -> Q^T operands; pooled queries from the same registers ----
-    bf16x8 qop[2][NDS];
+    // routing geometry and the operands of this wave's first step, whose
+    // loads are issued before the pooled queries are formed
+    constexpr int CT = D / 16;   // 16-column tiles of the pooled values
+    constexpr int NQB = D / 32;  // k-steps of a score tile
+    const int col = lane & 15, kq = lane >> 4;
+    const int nst = (Nk + 15) / 16;
+    const int cs = min(g0 / 16, nst - 1);
+    const bool gval = col < G && g0 + col < Nq;  // this lane's column is a score of a block of the group
+    uint16_t* kb16 = reinterpret_cast<uint16_t*>(&sm.kbits[0][0]);  // 16 kept bits per step
+    f32x4 accv[CT];
+#pragma unroll
+    for (int ci = 0; ci < CT; ++ci) accv[ci] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float Mw = -INFINITY;  // the wave's running maximum of column col's scores
+    float cdl = 0.f;       // this lane's share of the correction denominator
+    int nseq = 0;          // steps this wave has routed
+    int nlow = 0;          // of them, the ones routed before Mw reached its current value
+    // the operand planes of the head: 16-block tiles of 16 * D bf16, stored
+    // in operand order (a wave's load is one contiguous stretch)
+    const size_t tplane = (size_t)bh * p.Nkp * D;
+    const uint32_t tbytes = (uint32_t)p.Nkp * D * 2;
+    constexpr uint32_t kTile = 16 * D * 2;
+    const rsrc_t rk0 = make_rsrc(p.khi16 + tplane, tbytes);
+    const rsrc_t rk1 = make_rsrc(p.klo16 + tplane, tbytes);
+    const rsrc_t rk2 = make_rsrc(p.klo2 + tplane, tbytes);
+    const rsrc_t rv = make_rsrc(corr ? p.vt + tplane : p.khi16, corr ? tbytes : 0u);
+    // operands of a step: the key parts (each k-step's loaded for the next
+    // step as soon as this step's products have taken it) and the values
+    // (loaded when the step starts; first used after its scores)
+    struct StepOps {
+      bf16x8 k[3][NQB];  // rows col, 8-column chunks 4 ks + kq of the three key parts
+    };
+    struct StepVals {
+      i16x4 v[CT];  // column 16 ci + col of the values, key blocks 4 kq .. +3
+    };
+    auto load_ks = [&](StepOps& b, int st, int ks) {
+      const int o = st * (int)kTile + 16 * lane + 1024 * ks;
+      b.k[0][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk0, o, 0, 0));
+      b.k[1][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk1, o, 0, 0));
+      b.k[2][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk2, o, 0, 0));
+    };
+    auto load_step = [&](StepOps& b, int st) {
+#pragma unroll
+      for (int ks = 0; ks < NQB; ++ks) load_ks(b, st, ks);
+    };
+    auto load_vals = [&](StepVals& b, int st) {
+      if (corr) {
+        const int ov = st * (int)kTile + 8 * lane;
+#pragma unroll
+        for (int ci = 0; ci < CT; ++ci)
+          b.v[ci] = __builtin_bit_cast(i16x4, __builtin_amdgcn_raw_buffer_load_b64(rv, ov, 512 * ci, 0));
+      }
+    };
+    const int stEnd = p.Nkp / 16;
+    auto step_of = [&](int kk) { return kk < nst ? chunk_at(kk, cs, nst) : stEnd; };
+    StepOps b;
+    StepVals vv;
+
+    // ---- A. pooled queries of the G blocks; Gaussian thresholds ----
     {
       constexpr int PER = kBlk * CH / kThreads, RSTEP = kThreads / CH;
       const uint32_t qoff = ((tid / CH) * D + (tid % CH) * 8) * 2;
-      uint4 qr[2][PER];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const int nb = blk ? nB : nA;
-        const rsrc_t r = make_rsrc(p.q + hoff + (size_t)(qA + blk) * kBlk * D, (uint32_t)nb * D * 2);
+      for (int pr = 0; pr < G / 2; ++pr) {
+        uint4 qr[2][PER];
 #pragma unroll
-        for (int u = 0; u < PER; ++u) qr[blk][u] = ld16(r, qoff, u * RSTEP * D * 2);
-      }
-      float* part = reinterpret_cast<float*>(stA + kBlk * G::QS * 2);  // [4 waves][2][D], past Q tile A
+        for (int blk = 0; blk < 2; ++blk) {
+          const int qi = g0 + 2 * pr + blk;
+          const int nb = qi < Nq ? min(kBlk, N - qi * kBlk) : 0;
+          const rsrc_t r = make_rsrc(p.q + hoff + (size_t)min(qi, Nq - 1) * kBlk * D, (uint32_t)nb * D * 2);
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        uint16_t* qd = reinterpret_cast<uint16_t*>(blk ? stB : stA) + (tid / CH) * G::QS + (tid % CH) * 8;
-        float cs[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cs[e] = 0.f;
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          *reinterpret_cast<uint4*>(qd + u * RSTEP * G::QS) = qr[blk][u];
-          const uint4 w = qr[blk][u];
-          cs[0] += bf16lo(w.x); cs[1] += bf16hi(w.x); cs[2] += bf16lo(w.y); cs[3] += bf16hi(w.y);
-          cs[4] += bf16lo(w.z); cs[5] += bf16hi(w.z); cs[6] += bf16lo(w.w); cs[7] += bf16hi(w.w);
+          for (int u = 0; u < PER; ++u) qr[blk][u] = ld16(r, qoff, u * RSTEP * D * 2);
         }
-        // lanes l, l ^ 16, l ^ 32, l ^ 48 (and l ^ 8 when a row has 8 chunks)
-        // hold the same columns of other rows
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cs[e] = colsum_rows<CH>(cs[e]);
-        if (lane < CH) {
+        for (int blk = 0; blk < 2; ++blk) {
+          float csum[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) part[(wid * 2 + blk) * D + lane * 8 + e] = cs[e];
+          for (int e = 0; e < 8; ++e) csum[e] = 0.f;
+#pragma unroll
+          for (int u = 0; u < PER; ++u) {
+            const uint4 w = qr[blk][u];
+            csum[0] += bf16lo(w.x); csum[1] += bf16hi(w.x); csum[2] += bf16lo(w.y); csum[3] += bf16hi(w.y);
+            csum[4] += bf16lo(w.z); csum[5] += bf16hi(w.z); csum[6] += bf16lo(w.w); csum[7] += bf16hi(w.w);
+          }
+          // lanes l, l ^ 16, l ^ 32, l ^ 48 (and l ^ 8 when a row has 8 chunks)
+          // hold the same columns of other rows
+#pragma unroll
+          for (int e = 0; e < 8; ++e) csum[e] = colsum_rows<CH>(csum[e]);
+          if (lane < CH) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[(wid * G + 2 * pr + blk) * D + lane * 8 + e] = csum[e];
+          }
         }
       }
+      // routing state of the group
+      if (tid < G) sm.M[tid] = -INFINITY;
+      for (int w = tid; w < G * KW; w += kThreads) (&sm.kbits[0][0])[w] = 0u;
       __syncthreads();
-      if (tid < 2 * D) {
-        const int blk = tid / D, col = tid % D;
-        const int nb = blk ? nB : nA;
-        const float sq = (part[(0 * 2 + blk) * D + col] + part[(1 * 2 + blk) * D + col]) +
-                         (part[(2 * 2 + blk) * D + col] + part[(3 * 2 + blk) * D + col]);
-        sm.qbar[blk][col] = nb > 0 ? sq / (float)nb : 0.f;
+      for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int g = idx / D, col = idx % D;
+        const int qi = g0 + g;
+        const int nb = qi < Nq ? min(kBlk, N - qi * kBlk) : 0;
+        const float sq = (part[(0 * G + g) * D + col] + part[(1 * G + g) * D + col]) +
+                         (part[(2 * G + g) * D + col] + part[(3 * G + g) * D + col]);
+        qbar[idx] = nb > 0 ? sq / (float)nb : 0.f;
       }
-      const uint16_t* qs = reinterpret_cast<const uint16_t*>(qb ? stB : stA) + (qrow0 + c16) * G::QS + 8 * g;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds)
-          qop[qt][ds] = as_bf16x8(*reinterpret_cast<const uint4*>(&qs[16 * qt * G::QS + 32 * ds]));
-    }
-    __syncthreads();  // qbar complete; the Q tiles may now be overwritten
+      __syncthreads();  // pooled queries complete
 
-    // ---- 2. proxy rows s_j = q̄ . k̄_j / sqrt(d), both blocks, into LDS ----
-    {
-      constexpr int NV = D / 32;  // float4 per lane; 8 lanes cover one pooled key
-      constexpr int U = 4;        // key blocks in flight per lane (64 KiB per workgroup at d=128)
-      constexpr int JS = kThreads / 8;
-      const int sub = tid & 7, jg = tid >> 3;
-      float4 qa[NV], qbv[NV];
+      // Gaussian thresholds theta = mu + beta sigma, known before any score
+      // (§3 "Dynamic threshold routing"; App. B): mu = qbar . m_K / sqrt(d),
+      // sigma^2 = qbar^T C_K qbar / d (pooled-key covariance, SOL_ROUTE_GAUSS)
+      // or sum_c qbar_c^2 v_Kc / d (its diagonal, SOL_ROUTE_GAUSS_DIAG)
+      if (!rowmax) {
+        float a[G], b[G];
 #pragma unroll
-      for (int t = 0; t < NV; ++t) {
-        qa[t] = *reinterpret_cast<const float4*>(&sm.qbar[0][4 * (sub + 8 * t)]);
-        qbv[t] = *reinterpret_cast<const float4*>(&sm.qbar[1][4 * (sub + 8 * t)]);
-      }
-      const rsrc_t rk = make_rsrc(p.kpool + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
-      const uint32_t voff = (jg * D + sub * 4) * 4;
-      float mA = -INFINITY, mB = -INFINITY;
-      for (int j0 = 0; j0 < Nk; j0 += U * JS) {
-        float4 x[U][NV];
+        for (int g = 0; g < G; ++g) a[g] = b[g] = 0.f;
+        if (tid < D) {
+          if (p.rule == SOL_ROUTE_GAUSS_DIAG) {
+            const float mu = p.kstats[(size_t)bh * 2 * D + tid];
+            const float var = p.kstats[(size_t)bh * 2 * D + D + tid];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int t = 0; t < NV; ++t) x[u][t] = ld16f(rk, voff + t * 128, (uint32_t)(j0 + u * JS) * D * 4);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = j0 + u * JS + jg;
-          float a = 0.f, b = 0.f;
-#pragma unroll
-          for (int t = 0; t < NV; ++t) {
-            a += qa[t].x * x[u][t].x + qa[t].y * x[u][t].y + qa[t].z * x[u][t].z + qa[t].w * x[u][t].w;
-            b += qbv[t].x * x[u][t].x + qbv[t].y * x[u][t].y + qbv[t].z * x[u][t].z + qbv[t].w * x[u][t].w;
-          }
-          a = sum8(a);  // the 8 lanes of key block j
-          b = sum8(b);
-          a *= p.proxy_scale;
-          b *= p.proxy_scale;
-          if (j < Nk) {
-            if (sub == 0) {
-              wrow0[j] = a;
-              wrow1[j] = b;
+            for (int g = 0; g < G; ++g) {
+              const float x = qbar[g * D + tid];
+              a[g] = x * mu;
+              b[g] = x * x * var;
             }
-            mA = fmaxf(mA, a);
-            mB = fmaxf(mB, b);
+          } else {
+            const float mu = p.kmom[(size_t)bh * (D + 1) * D + tid];
+            // row tid of C_K against every pooled query: y_g = (C_K qbar_g)[tid]
+            const float* crow = p.kmom + (size_t)bh * (D + 1) * D + (size_t)(1 + tid) * D;
+            float y[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) y[g] = 0.f;
+            for (int c = 0; c < D; c += 4) {
+              const float4 cv = *reinterpret_cast<const float4*>(crow + c);
+#pragma unroll
+              for (int g = 0; g < G; ++g) {
+                const float4 qv = *reinterpret_cast<const float4*>(&qbar[g * D + c]);
+                y[g] += cv.x * qv.x + cv.y * qv.y + cv.z * qv.z + cv.w * qv.w;
+              }
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const float x = qbar[g * D + tid];
+              a[g] = x * mu;
+              b[g] = x * y[g];
+            }
           }
         }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          a[g] = wave_sum(a[g]);
+          b[g] = wave_sum(b[g]);
+        }
+        if (lane == 0) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            part[(wid * G + g) * 2] = a[g];
+            part[(wid * G + g) * 2 + 1] = b[g];
+          }
+        }
+        __syncthreads();
+        if (tid < G) {
+          float sa = 0.f, sb = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            sa += part[(w * G + tid) * 2];
+            sb += part[(w * G + tid) * 2 + 1];
+          }
+          const float inv_d = p.proxy_scale * p.proxy_scale;
+          sm.theta[tid] = sa * p.proxy_scale + p.beta * sqrtf(fmaxf(sb * inv_d, 0.f));
+        }
+        __syncthreads();
       }
-      mA = wave_max(mA);
-      mB = wave_max(mB);
-      if (lane == 0) {
-        sm.wred[0][wid] = mA;
-        sm.wred[1][wid] = mB;
+    }
+
+    // ---- R. the routing pass over the pooled keys and values ----
+    // Both products run on the matrix cores; lane l = col + 16 kq supplies
+    // row col of A and column col of B, and holds rows 4kq .. 4kq+3 of column
+    // col of the result:
+    //   scores  S^T[j][col] = sum_p kbar_p[j] . B[col] (16x16x32), the pooled
+    //           keys as three bf16 parts against the pooled queries as three
+    //           parts in the columns of B, [qh | qm | ql] (G <= 4) or [qh | qm]
+    //           and [ql | 0] (G = 8, kh only, the products below 2^-24 left
+    //           out); a block's score is the sum of its columns, an fp32-grade
+    //           dot product;
+    //   numerators cnum^T[c][col] = sum_j vbar^T[c][j] W[j][col] (16x16x16),
+    //           the pooled values in bf16 against the weights of the skipped
+    //           blocks in two parts, columns [wh | wl]. The score tile's result
+    //           layout is the weight operand's layout, so the weights never
+    //           leave the lanes that form them.
+    // The key blocks are cut into 16-block steps, taken outwards from the
+    // group's own blocks; wave w takes every fourth step and streams on its own
+    // (the next step's operands load while the current one is used), the
+    // waves merging at the end. Each wave keeps a running maximum per block
+    // and a correction against it (earlier terms rescaled when it rises).
+    // Gaussian rules: the threshold is known, so every decision is final when
+    // made. Row-max rule: a block is kept while its score is within tau of the
+    // running maximum; the maximum over the first step of every wave (the 64
+    // key blocks nearest the group's own) is taken before any decision, and
+    // once the true maximum is known, the blocks kept before the wave's
+    // maximum reached it are checked again (only where it rose after that
+    // first step, which the order makes rare) and the ones that fall below
+    // move to the correction.
+    {
+      // score B operands, from the pooled queries in LDS
+      bf16x8 qB1[NQB], qB2[NQB];
+      {
+        const int qp = G == 8 ? (col >> 3) : col / G;  // which part of the pooled query
+        const int g = G == 8 ? (col & 7) : col % G;
+        const bool on1 = G == 8 || col < 3 * G;
+        const bool on2 = G == 8 && col < 8;
+#pragma unroll
+        for (int ks = 0; ks < NQB; ++ks) {
+          uint32_t w1[4], w2[4];
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            float h[2], m[2], l[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float x = qbar[g * D + 32 * ks + 8 * kq + i + e];
+              h[e] = __uint_as_float(pack_bf16x2(x, 0.f) << 16);
+              const float r1 = x - h[e];
+              m[e] = __uint_as_float(pack_bf16x2(r1, 0.f) << 16);
+              l[e] = __uint_as_float(pack_bf16x2(r1 - m[e], 0.f) << 16);
+            }
+            const float* pick = qp == 0 ? h : qp == 1 ? m : l;
+            w1[i / 2] = on1 ? pack_bf16x2(pick[0], pick[1]) : 0u;
+            w2[i / 2] = on2 ? pack_bf16x2(l[0], l[1]) : 0u;
+          }
+          qB1[ks] = as_bf16x8(make_uint4(w1[0], w1[1], w1[2], w1[3]));
+          qB2[ks] = as_bf16x8(make_uint4(w2[0], w2[1], w2[2], w2[3]));
+        }
+      }
+      // the step's scores of column col's block, key blocks 16 st + 4 kq + e;
+      // the operands of step stn are loaded into b meanwhile (stn = stEnd, a
+      // tile past the plane, reads zeros without touching memory)
+      auto step_scores = [&](StepOps& b, int st, float (&sc)[4], int stn) {
+        f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NQB; ++ks) {
+          s1 = mfma16x16x32(b.k[0][ks], qB1[ks], s1);
+          s1 = mfma16x16x32(b.k[1][ks], qB1[ks], s1);
+          s1 = mfma16x16x32(b.k[2][ks], qB1[ks], s1);
+          if (G == 8) s2 = mfma16x16x32(b.k[0][ks], qB2[ks], s2);
+          load_ks(b, stn, ks);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // lane col g < G gathers its block's columns (g + G and g + 2G, or g + 8)
+          float v = s1[e];
+          if (G == 8)
+            v += __shfl_down(s1[e], 8, 16) + s2[e];
+          else
+            v += __shfl_down(s1[e], G, 16) + __shfl_down(s1[e], 2 * G, 16);
+          v *= p.proxy_scale;
+          if (!gval || 16 * st + 4 * kq + e >= Nk) v = -INFINITY;
+          sc[e] = v;
+        }
+      };
+      // correction weights w[e] (relative to Mw) of the step into the
+      // numerators, after rescaling them by alpha (per column)
+      auto accumulate = [&](const StepVals& b, const float (&w)[4], float alpha) {
+        uint32_t hp[2], lp[2];
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const float h0 = __uint_as_float(pack_bf16x2(w[e], 0.f) << 16);
+          const float h1 = __uint_as_float(pack_bf16x2(w[e + 1], 0.f) << 16);
+          hp[e / 2] = pack_bf16x2(h0, h1);
+          lp[e / 2] = pack_bf16x2(w[e] - h0, w[e + 1] - h1);
+        }
+        // column col of the weight operand: the high parts of block col
+        // (col < G), the remainders of block col - G (G <= col < 2G), else 0
+        const uint32_t l0 = __shfl_up(lp[0], G, 16), l1 = __shfl_up(lp[1], G, 16);
+        const uint32_t b0 = col < G ? hp[0] : col < 2 * G ? l0 : 0u;
+        const uint32_t b1 = col < G ? hp[1] : col < 2 * G ? l1 : 0u;
+        const i16x4 wB = __builtin_bit_cast(i16x4, make_uint2(b0, b1));
+        if (__ballot(alpha != 1.f)) {
+          const float ar = __shfl_up(alpha, G, 16);
+          const float al = col < G ? alpha : col < 2 * G ? ar : 1.f;
+#pragma unroll
+          for (int ci = 0; ci < CT; ++ci) accv[ci] *= al;
+        }
+#pragma unroll
+        for (int ci = 0; ci < CT; ++ci)
+          accv[ci] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(b.v[ci], wB, accv[ci], 0, 0, 0);
+      };
+      // the 16 kept bits of column col's block in the step: OR over its four lanes
+      auto or4 = [](uint32_t x) {
+        const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        x = a[0] | a[1];
+        const auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return c[0] | c[1];
+      };
+      const float thg = !rowmax && col < G ? sm.theta[col] : 0.f;
+      // route one step whose scores are sc
+      auto route_step = [&](const StepVals& b, int st, const float (&sc)[4]) {
+        float alpha = 1.f;
+        const float smax = rowmax4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        if (smax > Mw) {
+          alpha = __expf(Mw - smax);  // 0 on the first raise from -inf
+          Mw = smax;
+          nlow = nseq;
+        }
+        const float th = rowmax ? Mw - p.tau : thg;
+        uint32_t bits = 0u;
+        float w[4], wsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * st + 4 * kq + e;
+          const bool valid = gval && j < Nk;
+          const bool sink = (unsigned)(j - p.sink_lo) < (unsigned)(p.sink_hi - p.sink_lo);
+          const bool keep = valid && (sc[e] >= th || sink);
+          w[e] = corr && valid && !keep ? (float)min(kBlk, N - j * kBlk) * __expf(sc[e] - Mw) : 0.f;
+          wsum += w[e];
+          bits |= (keep ? 1u : 0u) << (4 * kq + e);
+        }
+        cdl = cdl * alpha + wsum;
+        bits = or4(bits);
+        if (lane < G && gval) kb16[col * 2 * KW + st] = (uint16_t)bits;
+        if (corr) accumulate(b, w, alpha);
+        ++nseq;
+      };
+
+      // the wave's steps: the scores of the next step (and the loads of the
+      // one after) are formed at the end of each iteration
+      float sc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      int k = wid;
+      if (k < nst) {
+        load_vals(vv, step_of(k));
+        load_step(b, step_of(k));
+        step_scores(b, step_of(k), sc, step_of(k + 4));
+      }
+      if (rowmax) {
+        // the maximum over the first step of every wave, before any decision
+        const float mx = rowmax4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+        if (lane < 16) sm.wmax[wid][lane] = mx;
+        __syncthreads();
+        Mw = fmaxf(fmaxf(sm.wmax[0][col], sm.wmax[1][col]), fmaxf(sm.wmax[2][col], sm.wmax[3][col]));
+      }
+      // (the values of step k + 4 load a whole iteration ahead of their use)
+      for (; k < nst; k += 4) {
+        StepVals vn;
+        if (k + 4 < nst) load_vals(vn, step_of(k + 4));
+        route_step(vv, step_of(k), sc);
+        if (k + 4 < nst) {
+          step_scores(b, step_of(k + 4), sc, step_of(k + 8));
+          vv = vn;
+        }
+      }
+      if (lane < 16) sm.wfin[wid][lane] = Mw;
+      __syncthreads();  // every wave's maximum is final
+
+      if (rowmax) {
+        // blocks kept against a lower maximum than the row's: the steps this
+        // wave routed before its maximum reached the row's (all of them if it
+        // never did) are routed again against the row's maximum. The scores
+        // come out bit for bit as before, so a block is only ever dropped.
+        const float M = fmaxf(fmaxf(sm.wfin[0][col], sm.wfin[1][col]), fmaxf(sm.wfin[2][col], sm.wfin[3][col]));
+        const int need = gval ? (Mw == M ? nlow : nseq) : 0;
+        const int nneed = (int)wave_max((float)need);
+        const float thM = M - p.tau;
+        for (int i = 0; i < nneed; ++i) {
+          const int st = chunk_at(wid + 4 * i, cs, nst);
+          const uint32_t old = i < need ? kb16[col * 2 * KW + st] : 0u;
+          if (!__ballot(old != 0u)) continue;
+          StepOps b;
+          StepVals vv;
+          load_step(b, st);
+          load_vals(vv, st);
+          float s2[4];
+          step_scores(b, st, s2, stEnd);
+          uint32_t drop = 0u;
+          float w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int bit = 4 * kq + e, j = 16 * st + bit;
+            const bool sink = (unsigned)(j - p.sink_lo) < (unsigned)(p.sink_hi - p.sink_lo);
+            const bool dr = ((old >> bit) & 1u) && !(s2[e] >= thM || sink);
+            w[e] = corr && dr ? (float)min(kBlk, N - j * kBlk) * __expf(s2[e] - Mw) : 0.f;
+            cdl += w[e];
+            drop |= (dr ? 1u : 0u) << bit;
+          }
+          drop = or4(drop);
+          if (lane < G && old != 0u) kb16[col * 2 * KW + st] = (uint16_t)(old & ~drop);
+          if (corr) accumulate(vv, w, 1.f);
+        }
+      }
+    }
+
+    // ---- R4. the waves' partial sums merged; the group's routing is final ----
+    {
+      float cd = cdl;
+      cd += __shfl_xor(cd, 16);
+      cd += __shfl_xor(cd, 32);
+      if (lane < 16) sm.wden[wid][lane] = cd;
+    }
+    __syncthreads();
+    {
+      // the group's maximum M of each block, and this wave's factor e^{Mw - M}
+      // for its partial sums (0 for a wave that saw none of the block's scores)
+      const int gc = col < G ? col : col - G;  // the block of column col (columns < 2G)
+      const float Mg = fmaxf(fmaxf(sm.wfin[0][gc], sm.wfin[1][gc]), fmaxf(sm.wfin[2][gc], sm.wfin[3][gc]));
+      const float Mwc = sm.wfin[wid][gc];
+      const float f = (col < 2 * G && Mwc > -INFINITY) ? __expf(Mwc - Mg) : 0.f;
+      float* partc = reinterpret_cast<float*>(stB);  // [4 waves][G][D]
+#pragma unroll
+      for (int ci = 0; ci < CT; ++ci) {
+        float4 cn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = accv[ci][e] * f;
+          (&cn.x)[e] = x + __shfl_down(x, G, 16);  // high and remainder columns of block col
+        }
+        if (col < G) *reinterpret_cast<float4*>(&partc[(wid * G + col) * D + 16 * ci + 4 * kq]) = cn;
+      }
+      if (tid < G) {
+        const float M = fmaxf(fmaxf(sm.wfin[0][tid], sm.wfin[1][tid]), fmaxf(sm.wfin[2][tid], sm.wfin[3][tid]));
+        float cd = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float mw = sm.wfin[w][tid];
+          cd += mw > -INFINITY ? sm.wden[w][tid] * __expf(mw - M) : 0.f;
+        }
+        sm.M[tid] = M;
+        sm.cden[tid] = corr ? cd : 0.f;
       }
     }
     __syncthreads();
-    const float MA = fmaxf(fmaxf(sm.wred[0][0], sm.wred[0][1]), fmaxf(sm.wred[0][2], sm.wred[0][3]));
-    const float MB = fmaxf(fmaxf(sm.wred[1][0], sm.wred[1][1]), fmaxf(sm.wred[1][2], sm.wred[1][3]));
-
-    // thresholds: the row max minus tau, or the Gaussian-calibrated mean +
-    // beta * std of the row (population statistics over the key blocks; the
-    // row is on chip, so both come exactly from it in two passes)
-    float thA = MA - p.tau, thB = MB - p.tau;
-    if (p.rule == SOL_ROUTE_GAUSS_DIAG) {
-      // mean and (diagonal-estimate) variance of the rows from the pooled-key
-      // statistics of the head: known without the rows themselves
-      float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;
-      if (tid < D) {
-        const rsrc_t rs = make_rsrc(p.kstats + (size_t)bh * 2 * D, 2 * D * 4);
-        const float mu = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, 0, 0));
-        const float var = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (D + tid) * 4, 0, 0));
-        const float x0 = sm.qbar[0][tid], x1 = sm.qbar[1][tid];
-        a0 = x0 * mu;
-        b0 = x0 * x0 * var;
-        a1 = x1 * mu;
-        b1 = x1 * x1 * var;
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int g = idx / D, c = idx % D;
+      const float* partc = reinterpret_cast<const float*>(stB);
+      sm.cnum[g][c] = corr ? (partc[(0 * G + g) * D + c] + partc[(1 * G + g) * D + c]) +
+                                 (partc[(2 * G + g) * D + c] + partc[(3 * G + g) * D + c])
+                           : 0.f;
+    }
+    __syncthreads();
+    if (p.bitmap) {
+      for (int idx = tid; idx < G * p.nwords; idx += kThreads) {
+        const int g = idx / p.nwords, w = idx % p.nwords;
+        if (g0 + g < Nq) p.bitmap[((size_t)bh * Nq + g0 + g) * p.nwords + w] = sm.kbits[g][w];
       }
-      a0 = wave_sum(a0);
-      b0 = wave_sum(b0);
-      a1 = wave_sum(a1);
-      b1 = wave_sum(b1);
-      if (lane == 0) {
-        sm.gred[0][wid] = a0;
-        sm.gred[0][4 + wid] = b0;
-        sm.gred[1][wid] = a1;
-        sm.gred[1][4 + wid] = b1;
-      }
+    }
+    if (p.route_only) {
+      if (p.static_grid) break;
       __syncthreads();
-      const float inv_d = p.proxy_scale * p.proxy_scale;
-      thA = ((sm.gred[0][0] + sm.gred[0][1]) + (sm.gred[0][2] + sm.gred[0][3])) * p.proxy_scale +
-            p.beta * sqrtf(((sm.gred[0][4] + sm.gred[0][5]) + (sm.gred[0][6] + sm.gred[0][7])) * inv_d);
-      thB = ((sm.gred[1][0] + sm.gred[1][1]) + (sm.gred[1][2] + sm.gred[1][3])) * p.proxy_scale +
-            p.beta * sqrtf(((sm.gred[1][4] + sm.gred[1][5]) + (sm.gred[1][6] + sm.gred[1][7])) * inv_d);
-    } else if (p.rule == SOL_ROUTE_GAUSS) {
-      float sA = 0.f, sB = 0.f;
-      for (int j = tid; j < Nk; j += kThreads) {
-        sA += wrow0[j];
-        sB += wrow1[j];
-      }
-      sA = wave_sum(sA);
-      sB = wave_sum(sB);
-      if (lane == 0) {
-        sm.gred[0][wid] = sA;
-        sm.gred[1][wid] = sB;
-      }
+      if (tid == 0) sm.item = item_of(take(ticket()));
       __syncthreads();
-      const float inv_nk = 1.f / (float)Nk;
-      const float muA = ((sm.gred[0][0] + sm.gred[0][1]) + (sm.gred[0][2] + sm.gred[0][3])) * inv_nk;
-      const float muB = ((sm.gred[1][0] + sm.gred[1][1]) + (sm.gred[1][2] + sm.gred[1][3])) * inv_nk;
-      float vA = 0.f, vB = 0.f;
-      for (int j = tid; j < Nk; j += kThreads) {
-        const float a = wrow0[j] - muA, b = wrow1[j] - muB;
-        vA += a * a;
-        vB += b * b;
-      }
-      vA = wave_sum(vA);
-      vB = wave_sum(vB);
-      if (lane == 0) {
-        sm.gred[0][4 + wid] = vA;
-        sm.gred[1][4 + wid] = vB;
-      }
-      __syncthreads();
-      thA = muA + p.beta * sqrtf(((sm.gred[0][4] + sm.gred[0][5]) + (sm.gred[0][6] + sm.gred[0][7])) * inv_nk);
-      thB = muB + p.beta * sqrtf(((sm.gred[1][4] + sm.gred[1][5]) + (sm.gred[1][6] + sm.gred[1][7])) * inv_nk);
+      continue;
     }
 
-    // ---- 3. route both rows; weights for skipped blocks; union kept list ----
-    int nu = 0, nkA = 0, nkB = 0;
-    {
-      float wsA = 0.f, wsB = 0.f;
-      uint32_t* bmA = p.bitmap ? p.bitmap + (size_t)(bh * p.Nq + qA) * p.nwords : nullptr;
-      uint32_t* bmB = (p.bitmap && hasB) ? bmA + p.nwords : nullptr;
+    // ---- the pairs of the group: Q tiles, union list, kept loop, fold ----
+    for (int pr = 0; pr < G / 2; ++pr) {
+      // The lane indices pass through an empty asm statement, so that the
+      // kept loop's per-lane offsets are formed here for every pair instead of
+      // being hoisted out of the item loop and held in registers through the
+      // routing pass.
+      int tid_ = tid;
+      asm volatile("" : "+v"(tid_));
+      const int tid = tid_, lane = tid_ & 63, g16 = lane >> 4, c16 = lane & 15;
+      const int qA = g0 + 2 * pr;
+      if (qA >= Nq) break;
+      const int gA = 2 * pr;
+      const bool hasB = qA + 1 < Nq;
+      const bool lastpair = pr == G / 2 - 1 || qA + 2 >= Nq;
+      const int nA = min(kBlk, N - qA * kBlk);
+      const int nB = hasB ? min(kBlk, N - (qA + 1) * kBlk) : 0;
+      const int nmine = qb ? nB : nA;
+
+      // ---- 1. Q tiles -> LDS -> Q^T operands ----
+      bf16x8 qop[2][NDS];
+      {
+        constexpr int PER = kBlk * CH / kThreads, RSTEP = kThreads / CH;
+        const uint32_t qoff = ((tid / CH) * D + (tid % CH) * 8) * 2;
+        uint4 qr[2][PER];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const int nb = blk ? nB : nA;
+          const rsrc_t r = make_rsrc(p.q + hoff + (size_t)min(qA + blk, Nq - 1) * kBlk * D, (uint32_t)nb * D * 2);
+#pragma unroll
+          for (int u = 0; u < PER; ++u) qr[blk][u] = ld16(r, qoff, u * RSTEP * D * 2);
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          uint16_t* qd = reinterpret_cast<uint16_t*>(blk ? stB : stA) + (tid / CH) * GM::QS + (tid % CH) * 8;
+#pragma unroll
+          for (int u = 0; u < PER; ++u) *reinterpret_cast<uint4*>(qd + u * RSTEP * GM::QS) = qr[blk][u];
+        }
+        __syncthreads();
+        const uint16_t* qs = reinterpret_cast<const uint16_t*>(qb ? stB : stA) + (qrow0 + c16) * GM::QS + 8 * g16;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int ds = 0; ds < NDS; ++ds)
+            qop[qt][ds] = as_bf16x8(*reinterpret_cast<const uint4*>(&qs[16 * qt * GM::QS + 32 * ds]));
+      }
+
+      // ---- 2. union of the two kept lists, from the kept bits ----
+      int nu = 0, nkA = 0, nkB = 0;
       for (int j0 = 0; j0 < Nk; j0 += kThreads) {
         const int j = j0 + tid;
         bool kA = false, kB = false;
         if (j < Nk) {
-          const float nj = (float)min(kBlk, N - j * kBlk);
-          const float sa = wrow0[j];
-          const bool sink = (unsigned)(j - p.sink_lo) < (unsigned)(p.sink_hi - p.sink_lo);
-          kA = sa >= thA || sink;
-          const float wa = kA ? 0.f : nj * expf(sa - MA);
-          wrow0[j] = wa;
-          wsA += wa;
-          float wb = 0.f;
-          if (hasB) {
-            const float sb = wrow1[j];
-            kB = sb >= thB || sink;
-            wb = kB ? 0.f : nj * expf(sb - MB);
-            wsB += wb;
-          }
-          wrow1[j] = wb;
+          kA = (sm.kbits[gA][j >> 5] >> (j & 31)) & 1u;
+          kB = hasB && ((sm.kbits[gA + 1][j >> 5] >> (j & 31)) & 1u);
         }
         const unsigned long long bA = __ballot(kA), bB = __ballot(kB), bU = bA | bB;
         if (lane == 0) {
           sm.cnt[0][wid] = __popcll(bU);
           sm.cnt[1][wid] = __popcll(bA);
           sm.cnt[2][wid] = __popcll(bB);
-          const int w0 = (j0 + 64 * wid) >> 5;
-          if (w0 < kMaxKeyWords) {
-            sm.kbits[0][w0] = (uint32_t)bA;
-            sm.kbits[1][w0] = (uint32_t)bB;
-          }
-          if (w0 + 1 < kMaxKeyWords) {
-            sm.kbits[0][w0 + 1] = (uint32_t)(bA >> 32);
-            sm.kbits[1][w0 + 1] = (uint32_t)(bB >> 32);
-          }
-          if (bmA) {
-            if (w0 < p.nwords) bmA[w0] = (uint32_t)bA;
-            if (w0 + 1 < p.nwords) bmA[w0 + 1] = (uint32_t)(bA >> 32);
-          }
-          if (bmB) {
-            if (w0 < p.nwords) bmB[w0] = (uint32_t)bB;
-            if (w0 + 1 < p.nwords) bmB[w0 + 1] = (uint32_t)(bB >> 32);
-          }
         }
         if (j == Nk - 1) {
           sm.lastkept[0] = kA;
           sm.lastkept[1] = kB;
         }
-        __syncthreads();
+        __syncthreads();  // (also: every wave holds its Q operands; the stages are free)
         int off = nu;
         for (int w2 = 0; w2 < wid; ++w2) off += sm.cnt[0][w2];
         if (kA || kB)
@@ -495,389 +823,321 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         nkB += sm.cnt[2][0] + sm.cnt[2][1] + sm.cnt[2][2] + sm.cnt[2][3];
         __syncthreads();
       }
-      wsA = wave_sum(wsA);
-      wsB = wave_sum(wsB);
-      if (lane == 0) {
-        sm.wred[0][4 + wid] = wsA;
-        sm.wred[1][4 + wid] = wsB;
+
+      // ---- 3. exact attention over the union list (online softmax, base 2) ----
+      f32x4 accO[2][NDT];
+      f32x4 lsum[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) accO[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-
-    // ---- 4. correction numerators cnum[b][c] = sum_j w_bj vbar_j[c] ----
-    {
-      constexpr int C4 = D / 4, JG = kThreads / C4, U = 8;  // 2 x 32 KiB of pooled values in flight
-      const int c4 = tid % C4, jg = tid / C4;
-      float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-      if (!RC && !p.exact_only && (nkA < Nk || (hasB && nkB < Nk))) {
-        const rsrc_t rv = make_rsrc(p.vmean + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
-        const uint32_t voff = (jg * U * D + c4 * 4) * 4;
-        // two batches of U pooled values per lane (lane group jg takes U
-        // consecutive key blocks of each batch): one in flight while the
-        // other is used (loads past Nk read zero and are never used)
-        auto load = [&](float4 (&x)[U], int j0) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) x[u] = ld16f(rv, voff, (uint32_t)(j0 + u) * D * 4);
+      float m[2] = {-INFINITY, -INFINITY};
+      {
+        const bf16x8 ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+        const uint16_t* kh = p.k + hoff;
+        const uint16_t* vh = p.v + hoff;
+        const int ownbit = 1 << (14 + qb);
+        // K and V tiles of kept key block ulist[t] into one stage
+        auto dma = [&](unsigned char* stage, int t) {
+          const int j = ulist[t] & 0x3fff;
+          const uint32_t bytes = (uint32_t)min(kBlk, N - j * kBlk) * D * 2;
+          dma_tile<D>(stage, make_rsrc(kh + (size_t)j * kBlk * D, bytes), make_rsrc(vh + (size_t)j * kBlk * D, bytes),
+                      wid, lane);
         };
-        // all weights of a batch are read before any is used, with no branch
-        // in between (four 16-byte LDS reads), so their round trips overlap
-        // (blocks past Nk get weight 0; their pooled values read as zero)
-        auto use = [&](const float4 (&x)[U], int j0) {
-          const int jb = j0 + jg * U;  // (reads up to Nk rounded to 64 stay in the stage)
-          float w0[U], w1[U];
-#pragma unroll
-          for (int u = 0; u < U; u += 4) {
-            const float4 a = *reinterpret_cast<const float4*>(&wrow0[jb + u]);
-            const float4 b = *reinterpret_cast<const float4*>(&wrow1[jb + u]);
-            w0[u] = a.x; w0[u + 1] = a.y; w0[u + 2] = a.z; w0[u + 3] = a.w;
-            w1[u] = b.x; w1[u + 1] = b.y; w1[u + 2] = b.z; w1[u + 3] = b.w;
-          }
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            w0[u] = jb + u < Nk ? w0[u] : 0.f;
-            w1[u] = jb + u < Nk ? w1[u] : 0.f;
-          }
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            a0.x += w0[u] * x[u].x; a0.y += w0[u] * x[u].y; a0.z += w0[u] * x[u].z; a0.w += w0[u] * x[u].w;
-            a1.x += w1[u] * x[u].x; a1.y += w1[u] * x[u].y; a1.z += w1[u] * x[u].z; a1.w += w1[u] * x[u].w;
-          }
+        // pooled tile c (per-row correction): the two bf16 parts of the pooled
+        // keys fill stage A (both as K rows), the pooled values stage B's V half
+        auto dma_pooled = [&](int c) {
+          // (the tiled key planes hold zeros past Nk; the row-major values are bounded)
+          const size_t toff = ((size_t)bh * p.Nkp + (size_t)c * kBlk) * D;
+          dma_one<D, true, true>(stA, make_rsrc(p.khi16 + toff, GM::TILE), wid, lane);
+          dma_one<D, true, true>(stA + GM::TILE, make_rsrc(p.klo16 + toff, GM::TILE), wid, lane);
+          const uint32_t bytes = (uint32_t)min(kBlk, Nk - c * kBlk) * D * 2;
+          const size_t off = ((size_t)bh * Nk + (size_t)c * kBlk) * D;
+          dma_one<D, false>(stB + GM::TILE, make_rsrc(p.vbar16 + off, bytes), wid, lane);
         };
-        float4 x0[U], x1[U];
-        load(x0, 0);
-        for (int j0 = 0; j0 < Nk; j0 += 2 * U * JG) {
-          load(x1, j0 + U * JG);
-          use(x0, j0);
-          if (j0 + U * JG >= Nk) break;
-          if (j0 + 2 * U * JG < Nk) load(x0, j0 + 2 * U * JG);
-          use(x1, j0 + U * JG);
-        }
-      }
-      __syncthreads();  // weights fully read: their space becomes reduction scratch
-      float* red = reinterpret_cast<float*>(stA);  // [2][JG][D]
-      *reinterpret_cast<float4*>(&red[(0 * JG + jg) * D + 4 * c4]) = a0;
-      *reinterpret_cast<float4*>(&red[(1 * JG + jg) * D + 4 * c4]) = a1;
-      __syncthreads();
-      if (tid < 2 * D) {
-        const int blk = tid / D, col = tid % D;
-        float s = 0.f;
+        // per-lane byte offsets of the swizzled operand reads (independent of the key tile kt)
+        int koffs[NDS];
 #pragma unroll
-        for (int r = 0; r < JG; ++r) s += red[(blk * JG + r) * D + col];
-        sm.cnum[blk][col] = s;
-      }
-      if (tid < 2)
-        sm.cden[tid] = RC ? 0.f : (sm.wred[tid][4] + sm.wred[tid][5]) + (sm.wred[tid][6] + sm.wred[tid][7]);
-      __syncthreads();  // the tile stages are free again
-    }
+        for (int ds = 0; ds < NDS; ++ds) koffs[ds] = c16 * GM::RB + 16 * kslot<D>(c16, 4 * ds + g16);
+        // transposing V reads: this lane addresses row 4g + e (+32ks +16h) and the
+        // 8 bytes of columns 16dt + 4cc .. +3
+        const int ve = (lane >> 2) & 3, vcc = lane & 3, vrow = 4 * g16 + ve;
+        int voffs[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          voffs[dt] = GM::TILE + vrow * GM::RB + 16 * vslot<D>(vrow, 2 * dt + (vcc >> 1)) + 8 * (vcc & 1);
 
-
-    // ---- 5. exact attention over the union list (online softmax, base 2) ----
-    f32x4 acc[2][NDT];
-    f32x4 lsum[2];
+        auto compute = [&](const unsigned char* stage, int e, auto pooled) {
+          constexpr bool kPooled = decltype(pooled)::value;
+          if (!kPooled && !(e & ownbit)) return;  // wave-uniform: this wave's block skips the entry
+          const int j = e & 0x3fff;
+          const int nj = kPooled ? kBlk : min(kBlk, N - j * kBlk);
+          // S^T[kv][q]: 4 key tiles x 2 query tiles; each K operand serves both
+          f32x4 st[2][4];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    float m[2] = {-INFINITY, -INFINITY};
-    {
-      const bf16x8 ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
-      const uint16_t* kh = p.k + hoff;
-      const uint16_t* vh = p.v + hoff;
-      const int ownbit = 1 << (14 + qb);
-      // K and V tiles of kept key block ulist[t] into one stage
-      auto dma = [&](unsigned char* stage, int t) {
-        const int j = ulist[t] & 0x3fff;
-        const uint32_t bytes = (uint32_t)min(kBlk, N - j * kBlk) * D * 2;
-        dma_tile<D>(stage, make_rsrc(kh + (size_t)j * kBlk * D, bytes), make_rsrc(vh + (size_t)j * kBlk * D, bytes),
-                    wid, lane);
-      };
-      // pooled tile c (per-row correction): the two bf16 parts of the pooled
-      // keys fill stage A (both as K rows), the pooled values stage B's V half
-      auto dma_pooled = [&](int c) {
-        const uint32_t bytes = (uint32_t)min(kBlk, Nk - c * kBlk) * D * 2;
-        const size_t off = ((size_t)bh * Nk + (size_t)c * kBlk) * D;
-        dma_one<D, true>(stA, make_rsrc(p.khi16 + off, bytes), wid, lane);
-        dma_one<D, true>(stA + G::TILE, make_rsrc(p.klo16 + off, bytes), wid, lane);
-        dma_one<D, false>(stB + G::TILE, make_rsrc(p.vbar16 + off, bytes), wid, lane);
-      };
-      // per-lane byte offsets of the swizzled operand reads (independent of the key tile kt)
-      int koff[NDS];
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) koff[ds] = c16 * G::RB + 16 * kslot<D>(c16, 4 * ds + g);
-      // transposing V reads: this lane addresses row 4g + e (+32ks +16h) and the
-      // 8 bytes of columns 16dt + 4cc .. +3
-      const int ve = (lane >> 2) & 3, vcc = lane & 3, vrow = 4 * g + ve;
-      int voff[NDT];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        voff[dt] = G::TILE + vrow * G::RB + 16 * vslot<D>(vrow, 2 * dt + (vcc >> 1)) + 8 * (vcc & 1);
-
-      auto compute = [&](const unsigned char* stage, int e, auto pooled) {
-        constexpr bool kPooled = decltype(pooled)::value;
-        if (!kPooled && !(e & ownbit)) return;  // wave-uniform: this wave's block skips the entry
-        const int j = e & 0x3fff;
-        const int nj = kPooled ? kBlk : min(kBlk, N - j * kBlk);
-        // S^T[kv][q]: 4 key tiles x 2 query tiles; each K operand serves both
-        f32x4 st[2][4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          st[0][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          st[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        // K operands four steps ahead of the MFMAs that use them (one step
-        // ahead leaves each MFMA pair waiting on its LDS read)
-        auto kread = [&](int i) {
-          return as_bf16x8(*reinterpret_cast<const uint4*>(stage + 16 * (i / NDS) * G::RB + koff[i % NDS]));
-        };
-        constexpr int KA = 4;
-        bf16x8 kop[4 * NDS];
-#pragma unroll
-        for (int i = 0; i < KA; ++i) kop[i] = kread(i);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-          for (int ds = 0; ds < NDS; ++ds) {
-            const int i = kt * NDS + ds;
-            const bf16x8 a = kop[i];
-            if (i + KA < 4 * NDS) kop[i + KA] = kread(i + KA);
-            __builtin_amdgcn_sched_barrier(0);
-            st[0][kt] = mfma16x16x32(a, qop[0][ds], st[0][kt]);
-            st[1][kt] = mfma16x16x32(a, qop[1][ds], st[1][kt]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kPooled) {  // the remainder part of the pooled keys, one tile further on
-              const bf16x8 b =
-                  as_bf16x8(*reinterpret_cast<const uint4*>(stage + G::TILE + 16 * kt * G::RB + koff[ds]));
-              st[0][kt] = mfma16x16x32(b, qop[0][ds], st[0][kt]);
-              st[1][kt] = mfma16x16x32(b, qop[1][ds], st[1][kt]);
-            }
+          for (int kt = 0; kt < 4; ++kt) {
+            st[0][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            st[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-        }
-        // lane holds S^T[16kt + 4g + i][row c16 of query tile qt]
-        if (kPooled) {
-          // pooled key 64e + 16kt + 4g + i: masked when kept by this wave's
-          // block (it is in the exact branch) or past Nk; otherwise its
-          // weight n_j enters as log2(n_j) on the base-2 logit, added here in
-          // raw dot-product units (n_j = 64 but for the ragged last block)
-          const uint32_t* kb = sm.kbits[qb];
-          const int valid = Nk - e * kBlk;
-          uint64_t off = (uint64_t)kb[2 * e] | ((uint64_t)kb[2 * e + 1] << 32);
-          if (valid < kBlk) off |= ~0ull << valid;
-          off >>= 4 * g;
-          const int last = Nk - 1 - e * kBlk - 4 * g;  // lane position of the last block, if here
+          // K operands four steps ahead of the MFMAs that use them (one step
+          // ahead leaves each MFMA pair waiting on its LDS read)
+          auto kread = [&](int i) {
+            return as_bf16x8(*reinterpret_cast<const uint4*>(stage + 16 * (i / NDS) * GM::RB + koffs[i % NDS]));
+          };
+          constexpr int KA = 4;
+          bf16x8 kop[4 * NDS];
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
+          for (int i = 0; i < KA; ++i) kop[i] = kread(i);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const bool masked = (off >> (16 * kt + i)) & 1ull;
-              const float b = masked ? -INFINITY : 16 * kt + i == last ? pbias_last : pbias;
-              st[0][kt][i] += b;
-              st[1][kt][i] += b;
-            }
-        } else if (nj < kBlk) {
+          for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (16 * kt + 4 * g + i >= nj) {
-                st[0][kt][i] = -INFINITY;
-                st[1][kt][i] = -INFINITY;
+            for (int ds = 0; ds < NDS; ++ds) {
+              const int i = kt * NDS + ds;
+              const bf16x8 a = kop[i];
+              if (i + KA < 4 * NDS) kop[i + KA] = kread(i + KA);
+              __builtin_amdgcn_sched_barrier(0);
+              st[0][kt] = mfma16x16x32(a, qop[0][ds], st[0][kt]);
+              st[1][kt] = mfma16x16x32(a, qop[1][ds], st[1][kt]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (kPooled) {  // the remainder part of the pooled keys, one tile further on
+                const bf16x8 b =
+                    as_bf16x8(*reinterpret_cast<const uint4*>(stage + GM::TILE + 16 * kt * GM::RB + koffs[ds]));
+                st[0][kt] = mfma16x16x32(b, qop[0][ds], st[0][kt]);
+                st[1][kt] = mfma16x16x32(b, qop[1][ds], st[1][kt]);
               }
-        }
-        bool raise = false;
-        float mn[2];
+            }
+          }
+          // lane holds S^T[16kt + 4g + i][row c16 of query tile qt]
+          if (kPooled) {
+            // pooled key 64e + 16kt + 4g + i: masked when kept by this wave's
+            // block (it is in the exact branch) or past Nk; otherwise its
+            // weight n_j enters as log2(n_j) on the base-2 logit, added here in
+            // raw dot-product units (n_j = 64 but for the ragged last block)
+            const uint32_t* kb = sm.kbits[gA + qb];
+            const int valid = Nk - e * kBlk;
+            uint64_t offb = (uint64_t)kb[2 * e] | ((uint64_t)kb[2 * e + 1] << 32);
+            if (valid < kBlk) offb |= ~0ull << valid;
+            offb >>= 4 * g16;
+            const int last = Nk - 1 - e * kBlk - 4 * g16;  // lane position of the last block, if here
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          // two chains of three-input maxima over the lane's 16 scores
-          float b0 = fmaxf(fmaxf(st[qt][0][0], st[qt][0][1]), st[qt][0][2]);
-          float b1 = fmaxf(fmaxf(st[qt][2][0], st[qt][2][1]), st[qt][2][2]);
-          b0 = fmaxf(fmaxf(b0, st[qt][0][3]), st[qt][1][0]);
-          b1 = fmaxf(fmaxf(b1, st[qt][2][3]), st[qt][3][0]);
-          b0 = fmaxf(fmaxf(b0, st[qt][1][1]), st[qt][1][2]);
-          b1 = fmaxf(fmaxf(b1, st[qt][3][1]), st[qt][3][2]);
-          b0 = fmaxf(b0, st[qt][1][3]);
-          b1 = fmaxf(b1, st[qt][3][3]);
-          const float bm = rowmax4(fmaxf(b0, b1)) * csc;
-          mn[qt] = bm > m[qt] + kLazyRescale ? bm : m[qt];
-          raise = raise || (mn[qt] != m[qt]);
-        }
-        if (__ballot(raise)) {  // rare: a row's max rose by more than the lazy margin
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const bool masked = (offb >> (16 * kt + i)) & 1ull;
+                const float b = masked ? -INFINITY : 16 * kt + i == last ? pbias_last : pbias;
+                st[0][kt][i] += b;
+                st[1][kt][i] += b;
+              }
+          } else if (nj < kBlk) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (16 * kt + 4 * g16 + i >= nj) {
+                  st[0][kt][i] = -INFINITY;
+                  st[1][kt][i] = -INFINITY;
+                }
+          }
+          bool raise = false;
+          float mn[2];
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
-            const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn[qt]);
-            lsum[qt] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] *= alpha;
-            m[qt] = mn[qt];
+            // two chains of three-input maxima over the lane's 16 scores
+            float b0 = fmaxf(fmaxf(st[qt][0][0], st[qt][0][1]), st[qt][0][2]);
+            float b1 = fmaxf(fmaxf(st[qt][2][0], st[qt][2][1]), st[qt][2][2]);
+            b0 = fmaxf(fmaxf(b0, st[qt][0][3]), st[qt][1][0]);
+            b1 = fmaxf(fmaxf(b1, st[qt][2][3]), st[qt][3][0]);
+            b0 = fmaxf(fmaxf(b0, st[qt][1][1]), st[qt][1][2]);
+            b1 = fmaxf(fmaxf(b1, st[qt][3][1]), st[qt][3][2]);
+            b0 = fmaxf(b0, st[qt][1][3]);
+            b1 = fmaxf(b1, st[qt][3][3]);
+            const float bm = rowmax4(fmaxf(b0, b1)) * csc;
+            mn[qt] = bm > m[qt] + kLazyRescale ? bm : m[qt];
+            raise = raise || (mn[qt] != m[qt]);
           }
-        }
-        // P^T operand slots 0-3 = keys 32ks+4g+i, slots 4-7 = keys 32ks+16+4g+i
-        bf16x8 pb[2][2];
+          if (__ballot(raise)) {  // rare: a row's max rose by more than the lazy margin
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          const float nm = -m[qt];
+            for (int qt = 0; qt < 2; ++qt) {
+              const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn[qt]);
+              lsum[qt] *= alpha;
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            uint32_t w[4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const f32x4& sv = st[qt][2 * ks + h];
-              w[2 * h + 0] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[0], csc, nm)),
-                                         __builtin_amdgcn_exp2f(fmaf(sv[1], csc, nm)));
-              w[2 * h + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[2], csc, nm)),
-                                         __builtin_amdgcn_exp2f(fmaf(sv[3], csc, nm)));
+              for (int dt = 0; dt < NDT; ++dt) accO[qt][dt] *= alpha;
+              m[qt] = mn[qt];
             }
-            pb[qt][ks] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
           }
-          // row sums of the bf16-rounded probabilities: every output row of
-          // ones x P^T is the sum over the 32 keys of the step
-          lsum[qt] = mfma16x16x32(ones, pb[qt][0], lsum[qt]);
-          lsum[qt] = mfma16x16x32(ones, pb[qt][1], lsum[qt]);
-        }
-        // O^T[d][q] += V^T[d][kv] P^T[kv][q]; the transposing reads of rows
-        // 32ks + 4g + e and 32ks + 16 + 4g + e give exactly the keys of the P^T
-        // slots; each V^T operand serves both query tiles
-        const unsigned char* vstage = kPooled ? stB : stage;
-        // V^T operands of the next 16 rows of d read while this slice's MFMAs run
-        auto vread = [&](int dt, uint2 (&o)[4]) {
+          // P^T operand slots 0-3 = keys 32ks+4g+i, slots 4-7 = keys 32ks+16+4g+i
+          bf16x8 pb[2][2];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            o[2 * ks] = ld_tr(vstage + voff[dt] + 32 * ks * G::RB);
-            o[2 * ks + 1] = ld_tr(vstage + voff[dt] + (32 * ks + 16) * G::RB);
+          for (int qt = 0; qt < 2; ++qt) {
+            const float nm = -m[qt];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              uint32_t w[4];
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const f32x4& sv = st[qt][2 * ks + h];
+                w[2 * h + 0] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[0], csc, nm)),
+                                           __builtin_amdgcn_exp2f(fmaf(sv[1], csc, nm)));
+                w[2 * h + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sv[2], csc, nm)),
+                                           __builtin_amdgcn_exp2f(fmaf(sv[3], csc, nm)));
+              }
+              pb[qt][ks] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+            }
+            // row sums of the bf16-rounded probabilities: every output row of
+            // ones x P^T is the sum over the 32 keys of the step
+            lsum[qt] = mfma16x16x32(ones, pb[qt][0], lsum[qt]);
+            lsum[qt] = mfma16x16x32(ones, pb[qt][1], lsum[qt]);
           }
-        };
-        uint2 vc[4], vn[4];
-        vread(0, vc);
+          // O^T[d][q] += V^T[d][kv] P^T[kv][q]; the transposing reads of rows
+          // 32ks + 4g + e and 32ks + 16 + 4g + e give exactly the keys of the P^T
+          // slots; each V^T operand serves both query tiles
+          const unsigned char* vstage = kPooled ? stB : stage;
+          // V^T operands of the next 16 rows of d read while this slice's MFMAs run
+          auto vread = [&](int dt, uint2 (&o)[4]) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          if (dt + 1 < NDT) vread(dt + 1, vn);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 a = as_bf16x8(make_uint4(vc[2 * ks].x, vc[2 * ks].y, vc[2 * ks + 1].x, vc[2 * ks + 1].y));
-            acc[0][dt] = mfma16x16x32(a, pb[0][ks], acc[0][dt]);
-            acc[1][dt] = mfma16x16x32(a, pb[1][ks], acc[1][dt]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) vc[e2] = vn[e2];
-        }
-      };
-
-      // Every barrier below is preceded by an explicit wait for all of this
-      // wave's outstanding copies: the copy into one stage is issued in one
-      // loop iteration and consumed in the next, a dependency the compiler's
-      // own wait insertion does not carry across the loop back-edge.
-      if (nu > 0) dma(stA, 0);
-      if (nu > 1) dma(stB, 1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();  // tiles 0 and 1 are in LDS
-      for (int t = 0; t < nu; t += 2) {
-        compute(stA, ulist[t], std::false_type{});
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // tile t+1 has landed in stB; nobody reads stA any more
-        if (t + 2 < nu) dma(stA, t + 2);
-        if (t + 1 < nu) {
-          compute(stB, ulist[t + 1], std::false_type{});
-          __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();  // tile t+2 has landed in stA; nobody reads stB any more
-          if (t + 3 < nu) dma(stB, t + 3);
-        }
-      }
-      if (RC) {
-        // pooled tiles, one at a time: each fills stage A and half of stage B
-        const int npool = (Nk + kBlk - 1) / kBlk;
-        for (int c = 0; c < npool; ++c) {
-          // a tile whose key blocks both rows keep holds only masked pooled
-          // keys (all of them, at tau = +inf): skipped, the same decision in
-          // every thread (kept bits in LDS), so the barriers stay matched
-          const int nv = min(kBlk, Nk - c * kBlk);
-          const uint64_t valid = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
-          const uint64_t ka = (uint64_t)sm.kbits[0][2 * c] | ((uint64_t)sm.kbits[0][2 * c + 1] << 32);
-          const uint64_t kb = (uint64_t)sm.kbits[1][2 * c] | ((uint64_t)sm.kbits[1][2 * c + 1] << 32);
-          if ((valid & ~ka) == 0 && (!hasB || (valid & ~kb) == 0)) continue;
-          dma_pooled(c);
-          __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();  // pooled tile c is in LDS
-          compute(stA, c, std::true_type{});
-          __syncthreads();  // nobody reads the pooled tile any more
-        }
-      }
-    }
-
-    // The next ticket is drawn now, so its round trip overlaps the fold
-    // below (it is resolved before this wave's stores); drawing it earlier
-    // would tie an item to this workgroup while it may still spend long on
-    // this one, which others could have taken.
-    unsigned next_ticket = 0;
-    if (tid == 0) next_ticket = ticket();
-
-    // ---- 6. fold exact and corrected terms, normalise, store ----
-    {
-      const float M2 = (qb ? MB : MA) * kLog2e;
-      const float cden = sm.cden[qb];
-      const int rbase = (qA + qb) * kBlk;
-      // with no correction mass (exact-only, the per-row mode, every block
-      // kept, or every skipped weight zero) the exact state alone is
-      // normalised: a common maximum with M2 could underflow it to zero
-      const bool corr = !p.exact_only && cden > 0.f;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float lt = lsum[qt][0];
-        const float mf = corr ? fmaxf(m[qt], M2) : m[qt];
-        const float fa = __builtin_amdgcn_exp2f(m[qt] - mf);
-        const float fc = corr ? __builtin_amdgcn_exp2f(M2 - mf) : 0.f;
-        const float inv = 1.f / (lt * fa + cden * fc);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int c = 16 * dt + 4 * g;
-          acc[qt][dt][0] = (acc[qt][dt][0] * fa + sm.cnum[qb][c + 0] * fc) * inv;
-          acc[qt][dt][1] = (acc[qt][dt][1] * fa + sm.cnum[qb][c + 1] * fc) * inv;
-          acc[qt][dt][2] = (acc[qt][dt][2] * fa + sm.cnum[qb][c + 2] * fc) * inv;
-          acc[qt][dt][3] = (acc[qt][dt][3] * fa + sm.cnum[qb][c + 3] * fc) * inv;
-        }
-      }
-      // the next item, resolved before this wave's stores, so that waiting
-      // for the ticket never waits for them
-      if (tid == 0) sm.item = item_of(take(next_ticket));
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int row = qrow0 + 16 * qt + c16;
-        if (row < nmine) {
-          const size_t orow = hoff + (size_t)(rbase + row) * D;
+            for (int ks = 0; ks < 2; ++ks) {
+              o[2 * ks] = ld_tr(vstage + voffs[dt] + 32 * ks * GM::RB);
+              o[2 * ks + 1] = ld_tr(vstage + voffs[dt] + (32 * ks + 16) * GM::RB);
+            }
+          };
+          uint2 vc[4], vn[4];
+          vread(0, vc);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const int c = 16 * dt + 4 * g;
-            const f32x4 o = acc[qt][dt];
-            if (p.out_bf16)
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + c) =
-                  make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-            else
-              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + c) = make_float4(o[0], o[1], o[2], o[3]);
+            if (dt + 1 < NDT) vread(dt + 1, vn);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const bf16x8 a = as_bf16x8(make_uint4(vc[2 * ks].x, vc[2 * ks].y, vc[2 * ks + 1].x, vc[2 * ks + 1].y));
+              accO[0][dt] = mfma16x16x32(a, pb[0][ks], accO[0][dt]);
+              accO[1][dt] = mfma16x16x32(a, pb[1][ks], accO[1][dt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) vc[e2] = vn[e2];
+          }
+        };
+
+        // Every barrier below is preceded by an explicit wait for all of this
+        // wave's outstanding copies: the copy into one stage is issued in one
+        // loop iteration and consumed in the next, a dependency the compiler's
+        // own wait insertion does not carry across the loop back-edge.
+        if (nu > 0) dma(stA, 0);
+        if (nu > 1) dma(stB, 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // tiles 0 and 1 are in LDS
+        for (int t = 0; t < nu; t += 2) {
+          compute(stA, ulist[t], std::false_type{});
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();  // tile t+1 has landed in stB; nobody reads stA any more
+          if (t + 2 < nu) dma(stA, t + 2);
+          if (t + 1 < nu) {
+            compute(stB, ulist[t + 1], std::false_type{});
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();  // tile t+2 has landed in stA; nobody reads stB any more
+            if (t + 3 < nu) dma(stB, t + 3);
+          }
+        }
+        if (RC) {
+          // pooled tiles, one at a time: each fills stage A and half of stage B
+          const int npool = (Nk + kBlk - 1) / kBlk;
+          for (int c = 0; c < npool; ++c) {
+            // a tile whose key blocks both rows keep holds only masked pooled
+            // keys (all of them, at tau = +inf): skipped, the same decision in
+            // every thread (kept bits in LDS), so the barriers stay matched
+            const int nv = min(kBlk, Nk - c * kBlk);
+            const uint64_t valid = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+            const uint64_t ka = (uint64_t)sm.kbits[gA][2 * c] | ((uint64_t)sm.kbits[gA][2 * c + 1] << 32);
+            const uint64_t kb = hasB ? ((uint64_t)sm.kbits[gA + 1][2 * c] | ((uint64_t)sm.kbits[gA + 1][2 * c + 1] << 32))
+                                     : valid;
+            if ((valid & ~ka) == 0 && (valid & ~kb) == 0) continue;
+            dma_pooled(c);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();  // pooled tile c is in LDS
+            compute(stA, c, std::true_type{});
+            __syncthreads();  // nobody reads the pooled tile any more
           }
         }
       }
-    }
 
-    if (tid == 0) {
-      const unsigned long long tokA = (unsigned long long)nkA * kBlk - (sm.lastkept[0] ? kBlk - nlast : 0);
-      st_pairs += tokA * (unsigned long long)nA;
-      st_kept += nkA;
-      st_tot += Nk;
-      st_min = min(st_min, (unsigned)nkA);
-      st_max = max(st_max, (unsigned)nkA);
-      if (hasB) {
-        const unsigned long long tokB = (unsigned long long)nkB * kBlk - (sm.lastkept[1] ? kBlk - nlast : 0);
-        st_pairs += tokB * (unsigned long long)nB;
-        st_kept += nkB;
-        st_tot += Nk;
-        st_min = min(st_min, (unsigned)nkB);
-        st_max = max(st_max, (unsigned)nkB);
+      // After the group's last pair the next ticket is drawn, so its round
+      // trip overlaps the fold below (it is resolved before this wave's
+      // stores); drawing it earlier would tie an item to this workgroup while
+      // it may still spend long on this one, which others could have taken.
+      unsigned next_ticket = 0;
+      if (lastpair && tid == 0 && !p.static_grid) next_ticket = ticket();
+
+      // ---- 4. fold exact and corrected terms, normalise, store ----
+      {
+        const int gm = gA + qb;
+        const float M2 = sm.M[gm] * kLog2e;
+        const float cden = sm.cden[gm];
+        const int rbase = (qA + qb) * kBlk;
+        // with no correction mass (exact-only, the per-row mode, every block
+        // kept, or every skipped weight zero) the exact state alone is
+        // normalised: a common maximum with M2 could underflow it to zero
+        const bool cm = corr && cden > 0.f;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const float lt = lsum[qt][0];
+          const float mf = cm ? fmaxf(m[qt], M2) : m[qt];
+          const float fa = __builtin_amdgcn_exp2f(m[qt] - mf);
+          const float fc = cm ? __builtin_amdgcn_exp2f(M2 - mf) : 0.f;
+          const float inv = 1.f / (lt * fa + cden * fc);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const int c = 16 * dt + 4 * g16;
+            accO[qt][dt][0] = (accO[qt][dt][0] * fa + sm.cnum[gm][c + 0] * fc) * inv;
+            accO[qt][dt][1] = (accO[qt][dt][1] * fa + sm.cnum[gm][c + 1] * fc) * inv;
+            accO[qt][dt][2] = (accO[qt][dt][2] * fa + sm.cnum[gm][c + 2] * fc) * inv;
+            accO[qt][dt][3] = (accO[qt][dt][3] * fa + sm.cnum[gm][c + 3] * fc) * inv;
+          }
+        }
+        // the next item, resolved before this wave's stores, so that waiting
+        // for the ticket never waits for them
+        if (lastpair && tid == 0) sm.item = p.static_grid ? -1 : item_of(take(next_ticket));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const int row = qrow0 + 16 * qt + c16;
+          if (row < nmine) {
+            const size_t orow = hoff + (size_t)(rbase + row) * D;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const int c = 16 * dt + 4 * g16;
+              const f32x4 o = accO[qt][dt];
+              if (p.out_bf16)
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow + c) =
+                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+              else
+                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow + c) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+          }
+        }
       }
+
+      if (tid == 0) {
+        const unsigned long long tokA = (unsigned long long)nkA * kBlk - (sm.lastkept[0] ? kBlk - nlast : 0);
+        st_pairs += tokA * (unsigned long long)nA;
+        st_kept += nkA;
+        st_tot += Nk;
+        st_min = min(st_min, (unsigned)nkA);
+        st_max = max(st_max, (unsigned)nkA);
+        if (hasB) {
+          const unsigned long long tokB = (unsigned long long)nkB * kBlk - (sm.lastkept[1] ? kBlk - nlast : 0);
+          st_pairs += tokB * (unsigned long long)nB;
+          st_kept += nkB;
+          st_tot += Nk;
+          st_min = min(st_min, (unsigned)nkB);
+          st_max = max(st_max, (unsigned)nkB);
+        }
+      }
+      lds_barrier();  // LDS is rewritten by the next pair or item (output stores may still be in flight)
     }
-    lds_barrier();  // the next item is in sm.item; LDS is rewritten by it (output stores may still be in flight)
   }
+  if (p.static_grid) return;
 
   // Each workgroup adds its stats once; the last one to finish publishes
   // them and leaves the header clean (zero tickets, zero counters) for the
@@ -915,15 +1175,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 
 size_t forward_dynamic_lds(int Nk) { return ((size_t)Nk * 2 + 15) & ~(size_t)15; }
 
-int forward_items(int BH, int Nq) { return BH * ((Nq + 1) / 2); }
+int forward_items(int BH, int Nq, int G) { return BH * ((Nq + G - 1) / G); }
 
-int forward_max_blocks(int d) {
-  // each fp32 routing row lives in one stage before the kept loop
-  return d == 128 ? Geom<128>::STAGE / 4 : Geom<64>::STAGE / 4;
-}
+int forward_max_group(int Nk) { return Nk <= kMaxKeyBlocksG8 ? 8 : 4; }
 
-template <int D, bool RC>
-static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+template <int D, int G, bool RC>
+static hipError_t launch_dg(const FwdParams& p, hipStream_t stream) {
   // per-device CU count and occupancy (bucketed by dynamic LDS in 4 KiB steps)
   static std::mutex mu;
   static int cus[64] = {0};
@@ -941,14 +1198,14 @@ static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
       int n = 0;
       e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<D, RC>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<D, G, RC>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 32 * 1024);
       if (e != hipSuccess) return e;
       cus[dev] = n;
     }
     if (occ_cache[dev][bucket] == 0) {
       int occ = 0;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&fwd_kernel<D, RC>),
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&fwd_kernel<D, G, RC>),
                                                        kThreads, (size_t)(bucket + 1) * 4096);
       if (e != hipSuccess) return e;
       occ_cache[dev][bucket] = occ < 1 ? 1 : occ;
@@ -956,9 +1213,18 @@ static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     ncu = cus[dev];
     grid_per_cu = occ_cache[dev][bucket];
   }
-  const int grid = (int)std::min<long long>((long long)ncu * grid_per_cu, p.nitems);
-  hipLaunchKernelGGL((fwd_kernel<D, RC>), dim3(grid), dim3(kThreads), dyn, stream, p);
+  const int grid = p.static_grid ? p.nitems : (int)std::min<long long>((long long)ncu * grid_per_cu, p.nitems);
+  hipLaunchKernelGGL((fwd_kernel<D, G, RC>), dim3(grid), dim3(kThreads), dyn, stream, p);
   return hipGetLastError();
+}
+
+template <int D, bool RC>
+static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+  switch (p.group) {
+    case 8: return launch_dg<D, 8, RC>(p, stream);
+    case 4: return launch_dg<D, 4, RC>(p, stream);
+    default: return launch_dg<D, 2, RC>(p, stream);
+  }
 }
 
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t stream) {

@@ -30,6 +30,10 @@ __host__ __device__ inline int queue_begin(int x, int nitems) {
   return (int)(((long long)x * nitems) / kQueues);
 }
 
+// Longest head (in key blocks) that a work item of eight query blocks
+// supports: its kept bits and kept list must fit the workgroup's LDS.
+constexpr int kMaxKeyBlocksG8 = 2048;
+
 struct FwdParams {
   const uint16_t* q;     // bf16 [BH][N][d]
   const uint16_t* k;     // bf16 [BH][N][d]
@@ -41,7 +45,11 @@ struct FwdParams {
   unsigned* hdr;         // workspace header (kHdr*), clean on entry
   sol_attn_stats* stats; // nullable, written by the last workgroup
   uint32_t* bitmap;      // nullable, [BH][Nq][nwords]
-  int N, Nq, Nk, nitems, nwords;  // nitems = forward_items(BH, Nq)
+  int N, Nq, Nk, nitems, nwords;  // nitems = forward_items(BH, Nq, group)
+  int group;             // query blocks per work item: 2, 4 or 8
+  int ngroups;           // work items per head, ceil(Nq / group)
+  int route_only;        // stop after routing (the kept-block bitmap is the only output)
+  int static_grid;       // one workgroup per item, no queues, no header, no stats (route_only)
   int rule;              // SOL_ROUTE_ROWMAX or SOL_ROUTE_GAUSS
   float tau;             // ROWMAX: >= 0, may be +inf
   float beta;            // GAUSS: standardized cutoff, finite
@@ -51,10 +59,14 @@ struct FwdParams {
   int exact_only;        // skipped blocks dropped instead of corrected
   int row_corr;          // per-row (token-to-block) correction over the pooled tiles below
   int out_bf16;          // store the output rounded to bf16
-  const uint16_t* khi16;   // bf16 [BH][Nk][d] pooled keys, high part (row_corr)
-  const uint16_t* klo16;   // bf16 [BH][Nk][d] pooled keys, the remainder (row_corr)
+  const uint16_t* khi16;   // bf16 pooled keys, first part, tiled (launch_prep kh)
+  const uint16_t* klo16;   // bf16 pooled keys, second part, tiled (launch_prep km)
+  const uint16_t* klo2;    // bf16 pooled keys, third part, tiled (launch_prep kl)
+  const uint16_t* vt;      // bf16 pooled values, tiled (launch_prep vt)
+  int Nkp;                 // key blocks per head in the tiled planes: Nk rounded up to 256
   const uint16_t* vbar16;  // bf16 [BH][Nk][d] pooled values (row_corr)
   const float* kstats;     // fp32 [BH][2][d]: mean and variance of the pooled keys (GAUSS_DIAG)
+  const float* kmom;       // fp32 [BH][d + 1][d]: mean, then covariance rows of the pooled keys (GAUSS)
 };
 
 // Up to three bf16 [BH][N][d] tensors pooled per 64-token block into fp32
@@ -69,14 +81,22 @@ struct PoolSet {
 // workspace header words.
 hipError_t launch_pool(const PoolSet& set, int BH, int N, int Nk, int d, unsigned* hdr, hipStream_t stream);
 
-// a = a_hi + a_lo in two bf16 parts (each rounded to nearest even; the pair
-// carries about 16 significant bits) and b16 = bf16(b), for n values each.
-hipError_t launch_to_bf16(const float* a, uint16_t* a_hi, uint16_t* a_lo, const float* b, uint16_t* b16, size_t n,
-                          hipStream_t stream);
+// Routing operand planes from the fp32 pooled keys and values (pool.hip):
+// kh + km + kl = kpool in three bf16 parts and vt = bf16(vmean), each
+// [BH][Nkp][d] in 16-block operand tiles (key blocks from Nk to Nkp, a
+// multiple of 64, zero); vrow = bf16(vmean) [BH][Nk][d] row-major when not
+// null; with vt null only the key planes are written.
+hipError_t launch_prep(const float* kpool, const float* vmean, uint16_t* kh, uint16_t* km, uint16_t* kl,
+                       uint16_t* vt, uint16_t* vrow, int BH, int Nk, int Nkp, int d, hipStream_t stream);
 
 // stats[bh][0][c] = mean_j kpool[bh][j][c], stats[bh][1][c] = population
 // variance over j (two passes), one workgroup per head.
 hipError_t launch_kstats(const float* kpool, float* stats, int BH, int Nk, int d, hipStream_t stream);
+
+// mom[bh][0][c] = m_c = mean_j kpool[bh][j][c]; mom[bh][1 + a][b] = population
+// covariance mean_j (kpool[j][a] - m_a)(kpool[j][b] - m_b) (mean first, then
+// the centred products).
+hipError_t launch_kmom(const float* kpool, float* mom, int BH, int Nk, int d, hipStream_t stream);
 
 // Resets the workspace header words (one small kernel).
 hipError_t launch_reset(unsigned* hdr, hipStream_t stream);
@@ -94,18 +114,7 @@ hipError_t launch_identity_order(unsigned* perm, int nitems, hipStream_t stream)
 // The fused routing + exact + correction kernel (persistent grid).
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t stream);
 
-// The mask builders (masks.hip).
-struct MaskParams {
-  const uint16_t* q;     // bf16 [BH][N][d]
-  const float* kpool;    // fp32 [BH][Nk][d]
-  uint32_t* bitmap;      // [BH][Nq][nwords]
-  int N, Nq, Nk, nwords;
-  int rule;              // SOL_ROUTE_*
-  float tau, beta, proxy_scale;
-  int sink_lo, sink_hi;
-};
-// On-chip threshold routing, one workgroup per pair of query blocks.
-hipError_t launch_mask_threshold(const MaskParams& p, int d, int BH, hipStream_t stream);
+// The top-k / top-p mask builders (masks.hip).
 // map[bh][i][j] = qpool_i . kpool_j * scale (fp32, written to device memory).
 hipError_t launch_proxy_map(const float* qpool, const float* kpool, float* map, int BH, int Nq, int Nk, int d,
                             float scale, hipStream_t stream);
@@ -116,10 +125,10 @@ hipError_t launch_sort_mask(const float* map, uint32_t* bitmap, int BH, int Nq, 
 // Dynamic LDS bytes the fused kernel needs for the kept list of Nk blocks.
 size_t forward_dynamic_lds(int Nk);
 
-// Number of work items (pairs of query blocks) of the fused kernel.
-int forward_items(int BH, int Nq);
+// Number of work items (groups of `group` query blocks) of the fused kernel.
+int forward_items(int BH, int Nq, int group);
 
-// Largest Nk whose two fp32 routing rows fit the kernel's LDS tile buffer.
-int forward_max_blocks(int d);
+// Largest group size the fused kernel supports for Nk key blocks.
+int forward_max_group(int Nk);
 
 }  // namespace sol

@@ -6,8 +6,9 @@
 // §4 "Efficient On-the-Fly Sparsification": threshold routing consumes the
 // scores on chip instead of materialising and traversing the proxy map).
 //
-// The threshold router keeps each proxy row in LDS and writes only the
-// kept-block bitmap. The top-k / top-p routers first write the full proxy map
+// The threshold router is the fused forward kernel stopped after its routing
+// (api.hip): it consumes the scores on chip and writes only the kept-block
+// bitmap. The top-k / top-p routers here first write the full proxy map
 // (fp32 [BH][Nq][Nk]) to device memory, then read it back one row per
 // workgroup, sort the row, and write the bitmap. All three produce the same
 // bitmap layout as sol_attn_forward_debug.
@@ -22,169 +23,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxMaskWords = (SOL_ATTN_MAX_N / kBlk + 31) / 32;  // bitmap words of the longest row
-
-// ---------------------------------------------------------------------------
-// threshold router: one workgroup per pair of query blocks
-// ---------------------------------------------------------------------------
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void mask_threshold_kernel(MaskParams p) {
-  constexpr int CH = D / 8;  // 16-byte chunks per row
-  constexpr int PER = kBlk * CH / kThreads, RSTEP = kThreads / CH;
-  __shared__ float part[4][2][D];
-  __shared__ float qbar[2][D];
-  __shared__ float red[4][2][4];
-  extern __shared__ __align__(16) unsigned char dyn[];
-  float* row0 = reinterpret_cast<float*>(dyn);  // [Nk] scores of block A
-  float* row1 = row0 + p.Nk;                   // [Nk] scores of block B
-
-  const int Nk = p.Nk, N = p.N;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int bh = blockIdx.y, qA = 2 * blockIdx.x;
-  const bool hasB = qA + 1 < p.Nq;
-  const int nA = min(kBlk, N - qA * kBlk), nB = hasB ? min(kBlk, N - (qA + 1) * kBlk) : 0;
-
-  // pooled queries of both blocks, summed from the loaded rows
-  {
-    const uint32_t qoff = ((tid / CH) * D + (tid % CH) * 8) * 2;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int nb = blk ? nB : nA;
-      const rsrc_t r = make_rsrc(p.q + ((size_t)bh * N + (size_t)(qA + blk) * kBlk) * D, (uint32_t)nb * D * 2);
-      uint4 u[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) u[i] = ld16(r, qoff, i * RSTEP * D * 2);
-      float cs[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) cs[e] = 0.f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        cs[0] += bf16lo(u[i].x); cs[1] += bf16hi(u[i].x); cs[2] += bf16lo(u[i].y); cs[3] += bf16hi(u[i].y);
-        cs[4] += bf16lo(u[i].z); cs[5] += bf16hi(u[i].z); cs[6] += bf16lo(u[i].w); cs[7] += bf16hi(u[i].w);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) cs[e] = colsum_rows<CH>(cs[e]);
-      if (lane < CH) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part[wid][blk][lane * 8 + e] = cs[e];
-      }
-    }
-    __syncthreads();
-    if (tid < 2 * D) {
-      const int blk = tid / D, col = tid % D, nb = blk ? nB : nA;
-      const float s = (part[0][blk][col] + part[1][blk][col]) + (part[2][blk][col] + part[3][blk][col]);
-      qbar[blk][col] = nb > 0 ? s / (float)nb : 0.f;
-    }
-    __syncthreads();
-  }
-
-  // both proxy rows into LDS, eight lanes per pooled key
-  float mA = -INFINITY, mB = -INFINITY;
-  {
-    constexpr int NV = D / 32, U = 4, JS = kThreads / 8;
-    const int sub = tid & 7, jg = tid >> 3;
-    float4 qa[NV], qb[NV];
-#pragma unroll
-    for (int t = 0; t < NV; ++t) {
-      qa[t] = *reinterpret_cast<const float4*>(&qbar[0][4 * (sub + 8 * t)]);
-      qb[t] = *reinterpret_cast<const float4*>(&qbar[1][4 * (sub + 8 * t)]);
-    }
-    const rsrc_t rk = make_rsrc(p.kpool + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
-    const uint32_t voff = (jg * D + sub * 4) * 4;
-    for (int j0 = 0; j0 < Nk; j0 += U * JS) {
-      float4 x[U][NV];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int t = 0; t < NV; ++t) x[u][t] = ld16f(rk, voff + t * 128, (uint32_t)(j0 + u * JS) * D * 4);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * JS + jg;
-        float a = 0.f, b = 0.f;
-#pragma unroll
-        for (int t = 0; t < NV; ++t) {
-          a += qa[t].x * x[u][t].x + qa[t].y * x[u][t].y + qa[t].z * x[u][t].z + qa[t].w * x[u][t].w;
-          b += qb[t].x * x[u][t].x + qb[t].y * x[u][t].y + qb[t].z * x[u][t].z + qb[t].w * x[u][t].w;
-        }
-        a = sum8(a) * p.proxy_scale;
-        b = sum8(b) * p.proxy_scale;
-        if (j < Nk) {
-          if (sub == 0) {
-            row0[j] = a;
-            row1[j] = b;
-          }
-          mA = fmaxf(mA, a);
-          mB = fmaxf(mB, b);
-        }
-      }
-    }
-    mA = wave_max(mA);
-    mB = wave_max(mB);
-    if (lane == 0) {
-      red[wid][0][0] = mA;
-      red[wid][1][0] = mB;
-    }
-  }
-  __syncthreads();
-  mA = fmaxf(fmaxf(red[0][0][0], red[1][0][0]), fmaxf(red[2][0][0], red[3][0][0]));
-  mB = fmaxf(fmaxf(red[0][1][0], red[1][1][0]), fmaxf(red[2][1][0], red[3][1][0]));
-
-  float thA = mA - p.tau, thB = mB - p.tau;
-  if (p.rule == SOL_ROUTE_GAUSS) {
-    const float inv_nk = 1.f / (float)Nk;
-    float sA = 0.f, sB = 0.f;
-    for (int j = tid; j < Nk; j += kThreads) {
-      sA += row0[j];
-      sB += row1[j];
-    }
-    sA = wave_sum(sA);
-    sB = wave_sum(sB);
-    if (lane == 0) {
-      red[wid][0][1] = sA;
-      red[wid][1][1] = sB;
-    }
-    __syncthreads();
-    const float muA = ((red[0][0][1] + red[1][0][1]) + (red[2][0][1] + red[3][0][1])) * inv_nk;
-    const float muB = ((red[0][1][1] + red[1][1][1]) + (red[2][1][1] + red[3][1][1])) * inv_nk;
-    float vA = 0.f, vB = 0.f;
-    for (int j = tid; j < Nk; j += kThreads) {
-      const float a = row0[j] - muA, b = row1[j] - muB;
-      vA += a * a;
-      vB += b * b;
-    }
-    vA = wave_sum(vA);
-    vB = wave_sum(vB);
-    if (lane == 0) {
-      red[wid][0][2] = vA;
-      red[wid][1][2] = vB;
-    }
-    __syncthreads();
-    thA = muA + p.beta * sqrtf(((red[0][0][2] + red[1][0][2]) + (red[2][0][2] + red[3][0][2])) * inv_nk);
-    thB = muB + p.beta * sqrtf(((red[0][1][2] + red[1][1][2]) + (red[2][1][2] + red[3][1][2])) * inv_nk);
-  }
-
-  uint32_t* bmA = p.bitmap + ((size_t)bh * p.Nq + qA) * p.nwords;
-  uint32_t* bmB = bmA + p.nwords;
-  for (int j0 = 0; j0 < Nk; j0 += kThreads) {
-    const int j = j0 + tid;
-    bool kA = false, kB = false;
-    if (j < Nk) {
-      const bool sink = (unsigned)(j - p.sink_lo) < (unsigned)(p.sink_hi - p.sink_lo);
-      kA = row0[j] >= thA || sink;
-      kB = hasB && (row1[j] >= thB || sink);
-    }
-    const unsigned long long bA = __ballot(kA), bB = __ballot(kB);
-    const int w0 = (j0 + 64 * wid) >> 5;
-    if (lane == 0 && w0 < p.nwords) {
-      bmA[w0] = (uint32_t)bA;
-      if (hasB) bmB[w0] = (uint32_t)bB;
-    }
-    if (lane == 32 && w0 + 1 < p.nwords) {
-      bmA[w0 + 1] = (uint32_t)(bA >> 32);
-      if (hasB) bmB[w0 + 1] = (uint32_t)(bB >> 32);
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // top-k / top-p routers: the proxy map in device memory, then a sort per row
@@ -348,16 +186,6 @@ __global__ __launch_bounds__(kThreads) void sort_mask_kernel(const float* __rest
 }
 
 }  // namespace
-
-hipError_t launch_mask_threshold(const MaskParams& p, int d, int BH, hipStream_t stream) {
-  const dim3 grid((p.Nq + 1) / 2, BH);
-  const size_t dyn = (size_t)2 * p.Nk * sizeof(float);
-  if (d == 128)
-    hipLaunchKernelGGL(mask_threshold_kernel<128>, grid, dim3(kThreads), dyn, stream, p);
-  else
-    hipLaunchKernelGGL(mask_threshold_kernel<64>, grid, dim3(kThreads), dyn, stream, p);
-  return hipGetLastError();
-}
 
 hipError_t launch_proxy_map(const float* qpool, const float* kpool, float* map, int BH, int Nq, int Nk, int d,
                             float scale, hipStream_t stream) {

@@ -296,7 +296,7 @@ hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, un
                        proxy_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nitems = forward_items(BH, Nq);
+  const int nitems = forward_items(BH, Nq, 2);  // the plan orders items of two query blocks
   hipLaunchKernelGGL(order_kernel, dim3(kQueues), dim3(1024), (size_t)(Nk + 1) * sizeof(unsigned), stream, cost,
                      perm, nitems, Nk);
   return hipGetLastError();

@@ -88,8 +88,22 @@ enum {
   SOL_F_ROW_CORRECTION = 1u << 3,
   /* `out` is bf16 [B][H][N][d] instead of fp32: the same fp32 result, rounded
    * to nearest even as it is stored (half the output bytes). */
-  SOL_F_OUT_BF16 = 1u << 4
+  SOL_F_OUT_BF16 = 1u << 4,
+  /* Bits 5-6: query blocks per work item of the fused kernel; the group's
+   * routing pass reads the head's pooled keys and values once for all of
+   * them. 0 (the default): chosen by the library (8 when the call has at
+   * least 16 such items per CU and at most 2048 key blocks, else 4 under the
+   * same item rule, else 2). SOL_F_GROUP2 / 4 / 8 ask for a size; 8 needs
+   * ceil(N/64) <= 2048 (SOL_EUNSUPPORTED otherwise) and none combines with
+   * SOL_F_PLANNED (SOL_EINVAL). The size only schedules work: results agree
+   * within floating-point rounding (sums are taken in another order), and
+   * are bitwise reproducible for a given size. */
+  SOL_F_GROUP2 = 1u << 5,
+  SOL_F_GROUP4 = 2u << 5,
+  SOL_F_GROUP8 = 3u << 5
 };
+#define SOL_F_GROUP_SHIFT 5
+#define SOL_F_GROUP_MASK (3u << SOL_F_GROUP_SHIFT)
 
 /* Routing rules of sol_attn_forward_ex (§3 "Dynamic threshold routing":
  * a query-dependent threshold on the block proxy scores s_ij). */
@@ -98,9 +112,12 @@ enum {
   SOL_ROUTE_ROWMAX = 0,
   /* keep iff s_ij >= mean_j s_ij + beta * std_j s_ij: the Gaussian-calibrated
    * threshold with a shared standardized cutoff beta (population statistics
-   * over the key blocks of the row; they equal the pooled-key first and
-   * second moment form of App. B "Threshold variance derivation", and are
-   * computed here from the proxy row, which stays on chip) */
+   * over the key blocks of the row), computed before any score from the
+   * head's pooled-key first and second moments (App. B "Threshold variance
+   * derivation"): mean = qbar_i . m_K / sqrt(d), var = qbar_i^T C_K qbar_i / d,
+   * m_K and C_K the mean and population covariance of the pooled keys
+   * (O(d^2) per head, in the workspace); the scores are then routed chunk by
+   * chunk as they are produced (§3 "On-the-fly sparsification") */
   SOL_ROUTE_GAUSS = 1,
   /* the same threshold with the diagonal estimator of App. B "Diagonal
    * threshold estimator": mean_j s_ij = qbar_i . m_K / sqrt(d) and
@@ -120,8 +137,8 @@ typedef struct sol_attn_route {
                    /* tokens retained as sinks); sink_count = 0: none          */
 } sol_attn_route;
 
-/* Largest supported sequence length: the routing rows of Nk = N/64 scores
- * and the kept list are held on chip (4096 key blocks). */
+/* Largest supported sequence length: the kept bits and the kept list of a
+ * query block are held on chip (4096 key blocks). */
 #define SOL_ATTN_MAX_N (4096 * 64)
 
 /* Per-call counters, written by sol_attn_forward into DEVICE memory: every
@@ -137,8 +154,9 @@ typedef struct sol_attn_stats {
 /* Bytes of device workspace sol_attn_forward and sol_attn_plan need: the
  * work-queue and stats words, one cost and one order slot per work item (a
  * pair of query blocks), bf16 copies of the pooled keys and values
- * [B][H][Nk][d] for SOL_F_ROW_CORRECTION, and the pooled-key statistics
- * [B][H][2][d] of SOL_ROUTE_GAUSS_DIAG. Returns 0 for unsupported sizes. */
+ * [B][H][Nk][d] for SOL_F_ROW_CORRECTION, the pooled-key statistics
+ * [B][H][2][d] of SOL_ROUTE_GAUSS_DIAG and the pooled-key mean and covariance
+ * [B][H][d + 1][d] of SOL_ROUTE_GAUSS. Returns 0 for unsupported sizes. */
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
 
 /*
@@ -231,12 +249,16 @@ int sol_attn_forward_ex(const void* q, const void* k, const void* v, void* out,
  *   q          bf16 [B][H][N][d]; kpool fp32 [B][H][Nk][d] (sol_attn_pool)
  *   kept_bitmap device uint32 [B][H][Nq][ceil(Nk/32)], written in full
  * Errors as for sol_attn_forward; SOL_EUNSUPPORTED also when B * H > 65535,
- * and for SOL_ROUTE_GAUSS_DIAG (its statistics live in the forward's
- * workspace).
+ * and from sol_attn_mask_threshold for the Gaussian rules (their pooled-key
+ * statistics live in the forward's workspace).
  *
- * sol_attn_mask_threshold: the forward's own routing (pooled queries from the
- * Q tiles, both proxy rows of a pair of query blocks in LDS, the rule and
- * sinks of `route`); writes nothing but the bitmap.
+ * sol_attn_mask_threshold: the forward's own fused kernel, stopped after its
+ * routing pass (pooled queries from the query rows, scores consumed chunk by
+ * chunk on chip, the row-max rule and sinks of `route`), one workgroup per
+ * work item; the workspace receives the pooled keys as the three bf16 parts
+ * the kernel's score products take (as in the forward's workspace), and
+ * nothing but the bitmap is written beyond it: the same bits a forward of
+ * these inputs exports.
  *
  * sol_attn_mask_topk / sol_attn_mask_topp: pool q into the workspace, write
  * the full fp32 proxy map [B][H][Nq][Nk] to the workspace, then sort each
@@ -248,7 +270,8 @@ int sol_attn_forward_ex(const void* q, const void* k, const void* v, void* out,
  */
 size_t sol_attn_mask_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
 int sol_attn_mask_threshold(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk,
-                            const sol_attn_route* route, uint32_t* kept_bitmap, void* stream);
+                            const sol_attn_route* route, uint32_t* kept_bitmap, void* workspace,
+                            size_t workspace_bytes, void* stream);
 int sol_attn_mask_topk(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, int k,
                        uint32_t* kept_bitmap, void* workspace, size_t workspace_bytes, void* stream);
 int sol_attn_mask_topp(const void* q, const float* kpool, int B, int H, int N, int d, int Bq, int Bk, float p,
@@ -281,8 +304,8 @@ int sol_attn_forward_debug(const void* q, const void* k, const void* v, void* ou
  *                when the library is loaded and held until the process ends,
  *                laid out as [workspace | kpool | vmean]: a problem needs
  *                sol_attn_workspace_bytes() + 2 * round_up(B*H*ceil(N/Bk)*d*4,
- *                256) bytes of it (about 76 MiB for B*H = 24 heads of 118800
- *                tokens at d = 128)
+ *                256) bytes of it (about 113 MiB for B*H = 24 heads of
+ *                118800 tokens at d = 128)
  * Errors: those of sol_attn_forward_ex; SOL_EINVAL also for SOL_F_POOLED or
  * SOL_F_PLANNED (the array holds whatever the previous call on this GPU left,
  * so every call pools afresh); SOL_ESCRATCH, before any launch, when the
@@ -294,7 +317,7 @@ int sol_attn_forward_debug(const void* q, const void* k, const void* v, void* ou
  * streams or threads) race and may both return wrong results. Calls on one
  * stream are ordered and safe.
  */
-#define SOL_ATTN_SCRATCH_BYTES (96u << 20)
+#define SOL_ATTN_SCRATCH_BYTES (128u << 20)
 int sol_attn_forward_noalloc(const void* q, const void* k, const void* v, void* out,
                              int B, int H, int N, int d, int Bq, int Bk,
                              const sol_attn_route* route, unsigned flags, sol_attn_stats* stats,

@@ -186,7 +186,7 @@ def test_mask_workspace_bytes():
 def test_mask_builders_reject_before_launch(args, code):
     L = sa.lib()
     route = ctypes.byref(_lib.sol_attn_route(0, 2.0, 0.0, 0, 0))
-    assert L.sol_attn_mask_threshold(*args, route, P, None) == code
+    assert L.sol_attn_mask_threshold(*args, route, P, P, 1 << 40, None) == code
     assert L.sol_attn_mask_topk(*args, 4, P, P, 1 << 40, None) == code
     assert L.sol_attn_mask_topp(*args, ctypes.c_float(0.9), P, P, 1 << 40, None) == code
 
@@ -195,11 +195,17 @@ def test_mask_builders_reject_bad_route_bitmap_workspace():
     L = sa.lib()
     a = (P, P, 1, 2, 1000, 128, 64, 64)
     good = ctypes.byref(_lib.sol_attn_route(0, 2.0, 0.0, 0, 0))
-    assert L.sol_attn_mask_threshold(*a, None, P, None) == sa.SOL_EINVAL
-    assert L.sol_attn_mask_threshold(*a, ctypes.byref(_lib.sol_attn_route(1, 0.0, math.nan, 0, 0)), P,
+    assert L.sol_attn_mask_threshold(*a, None, P, P, 1 << 40, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_threshold(*a, ctypes.byref(_lib.sol_attn_route(1, 0.0, math.nan, 0, 0)), P, P, 1 << 40,
                                      None) == sa.SOL_EINVAL
-    assert L.sol_attn_mask_threshold(*a, good, None, None) == sa.SOL_EINVAL
-    assert L.sol_attn_mask_threshold(*a, good, P + 2, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_threshold(*a, good, None, P, 1 << 40, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_threshold(*a, good, P + 2, P, 1 << 40, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_threshold(*a, good, P, None, 1 << 40, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_threshold(*a, good, P, P + 64, 1 << 40, None) == sa.SOL_EINVAL
+    assert L.sol_attn_mask_threshold(*a, good, P, P, 64, None) == sa.SOL_EWORKSPACE
+    # the Gaussian rules are the forward's only (statistics in its workspace)
+    assert L.sol_attn_mask_threshold(*a, ctypes.byref(_lib.sol_attn_route(1, 0.0, 1.0, 0, 0)), P, P, 1 << 40,
+                                     None) == sa.SOL_EUNSUPPORTED
     assert L.sol_attn_mask_topk(*a, 4, P, None, 1 << 40, None) == sa.SOL_EINVAL
     assert L.sol_attn_mask_topk(*a, 4, P, P + 64, 1 << 40, None) == sa.SOL_EINVAL
     assert L.sol_attn_mask_topk(*a, 4, P, P, 64, None) == sa.SOL_EWORKSPACE
@@ -250,13 +256,28 @@ def test_noalloc_rejects_before_launch(route, over, code):
 def test_noalloc_scratch_limit():
     """The array's size is the header's constant; the 119K-token layer (24
     heads, d = 128) fits in it in every mode."""
-    assert sa.SOL_ATTN_SCRATCH_BYTES == 96 << 20
+    assert sa.SOL_ATTN_SCRATCH_BYTES == 128 << 20
     text = open(HEADER).read()
-    assert "#define SOL_ATTN_SCRATCH_BYTES (96u << 20)" in text
+    assert "#define SOL_ATTN_SCRATCH_BYTES (128u << 20)" in text
     L = sa.lib()
     ws = L.sol_attn_workspace_bytes(1, 24, 118800, 128, 64, 64)
     pooled = -(-(24 * 1857 * 128 * 4) // 256) * 256
     assert ws + 2 * pooled <= sa.SOL_ATTN_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(flags=sa.SOL_F_GROUP2), sa.SOL_EWORKSPACE),       # valid: the small workspace fails next
+    (dict(flags=sa.SOL_F_GROUP4), sa.SOL_EWORKSPACE),
+    (dict(flags=sa.SOL_F_GROUP8), sa.SOL_EWORKSPACE),
+    # eight query blocks per item only up to 2048 key blocks
+    (dict(flags=sa.SOL_F_GROUP8, N=2048 * 64 + 1), sa.SOL_EUNSUPPORTED),
+    (dict(flags=sa.SOL_F_GROUP4, N=2048 * 64 + 1), sa.SOL_EWORKSPACE),
+    # a plan orders the items of the automatic group size
+    (dict(flags=sa.SOL_F_GROUP2 | sa.SOL_F_POOLED | sa.SOL_F_PLANNED), sa.SOL_EINVAL),
+    (dict(flags=1 << 7), sa.SOL_EINVAL),                     # unknown bit
+])
+def test_group_field_of_the_flags(over, code):
+    assert fwd(**over) == code
 
 
 def test_forward_ex_accepts_diag_rule_arguments():

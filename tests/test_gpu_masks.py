@@ -63,8 +63,8 @@ def _wl(name, arg):
 
 
 @pytest.mark.parametrize("name,arg", WLS)
-@pytest.mark.parametrize("route", [dict(tau=0.0), dict(tau=2.0), dict(tau=8.0), dict(beta=1.0),
-                                   dict(tau=1.0, sinks=(1, 2)), dict(beta=0.5, sinks=(0, 1))])
+@pytest.mark.parametrize("route", [dict(tau=0.0), dict(tau=2.0), dict(tau=8.0), dict(tau=math.inf),
+                                   dict(tau=1.0, sinks=(1, 2)), dict(tau=0.0, sinks=(0, 1))])
 def test_threshold_router_matches_forward_and_oracle(name, arg, route):
     wl = _wl(name, arg)
     x, q, k, v, kpool, _ = _setup(wl)
@@ -81,6 +81,25 @@ def test_threshold_router_matches_forward_and_oracle(name, arg, route):
             qh, kh = bf16_bits_to_f64(x["q"][b, h]), bf16_bits_to_f64(x["k"][b, h])
             s, theta, ok, forced = oracle_route(qh, kh, route.get("tau", 0.0), route.get("beta"), route.get("sinks"))
             check_bitmap(keep[b, h], s, theta, ok, forced, "beta" not in route, where=f"{wl.name} b={b} h={h}")
+
+
+def test_threshold_router_rejects_gaussian_rules():
+    """The Gaussian thresholds take their pooled-key statistics from the
+    forward's workspace, which the mask router does not have."""
+    import ctypes
+
+    from block_sparse_attention_14_amd import _lib
+
+    wl = _custom(1000, 128, H=1)
+    x, q, k, v, kpool, _ = _setup(wl)
+    bm = torch.zeros(sa.bitmap_shape(1, 1, 1000), dtype=torch.int32, device=q.device)
+    for rule in (sa.SOL_ROUTE_GAUSS, sa.SOL_ROUTE_GAUSS_DIAG):
+        route = _lib.sol_attn_route(rule, 0.0, 1.0, 0, 0)
+        ws = torch.empty(sa.lib().sol_attn_mask_workspace_bytes(1, 1, 1000, 128, 64, 64) // 8 + 1, dtype=torch.int64,
+                         device=q.device)
+        rc = sa.lib().sol_attn_mask_threshold(q.data_ptr(), kpool.data_ptr(), 1, 1, 1000, 128, 64, 64,
+                                              ctypes.byref(route), bm.data_ptr(), ws.data_ptr(), ws.numel() * 8, None)
+        assert rc == sa.SOL_EUNSUPPORTED
 
 
 @pytest.mark.parametrize("name,arg", WLS)

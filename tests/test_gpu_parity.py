@@ -33,12 +33,13 @@ def _report(name, tag, err):
 
 
 def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, seed=0, beta=None, sinks=None,
-                 flags=0, diag=False, stratified=False, whole_heads=(), heads=None):
+                 flags=0, diag=False, stratified=False, whole_heads=(), heads=None, group=0):
     """GPU call through the C ABI, then per head: the bitmap on every query
     block; outputs on every row (default), on `query_blocks_per_head` random
     blocks, or (stratified=True) on the scheduling-stratified sample plus the
     `whole_heads` checked on every row. `heads` limits the checked heads."""
     x = inputs or make_inputs(wl)
+    flags |= sa.api.group_flag(group)
     out, keep, stats = run_gpu(x["q"], x["k"], x["v"], tau, beta=beta, sinks=sinks, flags=flags, diag=diag)
     check_stats(stats, keep, wl.N)
     rng = np.random.default_rng(seed)
@@ -50,6 +51,10 @@ def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, see
     rowc = bool(flags & sa.SOL_F_ROW_CORRECTION)
     if rowc:
         tag += " row-correction"
+    if group:
+        tag += f" group={group}"
+    if flags & sa.SOL_F_EXACT_ONLY:
+        tag += " exact-only"
     checked = 0
     for b in range(wl.B):
         for h in range(wl.H):
@@ -62,7 +67,8 @@ def _full_parity(wl: Workload, tau, inputs=None, query_blocks_per_head=None, see
             checked += wl.Nq if qbs is None else len(qbs)
             worst = max(worst, check_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], out[b, h], keep[b, h],
                                           tau, qbs, where=f"{wl.name} b={b} h={h} {tag}", beta=beta, sinks=sinks,
-                                          row_correction=rowc, diag=diag))
+                                          row_correction=rowc, diag=diag,
+                                          correction=not (flags & sa.SOL_F_EXACT_ONLY)))
     _report(wl.name, tag + f" query_blocks_checked={checked}", worst)
     return out, keep, stats
 
@@ -141,9 +147,84 @@ def video119k():
 
 @pytest.mark.parametrize("tau,whole", [(2.0, 3), (4.0, 11), (8.0, 23)])
 def test_video_dit_119k(video119k, tau, whole):
-    """The stratified sample over the work queues and one whole head per tau."""
+    """The stratified sample over the work queues and one whole head per tau
+    (the library routes eight query blocks per work item here)."""
     _full_parity(get_workload("video_dit_119k"), tau, video119k, stratified=True, whole_heads=(whole,),
                  seed=int(tau))
+
+
+def test_video_dit_119k_router_and_group_sizes(video119k):
+    """On the 119K layer: the threshold router (the fused kernel stopped after
+    routing) exports the forward's bitmap bit for bit; groups of two, four and
+    eight query blocks route alike away from the tie band (their scores are
+    summed in different orders), give outputs within the bar of each other
+    where they route alike, and match the oracle on their own routing where
+    they do not."""
+    from parity import BITMAP_TIE, oracle_route
+
+    wl = get_workload("video_dit_119k")
+    q, k, v = (to_device_bf16(video119k[n]) for n in "qkv")
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    tau = 4.0
+    outs, bms = {}, {}
+    for g in (0, 2, 4, 8):
+        bm = torch.zeros(sa.bitmap_shape(wl.B, wl.H, wl.N), dtype=torch.int32, device=q.device)
+        outs[g] = r(q, k, v, tau, bitmap=bm, group=g).clone()
+        bms[g] = bm
+    torch.cuda.synchronize()
+    assert torch.equal(bms[0], bms[8]) and torch.equal(outs[0].view(torch.int32), outs[8].view(torch.int32))
+    mb = sa.MaskBuilder(wl.B, wl.H, wl.N, wl.d)
+    assert torch.equal(mb.threshold(q, r.kpool, tau=tau), bms[0])
+    keep8 = sa.unpack_bitmap(bms[8], wl.Nk)[0]
+    out8 = outs[8].cpu().numpy()[0]
+    for g in (2, 4):
+        keep = sa.unpack_bitmap(bms[g], wl.Nk)[0]
+        out = outs[g].cpu().numpy()[0]
+        rows_differ = (keep != keep8).any(axis=-1)  # [H, Nq]
+        same = np.repeat(~rows_differ, 64, axis=1)[:, :wl.N]
+        err = np.abs(out - out8).max(axis=-1)[same].max()
+        print(f"[parity] video_dit_119k group {g} vs 8: {int(rows_differ.sum())} query blocks route differently, "
+              f"max abs diff elsewhere {err:.3e}", flush=True)
+        assert err <= 2e-2
+        for h, i in np.argwhere(rows_differ)[:8]:
+            qh, kh, vh = (bf16_bits_to_f64(video119k[n][0, h]) for n in "qkv")
+            sc, theta, _, _ = oracle_route(qh, kh, tau)
+            flip = keep[h, i] != keep8[h, i]
+            assert (np.abs(sc[i, flip] - theta[i]) <= BITMAP_TIE).all(), "a decision differs away from the threshold"
+            for kk, oo in ((keep[h], out[h]), (keep8[h], out8[h])):
+                ref = attend_head(qh, kh, vh, 64, 64, tau, keep_override=kk, query_blocks=[i])["out"]
+                sl = slice(64 * i, min(wl.N, 64 * i + 64))
+                assert np.abs(oo[sl] - ref[sl]).max() <= 2e-2
+
+
+@pytest.mark.parametrize("group", [2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [65, 1000, 4000])
+@pytest.mark.parametrize("tau", [0.0, 2.0, INF])
+def test_group_sizes(group, d, N, tau):
+    """Every group size on ragged heads: 2, 16 and 63 query blocks, so that
+    groups of four and eight end partial (63 = 7 x 8 + 7), on every row."""
+    _full_parity(_custom(N, d, H=2, seed=N + d + group), tau, group=group)
+
+
+@pytest.mark.parametrize("group", [4, 8])
+def test_group_sizes_gauss_sinks_and_row_correction(group):
+    wl = _custom(4000, 128, H=2, seed=88)
+    _full_parity(wl, 0.0, beta=1.0, group=group)
+    _full_parity(wl, 0.0, beta=2.0, diag=True, sinks=(5, 3), group=group)
+    _full_parity(wl, 1.0, flags=sa.SOL_F_ROW_CORRECTION, group=group)
+    _full_parity(wl, 1.0, sinks=(60, 3), flags=sa.SOL_F_EXACT_ONLY, group=group)
+
+
+def test_group8_far_maximum_rechecks_early_candidates():
+    """A long head (1500 key blocks, six routing chunks) whose best blocks are
+    sink blocks at the start of the sequence: every group meets its maximum
+    in a late chunk, so blocks kept against the running maximum of earlier
+    chunks are rechecked and moved to the correction. Every row checked."""
+    wl = Workload(name="sink_far_N96000_d64", B=1, H=2, grid=(1, 1, 96000), d=64, dtype="bf16", taus=(), seed=515,
+                  locality=(3.0, 3.0), sink_heads=(0, 1), sink_blocks=4)
+    for tau in (2.0, 6.0):
+        _full_parity(wl, tau, group=8)
 
 
 def test_row_correction_video_dit_119k(video119k):
@@ -507,20 +588,6 @@ def test_gauss_diag_rule_video(video32k):
     _full_parity(get_workload("image_dit_4k"), 0.0, beta=1.5, diag=True)
     _full_parity(get_workload("video_dit_32k"), 0.0, video32k, beta=3.0, diag=True,
                  sinks=(0, 1), flags=sa.SOL_F_ROW_CORRECTION)
-
-
-def test_mask_threshold_rejects_diag():
-    wl = _custom(1000, 128, H=1)
-    x = make_inputs(wl)
-    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
-    kp, _ = sa.pool(k, v)
-    import ctypes
-    from block_sparse_attention_14_amd import _lib
-    route = _lib.sol_attn_route(sa.SOL_ROUTE_GAUSS_DIAG, 0.0, 1.0, 0, 0)
-    bm = torch.zeros(sa.bitmap_shape(1, 1, 1000), dtype=torch.int32, device=q.device)
-    rc = sa.lib().sol_attn_mask_threshold(q.data_ptr(), kp.data_ptr(), 1, 1, 1000, 128, 64, 64, ctypes.byref(route),
-                                          bm.data_ptr(), None)
-    assert rc == sa.SOL_EUNSUPPORTED
 
 
 def test_order_never_changes_the_result():
