@@ -46,12 +46,12 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // statistics of the optional modes]. The cost and order slots are sized for
 // items of two query blocks, the most items any group size gives.
 struct WsLayout {
-  size_t cost, perm, kh, km, kl, vt, vbar16, kstats, kmom, total;
+  size_t cost, perm, qpool, kh, km, kl, vt, vbar16, kstats, kmom, total;
 };
 
-// Key blocks per head in the tiled operand planes: Nk rounded up to 256 (the
-// padding is written as zeros, so no read of a plane needs a bound).
-int padded_blocks(int Nk) { return (Nk + 255) / 256 * 256; }
+// Key blocks per head in the tiled operand planes: Nk rounded up to 64 (the
+// pre-pass writes the padding as zeros, so no read of a plane needs a bound).
+int padded_blocks(int Nk) { return (Nk + 63) / 64 * 64; }
 
 WsLayout ws_layout(int BH, int N, int d) {
   const size_t Nq = (size_t)(N + 63) / 64;
@@ -61,7 +61,8 @@ WsLayout ws_layout(int BH, int N, int d) {
   WsLayout w;
   w.cost = sol::kHdrWords * 4;
   w.perm = round_up(w.cost + 4 * items, 256);
-  w.kh = round_up(w.perm + 4 * items, 256);
+  w.qpool = round_up(w.perm + 4 * items, 256);
+  w.kh = round_up(w.qpool + (size_t)BH * Nq * (size_t)d * 4, 256);
   w.km = w.kh + tplane;
   w.kl = w.km + tplane;
   w.vt = w.kl + tplane;
@@ -135,8 +136,9 @@ constexpr long long kPlanMinPairs = 1ll << 21;
 constexpr int kMaxGridHeads = 65535;
 
 bool plan_by_default(const sol_attn_route& r, int BH, int Nq, int nitems, int group) {
-  return group == 2 && r.rule == SOL_ROUTE_ROWMAX && r.tau >= kPlanMinTau && use_order(r.tau, nitems) &&
-         nitems <= kPlanMaxItems && (long long)BH * Nq * Nq >= kPlanMinPairs && BH <= kMaxGridHeads;
+  return group == auto_group(BH, Nq) && r.rule == SOL_ROUTE_ROWMAX && r.tau >= kPlanMinTau &&
+         use_order(r.tau, nitems) && nitems <= kPlanMaxItems && (long long)BH * Nq * Nq >= kPlanMinPairs &&
+         BH <= kMaxGridHeads;
 }
 
 int check_sizes(int B, int H, int N, int d, int Bq, int Bk) {
@@ -162,9 +164,9 @@ sol_attn_route rowmax_route(float tau) {
 }
 
 // Planning: per-item costs and the order of each queue into the workspace
-// (row-max rule, finite tau, items of two query blocks, sizes the sort
-// handles), else the identity order, which every later planned forward may
-// still read. The items are those of the automatic group size.
+// (row-max rule, finite tau, sizes the sort handles), else the identity
+// order, which every later planned forward may still read. The items are
+// those of the automatic group size.
 hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d, float tau, void* ws, hipStream_t s,
                      bool* ordered) {
   const WsLayout w = ws_layout(BH, N, d);
@@ -173,10 +175,10 @@ hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d
   unsigned* perm = reinterpret_cast<unsigned*>(wsb + w.perm);
   const int group = auto_group(BH, Nq);
   const int nitems = sol::forward_items(BH, Nq, group);
-  *ordered = group == 2 && use_order(tau, nitems) && BH <= kMaxGridHeads;
+  *ordered = use_order(tau, nitems) && BH <= kMaxGridHeads;
   if (*ordered)
     return sol::launch_plan(q, kpool, reinterpret_cast<unsigned*>(wsb + w.cost), perm, BH, N, Nq, Nk, d, tau,
-                            (float)(1.0 / sqrt((double)d)), s);
+                            (float)(1.0 / sqrt((double)d)), group, s);
   return sol::launch_identity_order(perm, nitems, s);
 }
 
@@ -250,21 +252,49 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
 
   const unsigned* perm = nullptr;
   hipError_t e = hipSuccess;
+  // the pooling pre-pass: the pooled queries always (the routing pass reads
+  // them), the pooled keys and values unless the caller pooled them; it also
+  // resets the header words, except where a plan left them
+  // The same pass writes the routing pass's bf16 operand planes (and the
+  // per-row correction's pooled values), from its own means or the caller's.
+  float* qpool = reinterpret_cast<float*>(wsb + w.qpool);
+  uint16_t* kh = reinterpret_cast<uint16_t*>(wsb + w.kh);
+  uint16_t* km = reinterpret_cast<uint16_t*>(wsb + w.km);
+  uint16_t* kl = reinterpret_cast<uint16_t*>(wsb + w.kl);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(wsb + w.vt);
+  uint16_t* vbar16 = reinterpret_cast<uint16_t*>(wsb + w.vbar16);
+  const int Nkp = padded_blocks(Nk);
+  {
+    sol::PoolSet set;
+    set.planes.kh = kh;
+    set.planes.km = km;
+    set.planes.kl = kl;
+    set.planes.vt = vt;
+    set.planes.vrow = (flags & SOL_F_ROW_CORRECTION) ? vbar16 : nullptr;
+    set.planes.kpool = kpool;
+    set.planes.vmean = vmean;
+    set.planes.Nkp = Nkp;
+    set.src[0] = q16;
+    set.dst[0] = qpool;
+    set.n = 1;
+    if (flags & SOL_F_POOLED) {
+      set.role[0] = sol::kRoleKeysFromPool | sol::kRoleValuesFromPool;
+    } else {
+      set.src[1] = k16;
+      set.dst[1] = kpool;
+      set.role[1] = sol::kRoleKeys;
+      set.src[2] = v16;
+      set.dst[2] = vmean;
+      set.role[2] = sol::kRoleValues;
+      set.n = 3;
+    }
+    e = sol::launch_pool(set, BH, N, Nk, d, (flags & SOL_F_PLANNED) ? nullptr : static_cast<unsigned*>(ws), s);
+    if (e != hipSuccess) return SOL_EHIP;
+  }
   if (flags & SOL_F_PLANNED) {
     // the workspace holds a valid order from sol_attn_plan(), as a previous call left it
     perm = reinterpret_cast<const unsigned*>(wsb + w.perm);
   } else {
-    if (flags & SOL_F_POOLED) {
-      e = sol::launch_reset(static_cast<unsigned*>(ws), s);
-    } else {
-      sol::PoolSet set;
-      set.src[0] = k16;
-      set.dst[0] = kpool;
-      set.src[1] = v16;
-      set.dst[1] = vmean;
-      set.n = 2;
-      e = sol::launch_pool(set, BH, N, Nk, d, static_cast<unsigned*>(ws), s);
-    }
     // plan the order of the work where that was measured to pay (elsewhere
     // the items go in sequence; the order never changes the result)
     if (e == hipSuccess && plan_by_default(route, BH, Nq, nitems, group)) {
@@ -273,16 +303,6 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
       perm = reinterpret_cast<const unsigned*>(wsb + w.perm);
     }
   }
-  if (e != hipSuccess) return SOL_EHIP;
-  // bf16 operand planes of the routing pass (and of the per-row correction)
-  uint16_t* kh = reinterpret_cast<uint16_t*>(wsb + w.kh);
-  uint16_t* km = reinterpret_cast<uint16_t*>(wsb + w.km);
-  uint16_t* kl = reinterpret_cast<uint16_t*>(wsb + w.kl);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(wsb + w.vt);
-  uint16_t* vbar16 = reinterpret_cast<uint16_t*>(wsb + w.vbar16);
-  const int Nkp = padded_blocks(Nk);
-  e = sol::launch_prep(kpool, vmean, kh, km, kl, vt, (flags & SOL_F_ROW_CORRECTION) ? vbar16 : nullptr, BH, Nk, Nkp,
-                       d, s);
   if (e != hipSuccess) return SOL_EHIP;
   float* kstats = reinterpret_cast<float*>(wsb + w.kstats);
   if (route.rule == SOL_ROUTE_GAUSS_DIAG) {
@@ -333,12 +353,14 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   p.vt = vt;
   p.Nkp = Nkp;
   p.vbar16 = vbar16;
+  p.qpool = qpool;
   e = sol::launch_forward(p, d, s);
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 
 // Workspace of the mask builders: top-k / top-p use [pooled queries | map];
-// the threshold router uses [three bf16 planes of the pooled keys].
+// the threshold router uses [three bf16 planes of the pooled keys | pooled
+// queries].
 struct MaskWs {
   size_t map, total;
 };
@@ -347,7 +369,8 @@ MaskWs mask_ws(int BH, int N, int d) {
   const size_t Nq = (size_t)(N + 63) / 64;
   MaskWs w;
   w.map = round_up((size_t)BH * Nq * (size_t)d * 4, 256);
-  const size_t planes = 3 * round_up((size_t)BH * padded_blocks((int)Nq) * (size_t)d * 2, 256);
+  const size_t planes = 3 * round_up((size_t)BH * padded_blocks((int)Nq) * (size_t)d * 2, 256) +
+                        round_up((size_t)BH * Nq * (size_t)d * 4, 256);
   w.total = std::max(round_up(w.map + (size_t)BH * Nq * Nq * 4, 256), planes);
   return w;
 }
@@ -405,12 +428,24 @@ int sol_attn_mask_threshold(const void* q, const float* kpool, int B, int H, int
   const int BH = B * H, Nq = (N + 63) / 64;
   if (workspace_bytes < mask_ws(BH, N, d).total) return SOL_EWORKSPACE;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // the score operands (the pooled keys in three bf16 parts), as the forward makes them
+  // the score operands (the pooled keys in three bf16 parts, the pooled
+  // queries), as the forward makes them
   const size_t plane = round_up((size_t)BH * padded_blocks(Nq) * (size_t)d * 2, 256);
   uint16_t* kh = static_cast<uint16_t*>(workspace);
   uint16_t* km = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) + plane);
   uint16_t* kl = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) + 2 * plane);
-  hipError_t e = sol::launch_prep(kpool, nullptr, kh, km, kl, nullptr, nullptr, BH, Nq, padded_blocks(Nq), d, s);
+  float* qpool = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + 3 * plane);
+  sol::PoolSet set;
+  set.src[0] = static_cast<const uint16_t*>(q);
+  set.dst[0] = qpool;
+  set.role[0] = sol::kRoleKeysFromPool;
+  set.n = 1;
+  set.planes.kh = kh;
+  set.planes.km = km;
+  set.planes.kl = kl;
+  set.planes.kpool = kpool;
+  set.planes.Nkp = padded_blocks(Nq);
+  hipError_t e = sol::launch_pool(set, BH, N, Nq, d, nullptr, s);
   if (e != hipSuccess) return SOL_EHIP;
   // the forward's own fused kernel, stopped after its routing: one workgroup
   // per item, no work queues, no correction sums; only the bitmap is written
@@ -422,6 +457,7 @@ int sol_attn_mask_threshold(const void* q, const float* kpool, int B, int H, int
   p.klo16 = km;
   p.klo2 = kl;
   p.Nkp = padded_blocks(Nq);
+  p.qpool = qpool;
   p.bitmap = kept_bitmap;
   p.N = N;
   p.Nq = Nq;

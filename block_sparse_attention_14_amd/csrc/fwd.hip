@@ -352,56 +352,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     };
     const int stEnd = p.Nkp / 16;
     auto step_of = [&](int kk) { return kk < nst ? chunk_at(kk, cs, nst) : stEnd; };
-    StepOps b;
-    StepVals vv;
 
-    // ---- A. pooled queries of the G blocks; Gaussian thresholds ----
+    // ---- A. pooled queries of the G blocks (from the pooling pre-pass); Gaussian thresholds ----
     {
-      constexpr int PER = kBlk * CH / kThreads, RSTEP = kThreads / CH;
-      const uint32_t qoff = ((tid / CH) * D + (tid % CH) * 8) * 2;
-#pragma unroll
-      for (int pr = 0; pr < G / 2; ++pr) {
-        uint4 qr[2][PER];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          const int qi = g0 + 2 * pr + blk;
-          const int nb = qi < Nq ? min(kBlk, N - qi * kBlk) : 0;
-          const rsrc_t r = make_rsrc(p.q + hoff + (size_t)min(qi, Nq - 1) * kBlk * D, (uint32_t)nb * D * 2);
-#pragma unroll
-          for (int u = 0; u < PER; ++u) qr[blk][u] = ld16(r, qoff, u * RSTEP * D * 2);
-        }
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          float csum[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) csum[e] = 0.f;
-#pragma unroll
-          for (int u = 0; u < PER; ++u) {
-            const uint4 w = qr[blk][u];
-            csum[0] += bf16lo(w.x); csum[1] += bf16hi(w.x); csum[2] += bf16lo(w.y); csum[3] += bf16hi(w.y);
-            csum[4] += bf16lo(w.z); csum[5] += bf16hi(w.z); csum[6] += bf16lo(w.w); csum[7] += bf16hi(w.w);
-          }
-          // lanes l, l ^ 16, l ^ 32, l ^ 48 (and l ^ 8 when a row has 8 chunks)
-          // hold the same columns of other rows
-#pragma unroll
-          for (int e = 0; e < 8; ++e) csum[e] = colsum_rows<CH>(csum[e]);
-          if (lane < CH) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part[(wid * G + 2 * pr + blk) * D + lane * 8 + e] = csum[e];
-          }
-        }
-      }
       // routing state of the group
       if (tid < G) sm.M[tid] = -INFINITY;
       for (int w = tid; w < G * KW; w += kThreads) (&sm.kbits[0][0])[w] = 0u;
-      __syncthreads();
       for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int g = idx / D, col = idx % D;
-        const int qi = g0 + g;
-        const int nb = qi < Nq ? min(kBlk, N - qi * kBlk) : 0;
-        const float sq = (part[(0 * G + g) * D + col] + part[(1 * G + g) * D + col]) +
-                         (part[(2 * G + g) * D + col] + part[(3 * G + g) * D + col]);
-        qbar[idx] = nb > 0 ? sq / (float)nb : 0.f;
+        const int g = idx / D, c = idx % D;
+        qbar[idx] = g0 + g < Nq ? p.qpool[((size_t)bh * Nq + g0 + g) * D + c] : 0.f;
       }
       __syncthreads();  // pooled queries complete
 
@@ -623,13 +582,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 
       // the wave's steps: the scores of the next step (and the loads of the
       // one after) are formed at the end of each iteration
-      float sc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      // (a wave with no step loads the tile past the planes: zeros, no traffic,
+      // and scores of -inf)
+      float sc[4];
       int k = wid;
-      if (k < nst) {
-        load_vals(vv, step_of(k));
-        load_step(b, step_of(k));
-        step_scores(b, step_of(k), sc, step_of(k + 4));
-      }
+      StepOps b;
+      StepVals vv;
+      load_vals(vv, step_of(k));
+      load_step(b, step_of(k));
+      step_scores(b, step_of(k), sc, step_of(k + 4));
       if (rowmax) {
         // the maximum over the first step of every wave, before any decision
         const float mx = rowmax4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));

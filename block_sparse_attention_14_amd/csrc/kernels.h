@@ -59,22 +59,42 @@ struct FwdParams {
   int exact_only;        // skipped blocks dropped instead of corrected
   int row_corr;          // per-row (token-to-block) correction over the pooled tiles below
   int out_bf16;          // store the output rounded to bf16
-  const uint16_t* khi16;   // bf16 pooled keys, first part, tiled (launch_prep kh)
-  const uint16_t* klo16;   // bf16 pooled keys, second part, tiled (launch_prep km)
-  const uint16_t* klo2;    // bf16 pooled keys, third part, tiled (launch_prep kl)
-  const uint16_t* vt;      // bf16 pooled values, tiled (launch_prep vt)
-  int Nkp;                 // key blocks per head in the tiled planes: Nk rounded up to 256
+  const uint16_t* khi16;   // bf16 pooled keys, first part, tiled (Planes kh)
+  const uint16_t* klo16;   // bf16 pooled keys, second part, tiled (Planes km)
+  const uint16_t* klo2;    // bf16 pooled keys, third part, tiled (Planes kl)
+  const uint16_t* vt;      // bf16 pooled values, tiled (Planes vt)
+  int Nkp;                 // key blocks per head in the tiled planes: Nk rounded up to 64
   const uint16_t* vbar16;  // bf16 [BH][Nk][d] pooled values (row_corr)
+  const float* qpool;      // fp32 [BH][Nq][d] pooled queries
   const float* kstats;     // fp32 [BH][2][d]: mean and variance of the pooled keys (GAUSS_DIAG)
   const float* kmom;       // fp32 [BH][d + 1][d]: mean, then covariance rows of the pooled keys (GAUSS)
 };
 
 // Up to three bf16 [BH][N][d] tensors pooled per 64-token block into fp32
 // [BH][Nk][d] means.
+// The fused kernel's routing planes (layout in pool.hip), written by the
+// pooling pre-pass.
+struct Planes {
+  uint16_t* kh;  // bf16 pooled keys, three parts, [BH][Nkp][d] in 16-block operand tiles
+  uint16_t* km;
+  uint16_t* kl;
+  uint16_t* vt;    // bf16 pooled values, [BH][Nkp][d] in 16-block operand tiles (null: none)
+  uint16_t* vrow;  // bf16 pooled values [BH][Nk][d], row-major (null: none)
+  const float* kpool;  // the caller's pooled keys (kRoleKeysFromPool)
+  const float* vmean;  // the caller's pooled values (kRoleValuesFromPool)
+  int Nkp;             // key blocks per head in the tiled planes: Nk rounded up to 64
+};
+// What a tensor's workgroups write besides its means: the key planes from
+// their own means (the tensor is k), the value planes likewise (v), or both
+// kinds from the caller's pooled tensors (given to the workgroups of q).
+constexpr int kRoleKeys = 1, kRoleValues = 2, kRoleKeysFromPool = 4, kRoleValuesFromPool = 8;
+
 struct PoolSet {
   const uint16_t* src[3];
   float* dst[3];
+  int role[3] = {0, 0, 0};
   int n;
+  Planes planes = {};
 };
 
 // Pools the tensors of `set`; when `hdr` is non-null, also resets the
@@ -82,12 +102,6 @@ struct PoolSet {
 hipError_t launch_pool(const PoolSet& set, int BH, int N, int Nk, int d, unsigned* hdr, hipStream_t stream);
 
 // Routing operand planes from the fp32 pooled keys and values (pool.hip):
-// kh + km + kl = kpool in three bf16 parts and vt = bf16(vmean), each
-// [BH][Nkp][d] in 16-block operand tiles (key blocks from Nk to Nkp, a
-// multiple of 64, zero); vrow = bf16(vmean) [BH][Nk][d] row-major when not
-// null; with vt null only the key planes are written.
-hipError_t launch_prep(const float* kpool, const float* vmean, uint16_t* kh, uint16_t* km, uint16_t* kl,
-                       uint16_t* vt, uint16_t* vrow, int BH, int Nk, int Nkp, int d, hipStream_t stream);
 
 // stats[bh][0][c] = mean_j kpool[bh][j][c], stats[bh][1][c] = population
 // variance over j (two passes), one workgroup per head.
@@ -101,12 +115,13 @@ hipError_t launch_kmom(const float* kpool, float* mom, int BH, int Nk, int d, hi
 // Resets the workspace header words (one small kernel).
 hipError_t launch_reset(unsigned* hdr, hipStream_t stream);
 
-// Per-item cost estimates (union of the kept sets of each pair of query
-// blocks, from sampled query means) and the order of each queue's range:
+// Per-pair cost estimates (union of the kept sets of each pair of query
+// blocks, from sampled query means) and the order of each queue's range of
+// items of `group` query blocks (an item costs the sum over its pairs):
 // head-major, then its last third heaviest first.
 // perm[rank] = item, with rank and item in the same queue range.
 hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, int BH, int N, int Nq,
-                       int Nk, int d, float tau, float proxy_scale, hipStream_t stream);
+                       int Nk, int d, float tau, float proxy_scale, int group, hipStream_t stream);
 
 // perm[i] = i for every item (the order of a plan that does not sort).
 hipError_t launch_identity_order(unsigned* perm, int nitems, hipStream_t stream);

@@ -6,7 +6,7 @@
 // routing": dynamic, query-dependent budgets). A persistent grid that takes
 // items in sequence order ends with a few workgroups finishing the heaviest
 // items while the rest idle. These two small kernels estimate every item's
-// cost (the size of the union of its two blocks' kept lists) and order each
+// cost (the sizes of the unions of its pairs' kept lists) and order each
 // XCD queue: head-major first, then its last third heaviest first, so the
 // queue ends on light items.
 //
@@ -232,17 +232,26 @@ __global__ __launch_bounds__(64 * kPlanWaves) void plan_kernel(const uint16_t* _
 // equal costs in no particular order), so the queue ends on its lightest
 // items and no workgroup starts a heavy one when the others are about to
 // finish.
+// An item of G query blocks costs the sum over its G / 2 pairs, bucketed in
+// units of G / 2 so that the histogram keeps Nk + 1 buckets.
 __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict__ cost, unsigned* __restrict__ perm,
-                                                     int nitems, int Nk) {
+                                                     int nitems, int Nk, int npairs, int group, int ngroups) {
   extern __shared__ unsigned hist[];  // [Nk + 1] counts, then running offsets
   __shared__ unsigned part[1024];
   const int tid = threadIdx.x, nt = blockDim.x;
   const int lo = queue_begin(blockIdx.x, nitems), hi = queue_begin(blockIdx.x + 1, nitems);
   const int t0 = hi - (hi - lo) / 3;  // first item of the sorted tail
+  const int hp = group / 2;           // pairs per item
+  auto bucket = [&](int i) {
+    const int bh = i / ngroups, p0 = hp * (i - bh * ngroups);
+    unsigned c = 0;
+    for (int t = 0; t < hp && p0 + t < npairs; ++t) c += cost[(size_t)bh * npairs + p0 + t];
+    return min(c / (unsigned)hp, (unsigned)Nk);
+  };
   for (int i = lo + tid; i < t0; i += nt) perm[i] = (unsigned)i;
   for (int b = tid; b <= Nk; b += nt) hist[b] = 0u;
   __syncthreads();
-  for (int i = t0 + tid; i < hi; i += nt) atomicAdd(&hist[min(cost[i], (unsigned)Nk)], 1u);
+  for (int i = t0 + tid; i < hi; i += nt) atomicAdd(&hist[bucket(i)], 1u);
   __syncthreads();
   // exclusive offsets with the highest cost first: position p is bucket Nk - p;
   // thread t owns positions [t*C, (t+1)*C)
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict_
     }
   }
   __syncthreads();
-  for (int i = t0 + tid; i < hi; i += nt) perm[atomicAdd(&hist[min(cost[i], (unsigned)Nk)], 1u)] = (unsigned)i;
+  for (int i = t0 + tid; i < hi; i += nt) perm[atomicAdd(&hist[bucket(i)], 1u)] = (unsigned)i;
 }
 
 __global__ __launch_bounds__(256) void iota_kernel(unsigned* __restrict__ perm, int nitems) {
@@ -286,7 +295,7 @@ hipError_t launch_identity_order(unsigned* perm, int nitems, hipStream_t stream)
 }
 
 hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, int BH, int N, int Nq,
-                       int Nk, int d, float tau, float proxy_scale, hipStream_t stream) {
+                       int Nk, int d, float tau, float proxy_scale, int group, hipStream_t stream) {
   const dim3 grid((Nq + kPlanQ - 1) / kPlanQ, BH);
   if (d == 128)
     hipLaunchKernelGGL(plan_kernel<128>, grid, dim3(64 * kPlanWaves), 0, stream, q, kpool, cost, N, Nq, Nk, tau,
@@ -296,9 +305,9 @@ hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, un
                        proxy_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nitems = forward_items(BH, Nq, 2);  // the plan orders items of two query blocks
+  const int nitems = forward_items(BH, Nq, group);
   hipLaunchKernelGGL(order_kernel, dim3(kQueues), dim3(1024), (size_t)(Nk + 1) * sizeof(unsigned), stream, cost,
-                     perm, nitems, Nk);
+                     perm, nitems, Nk, (Nq + 1) / 2, group, (Nq + group - 1) / group);
   return hipGetLastError();
 }
 

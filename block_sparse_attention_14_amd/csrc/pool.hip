@@ -1,19 +1,80 @@
-// Pooling pre-pass: per 64-token block, the fp32 mean of k and of v over the
+// Pooling pre-pass: per 64-token block, the fp32 mean of q, k and v over the
 // block's valid tokens (page "Sol-Attn: Accelerating Video Generation
 // Inference via On-the-Fly Attention Sparsification", §2 "Block-Sparse
 // Attention": mean-pooled blocks; §3 "Approximate correction": pooled keys and
-// summed values, the latter being n_j times the mean stored here).
+// summed values, the latter being n_j times the mean stored here), and the
+// bf16 operand planes the fused kernel's routing pass reads.
 //
 // One workgroup per (block j, head) and tensor (grid x = head * Nk + j, grid y
 // = tensor). Each thread streams 16-byte chunks of rows, the partial sums meet
 // in LDS, and thread c writes column c. The pass is a pure HBM stream: every
-// input byte is read once. The forward pools k and v here; its pooled queries
-// are summed inside the fused kernel from the Q tiles it loads anyway. The
-// top-k / top-p mask builders pool q with this kernel.
+// input byte is read once. A workgroup whose tensor has a plane role also
+// writes block j's entries of the routing planes, from its own mean or from
+// the caller's pooled keys and values.
 #include "common.h"
 #include "kernels.h"
 
 namespace sol {
+
+// The routing planes (Planes in kernels.h): 16-block tiles stored in the
+// order the matrix cores take their operands, so that one 64-lane load of the
+// fused kernel reads one contiguous stretch:
+//   kh, km, kl [BH][Nkp / 16][D / 8][16][8]: k = kh + km + kl + r, each part
+//     rounded to nearest even from the remainder of the parts before it
+//     (|r| <= 2^-24 |k| or so), so bf16 products of the parts carry an
+//     fp32-grade score; element (j, c) of a head sits in tile j / 16 at
+//     8-column chunk c / 8, row j % 16, position c % 8;
+//   vt [BH][Nkp / 16][D / 16][4][16][4]: the pooled values in bf16, element
+//     (j, c) in tile j / 16 at column tile c / 16, key quarter (j % 16) / 4,
+//     column c % 16, position j % 4;
+//   vrow [BH][Nk][D] (optional): bf16 pooled values, row-major (per-row
+//     correction).
+// Thread c of block j's workgroup writes column c of the planes its role
+// names, from x (the block's mean) or from the caller's pooled tensors. The
+// workgroup of the last block also zeroes rows Nk .. Nkp - 1, which the
+// fused kernel reads as padding of the last tile.
+__device__ __forceinline__ void key_parts(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+  const uint32_t hh = pack_bf16x2(x, 0.f) & 0xffffu;
+  const float r1 = x - __uint_as_float(hh << 16);
+  const uint32_t mm = pack_bf16x2(r1, 0.f) & 0xffffu;
+  const float r2 = r1 - __uint_as_float(mm << 16);
+  h = (uint16_t)hh;
+  m = (uint16_t)mm;
+  l = (uint16_t)(pack_bf16x2(r2, 0.f) & 0xffffu);
+}
+
+template <int D>
+__device__ void write_planes(const Planes& pl, int role, float x, int bh, int j, int Nk, int c) {
+  constexpr int CH = D / 8, CT = D / 16;
+  const size_t base = (size_t)bh * pl.Nkp * D;
+  auto koff = [&](int jj) { return base + ((size_t)((jj >> 4) * CH + (c >> 3)) * 16 + (jj & 15)) * 8 + (c & 7); };
+  auto voff = [&](int jj) {
+    return base + ((size_t)(((jj >> 4) * CT + (c >> 4)) * 4 + ((jj & 15) >> 2)) * 16 + (c & 15)) * 4 + (jj & 3);
+  };
+  const size_t rowc = ((size_t)bh * Nk + j) * D + c;
+  if (role & (kRoleKeys | kRoleKeysFromPool)) {
+    const float xk = (role & kRoleKeys) ? x : pl.kpool[rowc];
+    uint16_t h, m, l;
+    key_parts(xk, h, m, l);
+    const size_t o = koff(j);
+    pl.kh[o] = h;
+    pl.km[o] = m;
+    pl.kl[o] = l;
+    if (j == Nk - 1)
+      for (int jz = Nk; jz < pl.Nkp; ++jz) {
+        const size_t oz = koff(jz);
+        pl.kh[oz] = pl.km[oz] = pl.kl[oz] = 0;
+      }
+  }
+  if ((role & (kRoleValues | kRoleValuesFromPool)) && pl.vt) {
+    const float xv = (role & kRoleValues) ? x : pl.vmean[rowc];
+    const uint16_t b = (uint16_t)(pack_bf16x2(xv, 0.f) & 0xffffu);
+    pl.vt[voff(j)] = b;
+    if (pl.vrow) pl.vrow[rowc] = b;
+    if (j == Nk - 1)
+      for (int jz = Nk; jz < pl.Nkp; ++jz) pl.vt[voff(jz)] = 0;
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(PoolSet set, int N, int Nk, unsigned* hdr) {
@@ -53,81 +114,14 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolSet set, int N, int Nk, u
     float s = 0.f;
 #pragma unroll 8
     for (int r = 0; r < RPP; ++r) s += part[r][tid];
-    dst[tid] = s / (float)nj;
+    s /= (float)nj;
+    dst[tid] = s;
+    const int role = set.role[which];
+    if (role != 0) write_planes<D>(set.planes, role, s, bh, j, Nk, tid);
   }
 
   if (hdr != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
     for (int w = tid; w < kHdrWords; w += 256) hdr[w] = w == kHdrMin ? 0xffffffffu : 0u;
-}
-
-// bf16 operand planes of the fused kernel's routing pass, from the fp32
-// pooled keys and values, for 64 key blocks per workgroup (grid (Nkp / 64, BH)).
-// Both kinds are stored in 16-block tiles laid out in the order the matrix
-// cores take their operands, so that one 64-lane load reads one contiguous
-// stretch (512 or 1024 bytes) instead of 16-byte pieces of 16 rows:
-//   kh, km, kl [BH][Nkp / 16][D / 8][16][8]: k = kh + km + kl + r, each part
-//     rounded to nearest even from the remainder of the parts before it
-//     (|r| <= 2^-24 |k| or so), so bf16 products of the parts carry an
-//     fp32-grade score; element (j, c) of a head sits in tile j / 16 at
-//     8-column chunk c / 8, row j % 16, position c % 8;
-//   vt [BH][Nkp / 16][D / 16][4][16][4]: the pooled values in bf16, element
-//     (j, c) in tile j / 16 at column tile c / 16, key quarter (j % 16) / 4,
-//     column c % 16, position j % 4;
-//   vrow [BH][Nk][D] (optional): bf16 pooled values, row-major (per-row
-//     correction).
-// Key blocks from Nk to Nkp (a multiple of 64) are written as zeros. With vt
-// null only the key planes are written.
-template <int D>
-__global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ kpool, const float* __restrict__ vmean,
-                                                   uint16_t* __restrict__ kh, uint16_t* __restrict__ km,
-                                                   uint16_t* __restrict__ kl, uint16_t* __restrict__ vt,
-                                                   uint16_t* __restrict__ vrow, int Nk, int Nkp) {
-  constexpr int CH = D / 8, CT = D / 16;
-  __shared__ float ks[kBlk][D + 1];
-  __shared__ float vs[kBlk][D + 1];
-  const int bh = blockIdx.y, j0 = blockIdx.x * kBlk, tid = threadIdx.x;
-  const size_t rowbase = (size_t)bh * Nk;
-  for (int idx = tid; idx < kBlk * D; idx += 256) {
-    const int jj = idx / D, c = idx % D, j = j0 + jj;
-    float x = 0.f, v = 0.f;
-    if (j < Nk) {
-      x = kpool[(rowbase + j) * D + c];
-      if (vmean) v = vmean[(rowbase + j) * D + c];
-      if (vrow) vrow[(rowbase + j) * D + c] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
-    }
-    ks[jj][c] = x;
-    vs[jj][c] = v;
-  }
-  __syncthreads();
-  // this workgroup's 64 blocks are four whole tiles: a contiguous stretch of
-  // every plane, written in storage order
-  const size_t obase = ((size_t)bh * Nkp + j0) * D;
-  for (int o = tid; o < kBlk * D; o += 256) {
-    const int e8 = o % 8, r = (o / 8) % 16, cc = (o / 128) % CH, t = o / (128 * CH);
-    const float x = ks[16 * t + r][8 * cc + e8];
-    const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
-    const float r1 = x - __uint_as_float(h << 16);
-    const uint32_t m = pack_bf16x2(r1, 0.f) & 0xffffu;
-    const float r2 = r1 - __uint_as_float(m << 16);
-    kh[obase + o] = (uint16_t)h;
-    km[obase + o] = (uint16_t)m;
-    kl[obase + o] = (uint16_t)(pack_bf16x2(r2, 0.f) & 0xffffu);
-  }
-  if (vt == nullptr) return;  // the scores' planes only (routing without attention)
-  for (int o = tid; o < kBlk * D; o += 256) {
-    const int e4 = o % 4, col = (o / 4) % 16, kq = (o / 64) % 4, ci = (o / 256) % CT, t = o / (256 * CT);
-    vt[obase + o] = (uint16_t)(pack_bf16x2(vs[16 * t + 4 * kq + e4][16 * ci + col], 0.f) & 0xffffu);
-  }
-}
-
-hipError_t launch_prep(const float* kpool, const float* vmean, uint16_t* kh, uint16_t* km, uint16_t* kl,
-                       uint16_t* vt, uint16_t* vrow, int BH, int Nk, int Nkp, int d, hipStream_t stream) {
-  const dim3 grid((unsigned)(Nkp / kBlk), (unsigned)BH);
-  if (d == 128)
-    hipLaunchKernelGGL(prep_kernel<128>, grid, dim3(256), 0, stream, kpool, vmean, kh, km, kl, vt, vrow, Nk, Nkp);
-  else
-    hipLaunchKernelGGL(prep_kernel<64>, grid, dim3(256), 0, stream, kpool, vmean, kh, km, kl, vt, vrow, Nk, Nkp);
-  return hipGetLastError();
 }
 
 template <int D>

@@ -152,10 +152,12 @@ typedef struct sol_attn_stats {
 } sol_attn_stats;
 
 /* Bytes of device workspace sol_attn_forward and sol_attn_plan need: the
- * work-queue and stats words, one cost and one order slot per work item (a
- * pair of query blocks), bf16 copies of the pooled keys and values
- * [B][H][Nk][d] for SOL_F_ROW_CORRECTION, the pooled-key statistics
- * [B][H][2][d] of SOL_ROUTE_GAUSS_DIAG and the pooled-key mean and covariance
+ * work-queue and stats words, one cost and one order slot per pair of query
+ * blocks, the pooled queries [B][H][Nq][d] (fp32), the routing pass's bf16
+ * operand planes of the pooled keys (three parts) and values, each
+ * [B][H][Nk rounded up to 64][d], bf16 pooled values [B][H][Nk][d] for
+ * SOL_F_ROW_CORRECTION, the pooled-key statistics [B][H][2][d] of
+ * SOL_ROUTE_GAUSS_DIAG and the pooled-key mean and covariance
  * [B][H][d + 1][d] of SOL_ROUTE_GAUSS. Returns 0 for unsupported sizes. */
 size_t sol_attn_workspace_bytes(int B, int H, int N, int d, int Bq, int Bk);
 
@@ -304,7 +306,7 @@ int sol_attn_forward_debug(const void* q, const void* k, const void* v, void* ou
  *                when the library is loaded and held until the process ends,
  *                laid out as [workspace | kpool | vmean]: a problem needs
  *                sol_attn_workspace_bytes() + 2 * round_up(B*H*ceil(N/Bk)*d*4,
- *                256) bytes of it (about 113 MiB for B*H = 24 heads of
+ *                256) bytes of it (about 126 MiB for B*H = 24 heads of
  *                118800 tokens at d = 128)
  * Errors: those of sol_attn_forward_ex; SOL_EINVAL also for SOL_F_POOLED or
  * SOL_F_PLANNED (the array holds whatever the previous call on this GPU left,
