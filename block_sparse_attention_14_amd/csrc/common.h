@@ -46,6 +46,12 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 // Cross-lane moves inside a row of 16 lanes (DPP, a VALU operand modifier;
 // no LDS round trip). Controls: quad_perm [1,0,3,2] swaps neighbours,
 // quad_perm [2,3,0,1] swaps pairs, row_half_mirror maps lane i of each

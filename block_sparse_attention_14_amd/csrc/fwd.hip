@@ -199,7 +199,8 @@ struct alignas(16) Small {
   float wden[4][16];                // per wave and column: the wave's correction denominator
   uint32_t kbits[G][key_words<G>()];  // kept-block bits
   int cnt[3][4];
-  int lastkept[2];
+  unsigned long long st64[3];  // this workgroup's stats: kept blocks, total blocks, kept token pairs
+  unsigned st32[2];            // fewest and most kept blocks of a query block
   int item;  // the item of the next iteration (-1: none left)
   int last;  // this workgroup finished last
 };
@@ -273,8 +274,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     }
   };
   // per-workgroup stats, published once at the end (thread 0's registers)
-  unsigned long long st_kept = 0, st_tot = 0, st_pairs = 0;
-  unsigned st_min = 0xffffffffu, st_max = 0u;
+  // (in LDS, thread 0's, so that nothing of them is held in registers
+  // through the kept loops)
+  if (tid == 0) {
+    sm.st64[0] = sm.st64[1] = sm.st64[2] = 0ull;
+    sm.st32[0] = 0xffffffffu;
+    sm.st32[1] = 0u;
+  }
 
   // (an order entry out of range, possible only with a workspace that was
   // never planned, ends this workgroup's work instead of being followed)
@@ -511,9 +517,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
             v += __shfl_down(s1[e], 8, 16) + s2[e];
           else
             v += __shfl_down(s1[e], G, 16) + __shfl_down(s1[e], 2 * G, 16);
-          v *= p.proxy_scale;
-          if (!gval || 16 * st + 4 * kq + e >= Nk) v = -INFINITY;
-          sc[e] = v;
+          sc[e] = gval && 16 * st + 4 * kq + e < Nk ? v * p.proxy_scale : -INFINITY;
         }
       };
       // correction weights w[e] (relative to Mw) of the step into the
@@ -553,13 +557,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       const float thg = !rowmax && col < G ? sm.theta[col] : 0.f;
       // route one step whose scores are sc
       auto route_step = [&](const StepVals& b, int st, const float (&sc)[4]) {
-        float alpha = 1.f;
+        // (selects rather than branches: every lane evaluates the same
+        // instructions, and the exponentials of dropped lanes are discarded)
         const float smax = rowmax4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-        if (smax > Mw) {
-          alpha = __expf(Mw - smax);  // 0 on the first raise from -inf
-          Mw = smax;
-          nlow = nseq;
-        }
+        const bool raised = smax > Mw;
+        const float alpha = raised ? __builtin_amdgcn_exp2f((Mw - smax) * kLog2e) : 1.f;  // 0 on the first raise from -inf
+        Mw = raised ? smax : Mw;
+        nlow = raised ? nseq : nlow;
         const float th = rowmax ? Mw - p.tau : thg;
         uint32_t bits = 0u;
         float w[4], wsum = 0.f;
@@ -569,7 +573,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
           const bool valid = gval && j < Nk;
           const bool sink = (unsigned)(j - p.sink_lo) < (unsigned)(p.sink_hi - p.sink_lo);
           const bool keep = valid && (sc[e] >= th || sink);
-          w[e] = corr && valid && !keep ? (float)min(kBlk, N - j * kBlk) * __expf(sc[e] - Mw) : 0.f;
+          const float ev = __builtin_amdgcn_exp2f((sc[e] - Mw) * kLog2e);
+          w[e] = corr && valid && !keep ? (float)min(kBlk, N - j * kBlk) * ev : 0.f;
           wsum += w[e];
           bits |= (keep ? 1u : 0u) << (4 * kq + e);
         }
@@ -756,33 +761,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       }
 
       // ---- 2. union of the two kept lists, from the kept bits ----
-      int nu = 0, nkA = 0, nkB = 0;
-      for (int j0 = 0; j0 < Nk; j0 += kThreads) {
-        const int j = j0 + tid;
-        bool kA = false, kB = false;
-        if (j < Nk) {
-          kA = (sm.kbits[gA][j >> 5] >> (j & 31)) & 1u;
-          kB = hasB && ((sm.kbits[gA + 1][j >> 5] >> (j & 31)) & 1u);
+      // Thread t takes kept-bit word t of both blocks (at most 128 words):
+      // the union's count, a prefix over the threads, then the word's kept
+      // blocks in ascending order at that offset.
+      int nu;
+      {
+        const int nw = (Nk + 31) / 32;
+        const uint32_t wa = tid < nw ? sm.kbits[gA][tid] : 0u;
+        const uint32_t wb = tid < nw && hasB ? sm.kbits[gA + 1][tid] : 0u;
+        const uint32_t wu = wa | wb;
+        const int cu = __popc(wu);
+        int x = cu;  // inclusive prefix over the wave's lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(x, o);
+          x += lane >= o ? y : 0;
         }
-        const unsigned long long bA = __ballot(kA), bB = __ballot(kB), bU = bA | bB;
+        const int ca = wave_sum_int(__popc(wa)), cb = wave_sum_int(__popc(wb));
+        if (lane == 63) sm.cnt[0][wid] = x;
         if (lane == 0) {
-          sm.cnt[0][wid] = __popcll(bU);
-          sm.cnt[1][wid] = __popcll(bA);
-          sm.cnt[2][wid] = __popcll(bB);
-        }
-        if (j == Nk - 1) {
-          sm.lastkept[0] = kA;
-          sm.lastkept[1] = kB;
+          sm.cnt[1][wid] = ca;
+          sm.cnt[2][wid] = cb;
         }
         __syncthreads();  // (also: every wave holds its Q operands; the stages are free)
-        int off = nu;
+        int off = x - cu;
         for (int w2 = 0; w2 < wid; ++w2) off += sm.cnt[0][w2];
-        if (kA || kB)
-          ulist[off + __popcll(bU & ((1ull << lane) - 1ull))] = (uint16_t)(j | (kA ? 1 << 14 : 0) | (kB ? 1 << 15 : 0));
-        nu += sm.cnt[0][0] + sm.cnt[0][1] + sm.cnt[0][2] + sm.cnt[0][3];
-        nkA += sm.cnt[1][0] + sm.cnt[1][1] + sm.cnt[1][2] + sm.cnt[1][3];
-        nkB += sm.cnt[2][0] + sm.cnt[2][1] + sm.cnt[2][2] + sm.cnt[2][3];
-        __syncthreads();
+        for (uint32_t r = wu; r != 0u; r &= r - 1u) {
+          const int bit = __builtin_ctz(r);
+          ulist[off++] = (uint16_t)((32 * tid + bit) | (((wa >> bit) & 1u) << 14) | (((wb >> bit) & 1u) << 15));
+        }
+        nu = sm.cnt[0][0] + sm.cnt[0][1] + sm.cnt[0][2] + sm.cnt[0][3];
+        const int nkA = sm.cnt[1][0] + sm.cnt[1][1] + sm.cnt[1][2] + sm.cnt[1][3];
+        const int nkB = sm.cnt[2][0] + sm.cnt[2][1] + sm.cnt[2][2] + sm.cnt[2][3];
+        if (tid == 0) {
+          // this pair's stats (kept token pairs: the last key block has nlast tokens)
+          const int jl = Nk - 1;
+          const bool lastA = (sm.kbits[gA][jl >> 5] >> (jl & 31)) & 1u;
+          const bool lastB = hasB && ((sm.kbits[gA + 1][jl >> 5] >> (jl & 31)) & 1u);
+          const unsigned long long tokA = (unsigned long long)nkA * kBlk - (lastA ? kBlk - nlast : 0);
+          const unsigned long long tokB = (unsigned long long)nkB * kBlk - (lastB ? kBlk - nlast : 0);
+          sm.st64[0] += (unsigned long long)(nkA + (hasB ? nkB : 0));
+          sm.st64[1] += (unsigned long long)Nk * (hasB ? 2 : 1);
+          sm.st64[2] += tokA * (unsigned long long)nA + (hasB ? tokB * (unsigned long long)nB : 0ull);
+          sm.st32[0] = min(sm.st32[0], hasB ? (unsigned)min(nkA, nkB) : (unsigned)nkA);
+          sm.st32[1] = max(sm.st32[1], hasB ? (unsigned)max(nkA, nkB) : (unsigned)nkA);
+        }
+        __syncthreads();  // the list is complete
       }
 
       // ---- 3. exact attention over the union list (online softmax, base 2) ----
@@ -1079,22 +1103,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         }
       }
 
-      if (tid == 0) {
-        const unsigned long long tokA = (unsigned long long)nkA * kBlk - (sm.lastkept[0] ? kBlk - nlast : 0);
-        st_pairs += tokA * (unsigned long long)nA;
-        st_kept += nkA;
-        st_tot += Nk;
-        st_min = min(st_min, (unsigned)nkA);
-        st_max = max(st_max, (unsigned)nkA);
-        if (hasB) {
-          const unsigned long long tokB = (unsigned long long)nkB * kBlk - (sm.lastkept[1] ? kBlk - nlast : 0);
-          st_pairs += tokB * (unsigned long long)nB;
-          st_kept += nkB;
-          st_tot += Nk;
-          st_min = min(st_min, (unsigned)nkB);
-          st_max = max(st_max, (unsigned)nkB);
-        }
-      }
       lds_barrier();  // LDS is rewritten by the next pair or item (output stores may still be in flight)
     }
   }
@@ -1105,12 +1113,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   // next call on this workspace.
   if (tid == 0) {
     unsigned long long* acc64 = reinterpret_cast<unsigned long long*>(p.hdr);
-    if (p.stats != nullptr && st_tot != 0) {
-      atomicAdd(acc64 + kHdrKept / 2, st_kept);
-      atomicAdd(acc64 + kHdrTotal / 2, st_tot);
-      atomicAdd(acc64 + kHdrPairs / 2, st_pairs);
-      atomicMin(p.hdr + kHdrMin, st_min);
-      atomicMax(p.hdr + kHdrMax, st_max);
+    if (p.stats != nullptr && sm.st64[1] != 0) {
+      atomicAdd(acc64 + kHdrKept / 2, sm.st64[0]);
+      atomicAdd(acc64 + kHdrTotal / 2, sm.st64[1]);
+      atomicAdd(acc64 + kHdrPairs / 2, sm.st64[2]);
+      atomicMin(p.hdr + kHdrMin, sm.st32[0]);
+      atomicMax(p.hdr + kHdrMax, sm.st32[1]);
     }
     __threadfence();
     const unsigned done = atomicAdd(p.hdr + kHdrDone, 1u);
