@@ -174,22 +174,26 @@ def main():
         return elapsed(ev)
 
     def split_calls(rn, qq, kk, vv, oo, tau, n):
-        """The call's kernels timed one by one: the pool pass (k, v), the
-        planning kernels (item costs, queue order), then the fused kernel alone
-        in the planned order (HIP events on the stream it runs on)."""
-        ev1, ev2, ev3 = events(n), events(n), events(n)
-        for (a, b), (c, e), (f, g) in zip(ev1, ev2, ev3):
+        """The call's stages timed one by one: the pool pass of k and v, the
+        forward's pre-pass (pooled queries, routing planes), the planning
+        kernels (item costs, queue order), then the fused kernel alone in the
+        planned order (HIP events on the stream it runs on)."""
+        ev1, ev2, ev3, ev4 = events(n), events(n), events(n), events(n)
+        for (a, b), (c, e), (f, g), (h, i) in zip(ev1, ev2, ev3, ev4):
             a.record(stream)
             sa.pool(kk, vv, kpool=rn.kpool, vmean=rn.vmean)
             b.record(stream)
             c.record(stream)
-            rn.plan(qq, tau)
+            rn.prepare(qq)
             e.record(stream)
             f.record(stream)
-            rn(qq, kk, vv, tau, out=oo, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+            rn.plan(qq, tau)
             g.record(stream)
+            h.record(stream)
+            rn(qq, kk, vv, tau, out=oo, flags=sa.SOL_F_POOLED | sa.SOL_F_PREPARED | sa.SOL_F_PLANNED)
+            i.record(stream)
         torch.cuda.synchronize()
-        return elapsed(ev1), elapsed(ev2), elapsed(ev3)
+        return elapsed(ev1), elapsed(ev2), elapsed(ev3), elapsed(ev4)
 
     def kv_unique_tokens(rn, qq, kk, vv, oo, tau, w):
         """Tokens of the key blocks kept by at least one query block of their
@@ -219,13 +223,13 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         r["call_flushed"] = elapsed(ev)
-        r["pool"], r["plan"], r["fwd"] = split_calls(runner, q, k, v, out, tau, steps)
+        r["pool"], r["prepare"], r["plan"], r["fwd"] = split_calls(runner, q, k, v, out, tau, steps)
         stats = runner.read_stats()
         n = max(3, steps // 2)
         # the fused kernel with its items in sequence (the identity order)
         runner.plan(q, math.inf)
         r["fwd_sequence_order"] = timed_calls(
-            lambda: runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED), n)
+            lambda: runner(q, k, v, tau, out=out, flags=sa.SOL_F_POOLED | sa.SOL_F_PREPARED | sa.SOL_F_PLANNED), n)
         # the whole call with the token-to-block (per-row) correction
         r["call_row_correction"] = timed_calls(lambda: runner(q, k, v, tau, out=out, flags=sa.SOL_F_ROW_CORRECTION), n)
         # the whole call with the output stored as bf16 (SOL_F_OUT_BF16)
@@ -241,7 +245,7 @@ def main():
         steps = args.steps if tau == args.tau else max(3, args.steps // 2)
         r, wall, stats = measure(tau, steps, args.warmup if tau == args.tau else 2)
         ms_call = float(np.mean(r["call"]))
-        ms_pool, ms_plan, ms_fwd = (float(np.median(r[x_])) for x_ in ("pool", "plan", "fwd"))
+        ms_pool, ms_prep, ms_plan, ms_fwd = (float(np.median(r[x_])) for x_ in ("pool", "prepare", "plan", "fwd"))
         kv_tokens, _ = kv_unique_tokens(runner, q, k, v, out, tau, wl)
         rl = fwd_roofline(B, H, N, d, wl.Nk, stats, kv_tokens, ms_fwd)
         kept_pct = 100.0 * stats["kept_blocks"] / stats["total_blocks"]
@@ -250,6 +254,7 @@ def main():
             "call_ms": pct(r["call"]),
             "call_ms_l2_mall_flushed": pct(r["call_flushed"]),
             "ms_pool": round(ms_pool, 4),
+            "ms_prepare": round(ms_prep, 4),
             "ms_fwd": round(ms_fwd, 4),
             "fwd_ms": pct(r["fwd"]),
             "ms_plan": round(ms_plan, 4),
@@ -394,7 +399,7 @@ def main():
                     rw(qw, kw, vw, tau, out=ow)
                 torch.cuda.synchronize()
                 call = timed_calls(lambda: rw(qw, kw, vw, tau, out=ow), args.workload_steps)
-                _, _, fwd = split_calls(rw, qw, kw, vw, ow, tau, args.workload_steps)
+                _, _, _, fwd = split_calls(rw, qw, kw, vw, ow, tau, args.workload_steps)
                 st = rw.read_stats()
                 kv_tok, _ = kv_unique_tokens(rw, qw, kw, vw, ow, tau, w)
                 ms_c, ms_f = float(np.mean(call)), float(np.median(fwd))
@@ -462,13 +467,15 @@ def main():
         "ms_per_call": round(ms_call, 4),
         "kept_block_pct": round(kept_pct, 3),
         "ms_pool": round(ms_pool, 4),
+        "ms_prepare": round(per_tau[tau_key(args.tau)]["ms_prepare"], 4),
         "ms_plan": round(per_tau[tau_key(args.tau)]["ms_plan"], 4),
         "ms_fwd": round(ms_fwd, 4),
         "pool_gbs": per_tau[tau_key(args.tau)]["pool_gbs"],
         "device_copy_gbs": round(copy_gbs, 1),
         "roofline": {
-            "kernel": "fwd_kernel<128> (fused routing + kept MFMA + correction); HIP events around the "
-                      "fused launch alone (planned workspace)",
+            "kernel": "fwd_kernel<128, G> (fused routing + kept MFMA + correction; G query blocks per work item, "
+                      "chosen by the library); HIP events around the fused launch alone (prepared and planned "
+                      "workspace)",
             "bound": rl["bound"],
             "achieved": round(achieved, 1),
             "peak": peak,

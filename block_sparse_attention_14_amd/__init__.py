@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     SOL_F_OUT_BF16,
     SOL_F_PLANNED,
     SOL_F_POOLED,
+    SOL_F_PREPARED,
     SOL_F_ROW_CORRECTION,
     SOL_OK,
     SOL_ROUTE_GAUSS,

@@ -22,6 +22,7 @@ SOL_F_OUT_BF16 = 1 << 4
 SOL_F_GROUP2 = 1 << 5
 SOL_F_GROUP4 = 2 << 5
 SOL_F_GROUP8 = 3 << 5
+SOL_F_PREPARED = 1 << 7
 
 SOL_ROUTE_ROWMAX = 0
 SOL_ROUTE_GAUSS = 1
@@ -34,6 +35,7 @@ EXPORTS = (
     "sol_attn_workspace_bytes",
     "sol_attn_pool",
     "sol_attn_plan",
+    "sol_attn_prepare",
     "sol_attn_forward",
     "sol_attn_forward_ex",
     "sol_attn_forward_debug",
@@ -99,6 +101,9 @@ def lib() -> ctypes.CDLL:
                 L.sol_attn_pool.restype = _i
                 L.sol_attn_plan.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp, ctypes.c_size_t, _vp]
                 L.sol_attn_plan.restype = _i
+                L.sol_attn_prepare.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_uint, _vp,
+                                               ctypes.c_size_t, _vp]
+                L.sol_attn_prepare.restype = _i
                 L.sol_attn_forward.argtypes = _fwd_args
                 L.sol_attn_forward.restype = _i
                 L.sol_attn_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,

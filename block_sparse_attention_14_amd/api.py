@@ -15,7 +15,7 @@ import torch
 
 from . import _lib
 from ._lib import (SOL_F_EXACT_ONLY, SOL_F_GROUP2, SOL_F_GROUP4, SOL_F_GROUP8, SOL_F_OUT_BF16,  # noqa: F401
-                   SOL_F_PLANNED, SOL_F_POOLED, SOL_F_ROW_CORRECTION, check, lib)
+                   SOL_F_PLANNED, SOL_F_POOLED, SOL_F_PREPARED, SOL_F_ROW_CORRECTION, check, lib)
 
 STATS_WORDS = 4  # sol_attn_stats is 32 bytes
 
@@ -195,6 +195,16 @@ class SolAttention:
                                  ctypes.c_float(float(tau)), _ptr(self.workspace), self.workspace.numel() * 8,
                                  _stream(self.device))
         check(rc, "sol_attn_plan")
+
+    def prepare(self, q: torch.Tensor, flags: int = 0) -> None:
+        """The forward's pre-pass (pooled queries, routing planes of self.kpool
+        and self.vmean) into the workspace, for forwards with SOL_F_PREPARED;
+        flags: 0 or SOL_F_ROW_CORRECTION."""
+        _check_qkv("q", q, (self.B, self.H, self.N, self.d))
+        rc = lib().sol_attn_prepare(_ptr(q), _ptr(self.kpool), _ptr(self.vmean), self.B, self.H, self.N, self.d,
+                                    self.Bq, self.Bk, ctypes.c_uint(int(flags)), _ptr(self.workspace),
+                                    self.workspace.numel() * 8, _stream(self.device))
+        check(rc, "sol_attn_prepare")
 
     def read_stats(self) -> Dict[str, int]:
         return read_stats(self.stats)

@@ -206,7 +206,7 @@ int check_args(const void* q, const void* k, const void* v, const void* out, int
     return SOL_EINVAL;
   if (check_route(route, N, Bk) != SOL_OK) return SOL_EINVAL;
   if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION | SOL_F_OUT_BF16 |
-                          SOL_F_GROUP_MASK))
+                          SOL_F_GROUP_MASK | SOL_F_PREPARED))
     return SOL_EINVAL;
   // a plan orders the items of the automatic group size
   if ((flags & SOL_F_PLANNED) && (flags & SOL_F_GROUP_MASK)) return SOL_EINVAL;
@@ -214,7 +214,7 @@ int check_args(const void* q, const void* k, const void* v, const void* out, int
   // exact-only under a Gaussian threshold: a query block whose threshold lies
   // above its best block would keep nothing, and its rows would have no terms
   if ((flags & SOL_F_EXACT_ONLY) && route.rule != SOL_ROUTE_ROWMAX && route.sink_count == 0) return SOL_EINVAL;
-  if ((flags & SOL_F_PLANNED) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
+  if ((flags & (SOL_F_PLANNED | SOL_F_PREPARED)) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
   const int rc = check_sizes(B, H, N, d, Bq, Bk);
   if (rc != SOL_OK) return rc;
   // eight query blocks per item only up to kMaxKeyBlocksG8 key blocks
@@ -232,6 +232,41 @@ int check_forward(const void* q, const void* k, const void* v, const void* out, 
   if (rc != SOL_OK) return rc;
   if (ws_bytes < sol_attn_workspace_bytes(B, H, N, d, Bq, Bk)) return SOL_EWORKSPACE;
   return SOL_OK;
+}
+
+// The pooling pre-pass of a forward: the pooled queries always (the routing
+// pass reads them), the pooled keys and values when k16 and v16 are given
+// (else the caller's kpool and vmean are read), and from those means the
+// routing pass's bf16 operand planes (and, for the per-row correction, its
+// row-major bf16 pooled values); it resets the header words when hdr is set.
+hipError_t prepass(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16, float* kpool, float* vmean,
+                   int BH, int N, int d, bool row_corr, unsigned char* wsb, unsigned* hdr, hipStream_t s) {
+  const WsLayout w = ws_layout(BH, N, d);
+  const int Nk = (N + 63) / 64;
+  sol::PoolSet set;
+  set.planes.kh = reinterpret_cast<uint16_t*>(wsb + w.kh);
+  set.planes.km = reinterpret_cast<uint16_t*>(wsb + w.km);
+  set.planes.kl = reinterpret_cast<uint16_t*>(wsb + w.kl);
+  set.planes.vt = reinterpret_cast<uint16_t*>(wsb + w.vt);
+  set.planes.vrow = row_corr ? reinterpret_cast<uint16_t*>(wsb + w.vbar16) : nullptr;
+  set.planes.kpool = kpool;
+  set.planes.vmean = vmean;
+  set.planes.Nkp = padded_blocks(Nk);
+  set.src[0] = q16;
+  set.dst[0] = reinterpret_cast<float*>(wsb + w.qpool);
+  set.n = 1;
+  if (k16 == nullptr) {
+    set.role[0] = sol::kRoleKeysFromPool | sol::kRoleValuesFromPool;
+  } else {
+    set.src[1] = k16;
+    set.dst[1] = kpool;
+    set.role[1] = sol::kRoleKeys;
+    set.src[2] = v16;
+    set.dst[2] = vmean;
+    set.role[2] = sol::kRoleValues;
+    set.n = 3;
+  }
+  return sol::launch_pool(set, BH, N, Nk, d, hdr, s);
 }
 
 int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
@@ -252,11 +287,9 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
 
   const unsigned* perm = nullptr;
   hipError_t e = hipSuccess;
-  // the pooling pre-pass: the pooled queries always (the routing pass reads
-  // them), the pooled keys and values unless the caller pooled them; it also
-  // resets the header words, except where a plan left them
-  // The same pass writes the routing pass's bf16 operand planes (and the
-  // per-row correction's pooled values), from its own means or the caller's.
+  // the pooling pre-pass (unless the workspace holds it already); the header
+  // words are reset by it or, after sol_attn_prepare, by a reset kernel,
+  // except where a plan left them clean
   float* qpool = reinterpret_cast<float*>(wsb + w.qpool);
   uint16_t* kh = reinterpret_cast<uint16_t*>(wsb + w.kh);
   uint16_t* km = reinterpret_cast<uint16_t*>(wsb + w.km);
@@ -264,33 +297,15 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   uint16_t* vt = reinterpret_cast<uint16_t*>(wsb + w.vt);
   uint16_t* vbar16 = reinterpret_cast<uint16_t*>(wsb + w.vbar16);
   const int Nkp = padded_blocks(Nk);
-  {
-    sol::PoolSet set;
-    set.planes.kh = kh;
-    set.planes.km = km;
-    set.planes.kl = kl;
-    set.planes.vt = vt;
-    set.planes.vrow = (flags & SOL_F_ROW_CORRECTION) ? vbar16 : nullptr;
-    set.planes.kpool = kpool;
-    set.planes.vmean = vmean;
-    set.planes.Nkp = Nkp;
-    set.src[0] = q16;
-    set.dst[0] = qpool;
-    set.n = 1;
-    if (flags & SOL_F_POOLED) {
-      set.role[0] = sol::kRoleKeysFromPool | sol::kRoleValuesFromPool;
-    } else {
-      set.src[1] = k16;
-      set.dst[1] = kpool;
-      set.role[1] = sol::kRoleKeys;
-      set.src[2] = v16;
-      set.dst[2] = vmean;
-      set.role[2] = sol::kRoleValues;
-      set.n = 3;
-    }
-    e = sol::launch_pool(set, BH, N, Nk, d, (flags & SOL_F_PLANNED) ? nullptr : static_cast<unsigned*>(ws), s);
-    if (e != hipSuccess) return SOL_EHIP;
+  unsigned* hdr = (flags & SOL_F_PLANNED) ? nullptr : static_cast<unsigned*>(ws);
+  if (flags & SOL_F_PREPARED) {
+    if (hdr) e = sol::launch_reset(hdr, s);
+  } else {
+    const bool pooled = flags & SOL_F_POOLED;
+    e = prepass(q16, pooled ? nullptr : k16, pooled ? nullptr : v16, kpool, vmean, BH, N, d,
+                flags & SOL_F_ROW_CORRECTION, wsb, hdr, s);
   }
+  if (e != hipSuccess) return SOL_EHIP;
   if (flags & SOL_F_PLANNED) {
     // the workspace holds a valid order from sol_attn_plan(), as a previous call left it
     perm = reinterpret_cast<const unsigned*>(wsb + w.perm);
@@ -526,6 +541,20 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
   return e == hipSuccess ? SOL_OK : SOL_EHIP;
 }
 
+int sol_attn_prepare(const void* q, const float* kpool, const float* vmean, int B, int H, int N, int d, int Bq,
+                     int Bk, unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kpool || !vmean || !workspace) return SOL_EINVAL;
+  if (!aligned(q, 16) || !aligned(kpool, 16) || !aligned(vmean, 16) || !aligned(workspace, 256)) return SOL_EINVAL;
+  if (flags & ~(unsigned)SOL_F_ROW_CORRECTION) return SOL_EINVAL;
+  const int rc = check_sizes(B, H, N, d, Bq, Bk);
+  if (rc != SOL_OK) return rc;
+  if (workspace_bytes < sol_attn_workspace_bytes(B, H, N, d, Bq, Bk)) return SOL_EWORKSPACE;
+  const hipError_t e = prepass(static_cast<const uint16_t*>(q), nullptr, nullptr, const_cast<float*>(kpool),
+                               const_cast<float*>(vmean), B * H, N, d, flags & SOL_F_ROW_CORRECTION,
+                               static_cast<unsigned char*>(workspace), nullptr, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SOL_OK : SOL_EHIP;
+}
+
 int sol_attn_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int d,
                      int Bq, int Bk, float tau, unsigned flags, sol_attn_stats* stats, float* kpool,
                      float* vmean, void* workspace, size_t workspace_bytes, void* stream) {
@@ -559,7 +588,7 @@ int sol_attn_forward_noalloc(const void* q, const void* k, const void* v, void* 
   if (kept_bitmap && !aligned(kept_bitmap, 4)) return SOL_EINVAL;
   // the pooled buffers and the plan live in the shared scratch array, which
   // the previous call on this GPU may have overwritten: always pool afresh
-  if (flags & (SOL_F_POOLED | SOL_F_PLANNED)) return SOL_EINVAL;
+  if (flags & (SOL_F_POOLED | SOL_F_PLANNED | SOL_F_PREPARED)) return SOL_EINVAL;
   const int rc = check_args(q, k, v, out, B, H, N, d, Bq, Bk, *route, flags, stats);
   if (rc != SOL_OK) return rc;
   // scratch layout: [workspace | kpool | vmean], each 256-byte aligned

@@ -92,7 +92,7 @@ enum {
   /* Bits 5-6: query blocks per work item of the fused kernel; the group's
    * routing pass reads the head's pooled keys and values once for all of
    * them. 0 (the default): chosen by the library (8 when the call has at
-   * least 16 such items per CU and at most 2048 key blocks, else 4 under the
+   * least 6 such items per CU and at most 2048 key blocks, else 4 under the
    * same item rule, else 2). SOL_F_GROUP2 / 4 / 8 ask for a size; 8 needs
    * ceil(N/64) <= 2048 (SOL_EUNSUPPORTED otherwise) and none combines with
    * SOL_F_PLANNED (SOL_EINVAL). The size only schedules work: results agree
@@ -100,7 +100,11 @@ enum {
    * are bitwise reproducible for a given size. */
   SOL_F_GROUP2 = 1u << 5,
   SOL_F_GROUP4 = 2u << 5,
-  SOL_F_GROUP8 = 3u << 5
+  SOL_F_GROUP8 = 3u << 5,
+  /* The workspace holds sol_attn_prepare() of these q, kpool and vmean (with
+   * the same SOL_F_ROW_CORRECTION bit): skip the pre-pass. Requires
+   * SOL_F_POOLED. With SOL_F_PLANNED only the fused kernel is launched. */
+  SOL_F_PREPARED = 1u << 7
 };
 #define SOL_F_GROUP_SHIFT 5
 #define SOL_F_GROUP_MASK (3u << SOL_F_GROUP_SHIFT)
@@ -191,6 +195,24 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The forward's pre-pass on its own, for forwards with SOL_F_PREPARED (so that
+ * a caller or a benchmark can launch and time the fused kernel alone): pools
+ * q (fp32 [B][H][Nq][d] in the workspace) and writes the routing pass's bf16
+ * operand planes of kpool and vmean into the workspace (section "pooling
+ * pre-pass" of the forward below), one launch.
+ *   q          bf16 [B][H][N][d]
+ *   kpool, vmean  fp32 [B][H][Nk][d], sol_attn_pool() of k and v
+ *   flags      0 or SOL_F_ROW_CORRECTION (also writes the row-major bf16
+ *              pooled values that mode reads)
+ *   workspace  as for sol_attn_forward; only its prepared regions are
+ *              written (the queue words and any plan are left as they are)
+ * Errors: SOL_EINVAL for null or misaligned pointers or other flags, those
+ * of the sizes as for sol_attn_forward, SOL_EWORKSPACE, SOL_EHIP.
+ */
+int sol_attn_prepare(const void* q, const float* kpool, const float* vmean, int B, int H, int N, int d, int Bq,
+                     int Bk, unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Sparse attention forward with proxy correction (all sections cited above).
  *   q, k, v   bf16 [B][H][N][d] (read)
  *   out       fp32 [B][H][N][d] (written), or bf16 with SOL_F_OUT_BF16
@@ -203,20 +225,22 @@ int sol_attn_plan(const void* q, const float* kpool, int B, int H, int N, int d,
  *             256-byte aligned; its content on entry does not matter unless
  *             SOL_F_PLANNED is set. Every forward leaves its queue and stats
  *             words clean.
- * Launches the pooling pass of k and v (unless SOL_F_POOLED, which launches
- * a one-workgroup reset of the workspace words instead), the planning kernels
- * of sol_attn_plan where the order repays them (row-max rule with
+ * Launches the pooling pre-pass (means of q, and of k and v unless
+ * SOL_F_POOLED; the routing pass's bf16 operand planes of the pooled keys and
+ * values; a reset of the workspace words unless SOL_F_PLANNED), the planning
+ * kernels of sol_attn_plan where the order repays them (row-max rule with
  * 8 <= tau < +inf, where the per-block budgets spread widest, at most 4096
  * items and at least 2^21 query-block x key-block pairs in the call) and one
- * fused kernel;
- * with SOL_F_PLANNED only the fused kernel. The fused kernel's persistent
- * grid takes pairs of query blocks from eight atomic queues (one per XCD,
- * each over a contiguous range of items, stealing from the others once
- * drained); for each it pools the two query blocks, computes their proxy
- * rows on chip, routes, runs bf16 MFMA attention over the kept key blocks
- * with an online softmax, and folds the skipped blocks' correction into the
- * same accumulator. Two calls that share a workspace must not overlap in
- * time.
+ * fused kernel; with SOL_F_PLANNED no planning kernel, with SOL_F_PREPARED
+ * no pre-pass (then a one-workgroup reset unless SOL_F_PLANNED). The fused
+ * kernel's persistent grid takes groups of query blocks from eight atomic
+ * queues (one per XCD, each over a contiguous range of items, stealing from
+ * the others once drained); for each it routes the group in one pass over
+ * the pooled keys and values on the matrix cores (scores consumed as they
+ * are produced), then, pair by pair, runs bf16 MFMA attention over the kept
+ * key blocks with an online softmax and folds the skipped blocks' correction
+ * into the same accumulator. Two calls that share a workspace must not
+ * overlap in time.
  */
 int sol_attn_forward(const void* q, const void* k, const void* v, void* out,
                      int B, int H, int N, int d, int Bq, int Bk, float tau,

@@ -110,6 +110,30 @@ def test_plan_rejects_before_launch(args, code):
     assert sa.lib().sol_attn_plan(*a) == code
 
 
+@pytest.mark.parametrize("args,code", [
+    ((None, P, P, 1, 2, 1000, 128, 64, 64, 0, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, None, P, 1, 2, 1000, 128, 64, 64, 0, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, None, 1, 2, 1000, 128, 64, 64, 0, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, P, 1, 2, 1000, 128, 64, 64, 0, None, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, P + 4, 1, 2, 1000, 128, 64, 64, 0, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, P, 1, 2, 1000, 128, 64, 64, 0, P + 64, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, P, 1, 2, 1000, 128, 64, 64, sa.SOL_F_POOLED, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, P, 0, 2, 1000, 128, 64, 64, 0, P, 1 << 30, None), sa.SOL_EINVAL),
+    ((P, P, P, 1, 2, 1000, 96, 64, 64, 0, P, 1 << 30, None), sa.SOL_EUNSUPPORTED),
+    ((P, P, P, 1, 2, 1000, 128, 64, 64, 0, P, 64, None), sa.SOL_EWORKSPACE),
+])
+def test_prepare_rejects_before_launch(args, code):
+    a = list(args)
+    a[9] = ctypes.c_uint(a[9])
+    assert sa.lib().sol_attn_prepare(*a) == code
+
+
+def test_prepared_forward_needs_pooled_inputs():
+    # SOL_F_PREPARED reads the caller's pooled tensors' planes: only with SOL_F_POOLED
+    assert fwd(flags=sa.SOL_F_PREPARED) == sa.SOL_EINVAL
+    assert fwd(flags=sa.SOL_F_PREPARED | sa.SOL_F_PLANNED) == sa.SOL_EINVAL
+
+
 def test_debug_requires_bitmap():
     L = sa.lib()
     rc = L.sol_attn_forward_debug(P, P, P, P, 1, 2, 1000, 128, 64, 64, ctypes.c_float(2.0), ctypes.c_uint(0),
@@ -243,6 +267,7 @@ def fwd_noalloc(route=(0, 2.0, 0.0, 0, 0), bitmap=None, **over):
     ((0, 2.0, 0.0, 0, 0), dict(out=P + 4), sa.SOL_EINVAL),
     ((0, 2.0, 0.0, 0, 0), dict(flags=sa.SOL_F_POOLED), sa.SOL_EINVAL),
     ((0, 2.0, 0.0, 0, 0), dict(flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED), sa.SOL_EINVAL),
+    ((0, 2.0, 0.0, 0, 0), dict(flags=sa.SOL_F_POOLED | sa.SOL_F_PREPARED), sa.SOL_EINVAL),
     ((1, 0.0, 1.0, 0, 0), dict(flags=sa.SOL_F_EXACT_ONLY), sa.SOL_EINVAL),
     ((0, 2.0, 0.0, 0, 0), dict(d=96), sa.SOL_EUNSUPPORTED),
     # 64 heads of 118800 tokens need about 190 MiB of pooled buffers: beyond the array

@@ -432,6 +432,34 @@ def test_plan_then_planned_forwards_match_one_shot():
     assert torch.equal(out.view(torch.int32), dense_ref.view(torch.int32))
 
 
+def test_prepared_forwards_match_one_shot():
+    """sol_attn_pool + sol_attn_prepare (+ sol_attn_plan) + forward with
+    SOL_F_PREPARED launches only the fused kernel (and a reset when unplanned)
+    and equals the one-shot forward bit for bit, also with the per-row
+    correction; stats are right on every call."""
+    wl = get_workload("image_dit_4k")
+    x = make_inputs(wl)
+    q, k, v = (to_device_bf16(x[n]) for n in "qkv")
+    one = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    sa.pool(k, v, kpool=r.kpool, vmean=r.vmean)
+    for extra in (0, sa.SOL_F_ROW_CORRECTION):
+        ref = one(q, k, v, 8.0, flags=extra).clone()
+        ref_stats = one.read_stats()
+        r.prepare(q, flags=extra)
+        for planned in (False, True, True):
+            flags = sa.SOL_F_POOLED | sa.SOL_F_PREPARED | extra
+            if planned:
+                r.plan(q, 8.0)
+                flags |= sa.SOL_F_PLANNED
+            out = r(q, k, v, 8.0, flags=flags)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), (extra, planned)
+            assert r.read_stats() == ref_stats
+    print(f"[prepared] image_dit_4k tau=8: prepared forwards identical to one-shot, kept {ref_stats['kept_blocks']}",
+          flush=True)
+
+
 def test_garbage_workspace_is_reset():
     wl = _custom(1000, 128, H=3, seed=21)
     x = make_inputs(wl)
