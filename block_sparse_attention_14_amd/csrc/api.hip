@@ -478,7 +478,9 @@ int sol_attn_mask_threshold(const void* q, const float* kpool, int B, int H, int
   p.Nq = Nq;
   p.Nk = Nq;
   p.nwords = (Nq + 31) / 32;
-  p.group = auto_group(BH, Nq);
+  // (at most four blocks per item: the routing-only kernel then fits four
+  // workgroups per CU without spilling)
+  p.group = std::min(auto_group(BH, Nq), 4);
   p.ngroups = (Nq + p.group - 1) / p.group;
   p.nitems = sol::forward_items(BH, Nq, p.group);
   p.route_only = 1;

@@ -216,13 +216,17 @@ __device__ __forceinline__ int chunk_at(int k, int cs, int nch) {
 }
 
 // RC: the per-row (token-to-block) correction replaces the block-level one.
-template <int D, int G, bool RC>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
+// RO: routing only (the threshold router): the kernel stops after each
+// group's routing pass and writes the kept bits; without the kept loop it
+// needs a fraction of the registers and LDS, so four workgroups share a CU.
+template <int D, int G, bool RC, bool RO>
+__global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) {
   using GM = Geom<D>;
   // Two separate LDS objects for the two stages, so that reads of one stage
   // never wait for copies still landing in the other.
-  __shared__ __attribute__((aligned(16))) unsigned char stA[GM::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char stB[GM::STAGE];
+  constexpr int kStA = RO ? G * D * 4 : GM::STAGE, kStB = RO ? 4 * G * D * 4 : GM::STAGE;
+  __shared__ __attribute__((aligned(16))) unsigned char stA[kStA];
+  __shared__ __attribute__((aligned(16))) unsigned char stB[kStB];
   __shared__ Small<D, G> sm;
   extern __shared__ __align__(16) unsigned char dyn[];
   uint16_t* ulist = reinterpret_cast<uint16_t*>(dyn);  // [Nk] union of kept lists: j | A<<14 | B<<15
@@ -231,8 +235,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   //   stA: qbar[G][D] pooled queries
   //   stB: [4][G][D] per-wave partial sums (pooled queries, Gaussian
   //        statistics, correction numerators)
-  static_assert(G * D * 4 <= GM::STAGE, "routing buffers exceed stage A");
-  static_assert(4 * G * D * 4 <= GM::STAGE, "routing buffers exceed stage B");
+  static_assert(G * D * 4 <= kStA, "routing buffers exceed stage A");
+  static_assert(4 * G * D * 4 <= kStB, "routing buffers exceed stage B");
   float* qbar = reinterpret_cast<float*>(stA);
   float* part = reinterpret_cast<float*>(stB);  // [4 waves][G][D]
 
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   const float csc = p.scale_log2;
   const bool rowmax = p.rule == SOL_ROUTE_ROWMAX;
   // block-level correction sums are formed (not in the per-row or exact-only modes)
-  const bool corr = !RC && !p.exact_only;
+  const bool corr = !RC && !RO && !p.exact_only;
   // per-row correction: log2(n_j) of a full and of the ragged last key block
   // in raw dot-product units, formed once (per element they would become a
   // branch around a division)
@@ -706,13 +710,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         if (g0 + g < Nq) p.bitmap[((size_t)bh * Nq + g0 + g) * p.nwords + w] = sm.kbits[g][w];
       }
     }
-    if (p.route_only) {
+    if constexpr (RO) {
       if (p.static_grid) break;
       __syncthreads();
       if (tid == 0) sm.item = item_of(take(ticket()));
       __syncthreads();
       continue;
-    }
+    } else {
 
     // ---- the pairs of the group: Q tiles, union list, kept loop, fold ----
     for (int pr = 0; pr < G / 2; ++pr) {
@@ -1105,6 +1109,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 
       lds_barrier();  // LDS is rewritten by the next pair or item (output stores may still be in flight)
     }
+    }  // !RO
   }
   if (p.static_grid) return;
 
@@ -1148,7 +1153,7 @@ int forward_items(int BH, int Nq, int G) { return BH * ((Nq + G - 1) / G); }
 
 int forward_max_group(int Nk) { return Nk <= kMaxKeyBlocksG8 ? 8 : 4; }
 
-template <int D, int G, bool RC>
+template <int D, int G, bool RC, bool RO>
 static hipError_t launch_dg(const FwdParams& p, hipStream_t stream) {
   // per-device CU count and occupancy (bucketed by dynamic LDS in 4 KiB steps)
   static std::mutex mu;
@@ -1158,7 +1163,7 @@ static hipError_t launch_dg(const FwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  const size_t dyn = forward_dynamic_lds(p.Nk);
+  const size_t dyn = RO ? 0 : forward_dynamic_lds(p.Nk);
   const int bucket = (int)std::min<size_t>(7, dyn / 4096);
   int grid_per_cu = 0, ncu = 0;
   {
@@ -1167,14 +1172,14 @@ static hipError_t launch_dg(const FwdParams& p, hipStream_t stream) {
       int n = 0;
       e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<D, G, RC>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<D, G, RC, RO>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 32 * 1024);
       if (e != hipSuccess) return e;
       cus[dev] = n;
     }
     if (occ_cache[dev][bucket] == 0) {
       int occ = 0;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&fwd_kernel<D, G, RC>),
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&fwd_kernel<D, G, RC, RO>),
                                                        kThreads, (size_t)(bucket + 1) * 4096);
       if (e != hipSuccess) return e;
       occ_cache[dev][bucket] = occ < 1 ? 1 : occ;
@@ -1183,16 +1188,16 @@ static hipError_t launch_dg(const FwdParams& p, hipStream_t stream) {
     grid_per_cu = occ_cache[dev][bucket];
   }
   const int grid = p.static_grid ? p.nitems : (int)std::min<long long>((long long)ncu * grid_per_cu, p.nitems);
-  hipLaunchKernelGGL((fwd_kernel<D, G, RC>), dim3(grid), dim3(kThreads), dyn, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, G, RC, RO>), dim3(grid), dim3(kThreads), dyn, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool RC>
 static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   switch (p.group) {
-    case 8: return launch_dg<D, 8, RC>(p, stream);
-    case 4: return launch_dg<D, 4, RC>(p, stream);
-    default: return launch_dg<D, 2, RC>(p, stream);
+    case 8: return p.route_only ? launch_dg<D, 8, false, true>(p, stream) : launch_dg<D, 8, RC, false>(p, stream);
+    case 4: return p.route_only ? launch_dg<D, 4, false, true>(p, stream) : launch_dg<D, 4, RC, false>(p, stream);
+    default: return p.route_only ? launch_dg<D, 2, false, true>(p, stream) : launch_dg<D, 2, RC, false>(p, stream);
   }
 }
 
