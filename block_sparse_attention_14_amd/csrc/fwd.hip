@@ -312,6 +312,7 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
     // loads are issued before the pooled queries are formed
     constexpr int CT = D / 16;   // 16-column tiles of the pooled values
     constexpr int NQB = D / 32;  // k-steps of a score tile
+    constexpr bool kTwoCols = G > 5;  // the pooled queries' third part in a second product
     const int col = lane & 15, kq = lane >> 4;
     const int nst = (Nk + 15) / 16;
     const int cs = min(g0 / 16, nst - 1);
@@ -449,9 +450,9 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
     //   scores  S^T[j][col] = sum_p kbar_p[j] . B[col] (16x16x32), the pooled
     //           keys as three bf16 parts against the pooled queries as three
     //           parts in the columns of B, [qh | qm | ql] (G <= 4) or [qh | qm]
-    //           and [ql | 0] (G = 8, kh only, the products below 2^-24 left
-    //           out); a block's score is the sum of its columns, an fp32-grade
-    //           dot product;
+    //           and [ql | 0] (G = 6 or 8, kh only, the products below 2^-24
+    //           left out); a block's score is the sum of its columns, an
+    //           fp32-grade dot product;
     //   numerators cnum^T[c][col] = sum_j vbar^T[c][j] W[j][col] (16x16x16),
     //           the pooled values in bf16 against the weights of the skipped
     //           blocks in two parts, columns [wh | wl]. The score tile's result
@@ -474,10 +475,10 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
       // score B operands, from the pooled queries in LDS
       bf16x8 qB1[NQB], qB2[NQB];
       {
-        const int qp = G == 8 ? (col >> 3) : col / G;  // which part of the pooled query
-        const int g = G == 8 ? (col & 7) : col % G;
-        const bool on1 = G == 8 || col < 3 * G;
-        const bool on2 = G == 8 && col < 8;
+        const int qp = col / G;  // which part of the pooled query
+        const int g = col % G;
+        const bool on1 = col < (kTwoCols ? 2 : 3) * G;
+        const bool on2 = kTwoCols && col < G;
 #pragma unroll
         for (int ks = 0; ks < NQB; ++ks) {
           uint32_t w1[4], w2[4];
@@ -510,15 +511,16 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           s1 = mfma16x16x32(b.k[0][ks], qB1[ks], s1);
           s1 = mfma16x16x32(b.k[1][ks], qB1[ks], s1);
           s1 = mfma16x16x32(b.k[2][ks], qB1[ks], s1);
-          if (G == 8) s2 = mfma16x16x32(b.k[0][ks], qB2[ks], s2);
+          if (kTwoCols) s2 = mfma16x16x32(b.k[0][ks], qB2[ks], s2);
           load_ks(b, stn, ks);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // lane col g < G gathers its block's columns (g + G and g + 2G, or g + 8)
+          // lane col g < G gathers its block's columns (g + G and g + 2G, or
+          // g + G and column g of the second product)
           float v = s1[e];
-          if (G == 8)
-            v += __shfl_down(s1[e], 8, 16) + s2[e];
+          if (kTwoCols)
+            v += __shfl_down(s1[e], G, 16) + s2[e];
           else
             v += __shfl_down(s1[e], G, 16) + __shfl_down(s1[e], 2 * G, 16);
           sc[e] = gval && 16 * st + 4 * kq + e < Nk ? v * p.proxy_scale : -INFINITY;
