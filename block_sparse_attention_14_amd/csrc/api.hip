@@ -42,11 +42,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: [header words | item costs | item order | pooled-key copies and
-// statistics of the optional modes]. The cost and order slots are sized for
-// items of two query blocks, the most items any group size gives.
+// Workspace: [header words | the plan's item count | item costs | item order |
+// pooled-key copies and statistics of the optional modes]. The cost and order
+// slots are sized for items of two query blocks, the most items any group
+// size gives.
 struct WsLayout {
-  size_t cost, perm, qpool, kh, km, kl, vt, vbar16, kstats, kmom, total;
+  size_t plan, cost, perm, qpool, kh, km, kl, vt, vbar16, kstats, kmom, total;
 };
 
 // Key blocks per head in the tiled operand planes: Nk rounded up to 64 (the
@@ -59,7 +60,8 @@ WsLayout ws_layout(int BH, int N, int d) {
   const size_t plane = round_up((size_t)BH * Nq * (size_t)d * 2, 256);
   const size_t tplane = round_up((size_t)BH * (size_t)d * (size_t)padded_blocks((int)Nq) * 2, 256);
   WsLayout w;
-  w.cost = sol::kHdrWords * 4;
+  w.plan = round_up(sol::kHdrWords * 4, 256);
+  w.cost = w.plan + 256;
   w.perm = round_up(w.cost + 4 * items, 256);
   w.qpool = round_up(w.perm + 4 * items, 256);
   w.kh = round_up(w.qpool + (size_t)BH * Nq * (size_t)d * 4, 256);
@@ -75,11 +77,15 @@ WsLayout ws_layout(int BH, int N, int d) {
 
 // Query blocks per work item of the fused kernel. Larger groups read the
 // head's pooled keys and values once for more query blocks (the routing
-// pass's traffic falls as 1/G), smaller ones give the persistent grid more
-// items to balance; a group is taken only while the call keeps at least 16
-// items per CU (about eight per workgroup), and eight blocks only up to 2048
-// key blocks (their kept bits and kept list must fit the workgroup's LDS).
-// A flag may ask for a size; 0 there means this automatic choice.
+// pass's traffic falls as 1/G, and with 16 blocks every column of its score
+// tiles is a block), smaller ones give the persistent grid more items to
+// balance; a group is taken only while the call keeps at least 6 items per
+// CU (three per workgroup), and eight or sixteen blocks only up to 2048 key
+// blocks (their kept bits must fit the workgroup's LDS). Sixteen only where
+// the routing pass dominates the items: row-max routing with tau <= 4 (on the
+// 119K-token video layer: 12% faster at tau = 2, 3% at tau = 4, but 9%
+// slower at tau = 8, where larger items balance worse). A flag may ask for a
+// size; none there means this automatic choice.
 std::mutex cu_mu;
 int cu_count[64] = {0};
 
@@ -95,20 +101,26 @@ int device_cus() {
   return cu_count[dev];
 }
 
-int auto_group(int BH, int Nq) {
+constexpr float kGroup16MaxTau = 4.f;
+
+int auto_group(int BH, int Nq, const sol_attn_route& r) {
   const long long target = 6ll * device_cus();
+  if (r.rule == SOL_ROUTE_ROWMAX && r.tau <= kGroup16MaxTau && Nq <= sol::kMaxKeyBlocksG8 &&
+      (long long)sol::forward_items(BH, Nq, 16) >= target)
+    return 16;
   if (Nq <= sol::kMaxKeyBlocksG8 && (long long)sol::forward_items(BH, Nq, 8) >= target) return 8;
   if ((long long)sol::forward_items(BH, Nq, 4) >= target) return 4;
   return 2;
 }
 
 // The group size a flag field asks for (0: automatic), or 0 if unsupported.
-int group_of(unsigned flags, int BH, int Nq) {
+int group_of(unsigned flags, int BH, int Nq, const sol_attn_route& r) {
+  if (flags & SOL_F_GROUP16) return Nq <= sol::kMaxKeyBlocksG8 ? 16 : 0;
   switch ((flags & SOL_F_GROUP_MASK) >> SOL_F_GROUP_SHIFT) {
     case 1: return 2;
     case 2: return 4;
     case 3: return Nq <= sol::kMaxKeyBlocksG8 ? 8 : 0;
-    default: return auto_group(BH, Nq);
+    default: return auto_group(BH, Nq, r);
   }
 }
 
@@ -136,7 +148,7 @@ constexpr long long kPlanMinPairs = 1ll << 21;
 constexpr int kMaxGridHeads = 65535;
 
 bool plan_by_default(const sol_attn_route& r, int BH, int Nq, int nitems, int group) {
-  return group == auto_group(BH, Nq) && r.rule == SOL_ROUTE_ROWMAX && r.tau >= kPlanMinTau &&
+  return group == auto_group(BH, Nq, r) && r.rule == SOL_ROUTE_ROWMAX && r.tau >= kPlanMinTau &&
          use_order(r.tau, nitems) && nitems <= kPlanMaxItems && (long long)BH * Nq * Nq >= kPlanMinPairs &&
          BH <= kMaxGridHeads;
 }
@@ -173,13 +185,14 @@ hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   const int Nq = (N + 63) / 64, Nk = Nq;
   unsigned* perm = reinterpret_cast<unsigned*>(wsb + w.perm);
-  const int group = auto_group(BH, Nq);
+  unsigned* plan_items = reinterpret_cast<unsigned*>(wsb + w.plan);
+  const int group = auto_group(BH, Nq, rowmax_route(tau));
   const int nitems = sol::forward_items(BH, Nq, group);
   *ordered = use_order(tau, nitems) && BH <= kMaxGridHeads;
   if (*ordered)
-    return sol::launch_plan(q, kpool, reinterpret_cast<unsigned*>(wsb + w.cost), perm, BH, N, Nq, Nk, d, tau,
-                            (float)(1.0 / sqrt((double)d)), group, s);
-  return sol::launch_identity_order(perm, nitems, s);
+    return sol::launch_plan(q, kpool, reinterpret_cast<unsigned*>(wsb + w.cost), perm, plan_items, BH, N, Nq, Nk,
+                            d, tau, (float)(1.0 / sqrt((double)d)), group, s);
+  return sol::launch_identity_order(perm, plan_items, nitems, s);
 }
 
 int check_route(const sol_attn_route& r, int N, int Bk) {
@@ -206,10 +219,11 @@ int check_args(const void* q, const void* k, const void* v, const void* out, int
     return SOL_EINVAL;
   if (check_route(route, N, Bk) != SOL_OK) return SOL_EINVAL;
   if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION | SOL_F_OUT_BF16 |
-                          SOL_F_GROUP_MASK | SOL_F_PREPARED))
+                          SOL_F_GROUP_MASK | SOL_F_GROUP16 | SOL_F_PREPARED))
     return SOL_EINVAL;
-  // a plan orders the items of the automatic group size
-  if ((flags & SOL_F_PLANNED) && (flags & SOL_F_GROUP_MASK)) return SOL_EINVAL;
+  // one group size at most; a plan orders the items of the automatic size
+  if ((flags & SOL_F_GROUP16) && (flags & SOL_F_GROUP_MASK)) return SOL_EINVAL;
+  if ((flags & SOL_F_PLANNED) && (flags & (SOL_F_GROUP_MASK | SOL_F_GROUP16))) return SOL_EINVAL;
   if ((flags & SOL_F_EXACT_ONLY) && (flags & SOL_F_ROW_CORRECTION)) return SOL_EINVAL;
   // exact-only under a Gaussian threshold: a query block whose threshold lies
   // above its best block would keep nothing, and its rows would have no terms
@@ -217,8 +231,9 @@ int check_args(const void* q, const void* k, const void* v, const void* out, int
   if ((flags & (SOL_F_PLANNED | SOL_F_PREPARED)) && !(flags & SOL_F_POOLED)) return SOL_EINVAL;
   const int rc = check_sizes(B, H, N, d, Bq, Bk);
   if (rc != SOL_OK) return rc;
-  // eight query blocks per item only up to kMaxKeyBlocksG8 key blocks
-  if (((flags & SOL_F_GROUP_MASK) >> SOL_F_GROUP_SHIFT) == 3 && (N + 63) / 64 > sol::kMaxKeyBlocksG8)
+  // eight or sixteen query blocks per item only up to kMaxKeyBlocksG8 key blocks
+  if ((((flags & SOL_F_GROUP_MASK) >> SOL_F_GROUP_SHIFT) == 3 || (flags & SOL_F_GROUP16)) &&
+      (N + 63) / 64 > sol::kMaxKeyBlocksG8)
     return SOL_EUNSUPPORTED;
   return SOL_OK;
 }
@@ -282,7 +297,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   const WsLayout w = ws_layout(BH, N, d);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
-  const int group = group_of(flags, BH, Nq);
+  const int group = group_of(flags, BH, Nq, route);
   const int nitems = sol::forward_items(BH, Nq, group);
 
   const unsigned* perm = nullptr;
@@ -338,6 +353,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   p.kpool = kpool;
   p.vmean = vmean;
   p.perm = perm;
+  p.plan_items = reinterpret_cast<const unsigned*>(wsb + w.plan);
   p.hdr = static_cast<unsigned*>(ws);
   p.stats = stats;
   p.bitmap = bitmap;
@@ -480,7 +496,7 @@ int sol_attn_mask_threshold(const void* q, const float* kpool, int B, int H, int
   p.nwords = (Nq + 31) / 32;
   // (at most four blocks per item: the routing-only kernel then fits four
   // workgroups per CU without spilling)
-  p.group = std::min(auto_group(BH, Nq), 4);
+  p.group = std::min(auto_group(BH, Nq, *route), 4);
   p.ngroups = (Nq + p.group - 1) / p.group;
   p.nitems = sol::forward_items(BH, Nq, p.group);
   p.route_only = 1;

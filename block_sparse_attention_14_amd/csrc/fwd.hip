@@ -16,7 +16,7 @@
 //                                    exact and the corrected terms
 //
 // Work decomposition. A work item is a GROUP of G consecutive 64-row query
-// blocks of one head (G = 2, 4 or 8, chosen by the host so that there are
+// blocks of one head (G = 2, 4, 8 or 16, chosen by the host so that there are
 // enough items to balance the grid). A persistent grid of 256-thread
 // workgroups (two per CU) takes items from atomic ticket counters: per-block
 // budgets differ by two orders of magnitude, so a static split would idle CUs.
@@ -27,34 +27,33 @@
 // map to its items through the planned order.
 //
 // Per item:
-//   A. the pooled queries of the G blocks, from their rows (buffer loads; rows
-//      past the sequence read as zero), and, for the Gaussian rules, each
-//      block's threshold from the head's pooled-key moments (known before any
-//      score exists);
-//   R. one streaming pass over the head's pooled keys and pooled values, in
-//      chunks of 256 key blocks, starting at the chunk of the group's own
-//      blocks and moving outwards. Per chunk:
-//        R1 the proxy scores of all G blocks: eight lanes per key block, each
-//           with 16 (d = 128) or 8 columns of every pooled query in
-//           registers; the eight partial dot products of a key block are
-//           reduced so that lane g of the eight ends with block g's score;
-//        R2 per block: the running row maximum, the threshold (running
-//           maximum - tau, or the fixed Gaussian one), keep or skip, the
-//           weight n_j e^{s - M} of each skipped block against the running
-//           maximum (earlier weights rescaled when it rises), kept bits;
-//        R3 the correction numerators sum_j w_j vbar_j of all G blocks
-//           (rescaled with the running maximum), each pooled value read once
-//           for the whole group;
+//   A. the pooled queries of the G blocks (made by the pooling pre-pass) and,
+//      for the Gaussian rules, each block's threshold from the head's
+//      pooled-key moments (known before any score exists);
+//   R. one streaming pass over the head's pooled keys and pooled values (bf16
+//      operand planes from the pre-pass: keys in three parts, values in one),
+//      in steps of 16 key blocks taken outwards from the group's own blocks;
+//      wave w takes steps w, w + 4, ... and streams on its own. Per step:
+//        the proxy scores of the G blocks as MFMA products (three-part keys
+//        against three-part queries: fp32-grade dot products);
+//        per block: the wave's running maximum, the threshold (running
+//        maximum - tau, after a first maximum over every wave's first step,
+//        or the fixed Gaussian one), keep or skip, the weight n_j e^{s - M}
+//        of each skipped block against the running maximum (earlier weights
+//        rescaled when it rises), kept bits into LDS;
+//        the correction numerators sum_j w_j vbar_j of the G blocks as MFMA
+//        products of the pooled values with the weights;
 //      so the group reads the pooled keys and values once: G/2 times less
 //      than pairs of blocks would, which is what long sequences need;
-//   R4. row-max rule only: a block kept against a running maximum that later
-//      rose by more than its margin is rechecked against the final maximum
-//      and, if below it, moved to the correction; the group's bits are final;
+//   R4. row-max rule only: the steps a wave routed before its maximum reached
+//      the row's are routed again against the row's maximum (a block kept
+//      against a lower one may move to the correction); the waves' partial
+//      sums merge under the row maximum; the group's bits are final;
 //   then for each PAIR of blocks of the group:
 //   1. both Q tiles through LDS into registers, the B operand of S^T = K Q^T
 //      (waves 0-1 own block A, waves 2-3 block B, 32 rows each);
-//   2. the union of the two kept lists (ascending, 2-bit owner mask) from the
-//      kept bits;
+//   2. the union of the two kept lists, walked in ascending order straight
+//      from the kept bits (wave-uniform scalar state, no stored list);
 //   3. for every union entry, the K and V tiles stream from HBM straight into
 //      LDS (buffer loads with an LDS destination, no registers involved),
 //      double-buffered in two stages, one barrier per tile. 16-byte chunks are
@@ -107,11 +106,11 @@ __device__ __forceinline__ float rowmax4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Words of kept bits per query block: groups of eight blocks are used up to
-// 2048 key blocks, smaller groups up to the longest supported head.
+// Words of kept bits per query block: groups of eight or sixteen blocks are
+// used up to 2048 key blocks, smaller groups up to the longest supported head.
 template <int G>
 constexpr int key_words() {
-  return G == 8 ? kMaxKeyBlocksG8 / 32 : (SOL_ATTN_MAX_N / kBlk) / 32;
+  return G >= 8 ? kMaxKeyBlocksG8 / 32 : (SOL_ATTN_MAX_N / kBlk) / 32;
 }
 
 // LDS geometry. A K or V tile is 64 rows of 2d bytes, stored unpadded with
@@ -198,7 +197,6 @@ struct alignas(16) Small {
   float wfin[4][16];                // per wave and column: the wave's final maximum
   float wden[4][16];                // per wave and column: the wave's correction denominator
   uint32_t kbits[G][key_words<G>()];  // kept-block bits
-  int cnt[3][4];
   unsigned long long st64[3];  // this workgroup's stats: kept blocks, total blocks, kept token pairs
   unsigned st32[2];            // fewest and most kept blocks of a query block
   int item;  // the item of the next iteration (-1: none left)
@@ -228,8 +226,6 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
   __shared__ __attribute__((aligned(16))) unsigned char stA[kStA];
   __shared__ __attribute__((aligned(16))) unsigned char stB[kStB];
   __shared__ Small<D, G> sm;
-  extern __shared__ __align__(16) unsigned char dyn[];
-  uint16_t* ulist = reinterpret_cast<uint16_t*>(dyn);  // [Nk] union of kept lists: j | A<<14 | B<<15
   constexpr int KW = key_words<G>();
   // routing buffers in the stages (before any pair's kept loop):
   //   stA: qbar[G][D] pooled queries
@@ -286,10 +282,14 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
     sm.st32[1] = 0u;
   }
 
-  // (an order entry out of range, possible only with a workspace that was
-  // never planned, ends this workgroup's work instead of being followed)
+  // A planned order is followed only if it was made for this many items (a
+  // plan made for another group size is ignored: the items then go in
+  // sequence). An order entry out of range, possible only with a workspace
+  // that was never planned, ends this workgroup's work instead of being
+  // followed.
+  const unsigned* perm = p.perm != nullptr && *p.plan_items == (unsigned)p.nitems ? p.perm : nullptr;
   auto item_of = [&](int rank) {
-    const unsigned it = rank < 0 ? ~0u : (p.perm ? p.perm[rank] : (unsigned)rank);
+    const unsigned it = rank < 0 ? ~0u : (perm ? perm[rank] : (unsigned)rank);
     return it < (unsigned)p.nitems ? (int)it : -1;
   };
   if (tid == 0) sm.item = p.static_grid ? (int)blockIdx.x : item_of(take(ticket()));
@@ -312,7 +312,11 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
     // loads are issued before the pooled queries are formed
     constexpr int CT = D / 16;   // 16-column tiles of the pooled values
     constexpr int NQB = D / 32;  // k-steps of a score tile
-    constexpr bool kTwoCols = G > 5;  // the pooled queries' third part in a second product
+    // G = 16: every column of a score tile is a block of the group, one
+    // product per part of the pooled queries; G = 6 or 8: the queries' third
+    // part in a second product; G <= 4: all three parts in one.
+    constexpr bool kFull = G == 16;
+    constexpr bool kTwoCols = G > 5 && !kFull;
     const int col = lane & 15, kq = lane >> 4;
     const int nst = (Nk + 15) / 16;
     const int cs = min(g0 / 16, nst - 1);
@@ -473,15 +477,15 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
     // move to the correction.
     {
       // score B operands, from the pooled queries in LDS
-      bf16x8 qB1[NQB], qB2[NQB];
+      bf16x8 qB1[NQB], qB2[NQB], qB3[kFull ? NQB : 1];
       {
-        const int qp = col / G;  // which part of the pooled query
-        const int g = col % G;
-        const bool on1 = col < (kTwoCols ? 2 : 3) * G;
-        const bool on2 = kTwoCols && col < G;
+        const int qp = kFull ? 0 : col / G;  // which part of the pooled query
+        const int g = kFull ? col : col % G;
+        const bool on1 = kFull || col < (kTwoCols ? 2 : 3) * G;
+        const bool on2 = kFull || (kTwoCols && col < G);
 #pragma unroll
         for (int ks = 0; ks < NQB; ++ks) {
-          uint32_t w1[4], w2[4];
+          uint32_t w1[4], w2[4], w3[4];
 #pragma unroll
           for (int i = 0; i < 8; i += 2) {
             float h[2], m[2], l[2];
@@ -495,10 +499,12 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
             }
             const float* pick = qp == 0 ? h : qp == 1 ? m : l;
             w1[i / 2] = on1 ? pack_bf16x2(pick[0], pick[1]) : 0u;
-            w2[i / 2] = on2 ? pack_bf16x2(l[0], l[1]) : 0u;
+            w2[i / 2] = on2 ? (kFull ? pack_bf16x2(m[0], m[1]) : pack_bf16x2(l[0], l[1])) : 0u;
+            w3[i / 2] = pack_bf16x2(l[0], l[1]);
           }
           qB1[ks] = as_bf16x8(make_uint4(w1[0], w1[1], w1[2], w1[3]));
           qB2[ks] = as_bf16x8(make_uint4(w2[0], w2[1], w2[2], w2[3]));
+          if constexpr (kFull) qB3[ks] = as_bf16x8(make_uint4(w3[0], w3[1], w3[2], w3[3]));
         }
       }
       // the step's scores of column col's block, key blocks 16 st + 4 kq + e;
@@ -511,15 +517,25 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           s1 = mfma16x16x32(b.k[0][ks], qB1[ks], s1);
           s1 = mfma16x16x32(b.k[1][ks], qB1[ks], s1);
           s1 = mfma16x16x32(b.k[2][ks], qB1[ks], s1);
-          if (kTwoCols) s2 = mfma16x16x32(b.k[0][ks], qB2[ks], s2);
+          if constexpr (kFull) {
+            s2 = mfma16x16x32(b.k[0][ks], qB2[ks], s2);
+            s2 = mfma16x16x32(b.k[1][ks], qB2[ks], s2);
+            s2 = mfma16x16x32(b.k[2][ks], qB2[ks], s2);
+            s2 = mfma16x16x32(b.k[0][ks], qB3[ks], s2);
+          } else if constexpr (kTwoCols) {
+            s2 = mfma16x16x32(b.k[0][ks], qB2[ks], s2);
+          }
           load_ks(b, stn, ks);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // lane col g < G gathers its block's columns (g + G and g + 2G, or
-          // g + G and column g of the second product)
+          // g + G and column g of the second product; with G = 16 the two
+          // products' own column)
           float v = s1[e];
-          if (kTwoCols)
+          if constexpr (kFull)
+            v += s2[e];
+          else if constexpr (kTwoCols)
             v += __shfl_down(s1[e], G, 16) + s2[e];
           else
             v += __shfl_down(s1[e], G, 16) + __shfl_down(s1[e], 2 * G, 16);
@@ -537,21 +553,37 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           hp[e / 2] = pack_bf16x2(h0, h1);
           lp[e / 2] = pack_bf16x2(w[e] - h0, w[e + 1] - h1);
         }
-        // column col of the weight operand: the high parts of block col
-        // (col < G), the remainders of block col - G (G <= col < 2G), else 0
-        const uint32_t l0 = __shfl_up(lp[0], G, 16), l1 = __shfl_up(lp[1], G, 16);
-        const uint32_t b0 = col < G ? hp[0] : col < 2 * G ? l0 : 0u;
-        const uint32_t b1 = col < G ? hp[1] : col < 2 * G ? l1 : 0u;
-        const i16x4 wB = __builtin_bit_cast(i16x4, make_uint2(b0, b1));
-        if (__ballot(alpha != 1.f)) {
-          const float ar = __shfl_up(alpha, G, 16);
-          const float al = col < G ? alpha : col < 2 * G ? ar : 1.f;
+        if constexpr (kFull) {
+          // every column is a block: the high parts and the remainders in two
+          // products into the same numerators
+          const i16x4 wH = __builtin_bit_cast(i16x4, make_uint2(hp[0], hp[1]));
+          const i16x4 wL = __builtin_bit_cast(i16x4, make_uint2(lp[0], lp[1]));
+          if (__ballot(alpha != 1.f)) {
 #pragma unroll
-          for (int ci = 0; ci < CT; ++ci) accv[ci] *= al;
+            for (int ci = 0; ci < CT; ++ci) accv[ci] *= alpha;
+          }
+#pragma unroll
+          for (int ci = 0; ci < CT; ++ci) {
+            accv[ci] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(b.v[ci], wH, accv[ci], 0, 0, 0);
+            accv[ci] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(b.v[ci], wL, accv[ci], 0, 0, 0);
+          }
+        } else {
+          // column col of the weight operand: the high parts of block col
+          // (col < G), the remainders of block col - G (G <= col < 2G), else 0
+          const uint32_t l0 = __shfl_up(lp[0], G, 16), l1 = __shfl_up(lp[1], G, 16);
+          const uint32_t b0 = col < G ? hp[0] : col < 2 * G ? l0 : 0u;
+          const uint32_t b1 = col < G ? hp[1] : col < 2 * G ? l1 : 0u;
+          const i16x4 wB = __builtin_bit_cast(i16x4, make_uint2(b0, b1));
+          if (__ballot(alpha != 1.f)) {
+            const float ar = __shfl_up(alpha, G, 16);
+            const float al = col < G ? alpha : col < 2 * G ? ar : 1.f;
+#pragma unroll
+            for (int ci = 0; ci < CT; ++ci) accv[ci] *= al;
+          }
+#pragma unroll
+          for (int ci = 0; ci < CT; ++ci)
+            accv[ci] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(b.v[ci], wB, accv[ci], 0, 0, 0);
         }
-#pragma unroll
-        for (int ci = 0; ci < CT; ++ci)
-          accv[ci] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(b.v[ci], wB, accv[ci], 0, 0, 0);
       };
       // the 16 kept bits of column col's block in the step: OR over its four lanes
       auto or4 = [](uint32_t x) {
@@ -670,10 +702,11 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
     {
       // the group's maximum M of each block, and this wave's factor e^{Mw - M}
       // for its partial sums (0 for a wave that saw none of the block's scores)
-      const int gc = col < G ? col : col - G;  // the block of column col (columns < 2G)
+      // the block of column col (columns < 2G; with G = 16 the column itself)
+      const int gc = kFull || col < G ? col : col - G;
       const float Mg = fmaxf(fmaxf(sm.wfin[0][gc], sm.wfin[1][gc]), fmaxf(sm.wfin[2][gc], sm.wfin[3][gc]));
       const float Mwc = sm.wfin[wid][gc];
-      const float f = (col < 2 * G && Mwc > -INFINITY) ? __expf(Mwc - Mg) : 0.f;
+      const float f = ((kFull || col < 2 * G) && Mwc > -INFINITY) ? __expf(Mwc - Mg) : 0.f;
       float* partc = reinterpret_cast<float*>(stB);  // [4 waves][G][D]
 #pragma unroll
       for (int ci = 0; ci < CT; ++ci) {
@@ -681,7 +714,10 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = accv[ci][e] * f;
-          (&cn.x)[e] = x + __shfl_down(x, G, 16);  // high and remainder columns of block col
+          if constexpr (kFull)
+            (&cn.x)[e] = x;
+          else
+            (&cn.x)[e] = x + __shfl_down(x, G, 16);  // high and remainder columns of block col
         }
         if (col < G) *reinterpret_cast<float4*>(&partc[(wid * G + col) * D + 16 * ci + 4 * kq]) = cn;
       }
@@ -766,53 +802,41 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
             qop[qt][ds] = as_bf16x8(*reinterpret_cast<const uint4*>(&qs[16 * qt * GM::QS + 32 * ds]));
       }
 
-      // ---- 2. union of the two kept lists, from the kept bits ----
-      // Thread t takes kept-bit word t of both blocks (at most 128 words):
-      // the union's count, a prefix over the threads, then the word's kept
-      // blocks in ascending order at that offset.
-      int nu;
+      // ---- 2. the union of the two kept lists, walked in ascending order ----
+      // No list is stored: every wave holds a bit mask of the union's
+      // nonzero kept-bit words (one ballot per 64 words) and walks the union
+      // with wave-uniform scalar state, reading a word's bits from LDS when
+      // the walk reaches it. Wave 0 counts the pair's kept blocks for the stats.
+      uint64_t nz0, nz1 = 0ull;
       {
         const int nw = (Nk + 31) / 32;
-        const uint32_t wa = tid < nw ? sm.kbits[gA][tid] : 0u;
-        const uint32_t wb = tid < nw && hasB ? sm.kbits[gA + 1][tid] : 0u;
-        const uint32_t wu = wa | wb;
-        const int cu = __popc(wu);
-        int x = cu;  // inclusive prefix over the wave's lanes
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(x, o);
-          x += lane >= o ? y : 0;
+        auto uword = [&](int w) -> uint32_t {
+          return w < nw ? sm.kbits[gA][w] | (hasB ? sm.kbits[gA + 1][w] : 0u) : 0u;
+        };
+        nz0 = __ballot(uword(lane) != 0u);
+        if constexpr (KW > 64) nz1 = __ballot(uword(64 + lane) != 0u);
+        if (wid == 0) {
+          int ca = 0, cb = 0;
+          for (int w = lane; w < nw; w += 64) {
+            ca += __popc(sm.kbits[gA][w]);
+            cb += hasB ? __popc(sm.kbits[gA + 1][w]) : 0;
+          }
+          const int nkA = wave_sum_int(ca), nkB = wave_sum_int(cb);
+          if (lane == 0) {
+            // this pair's stats (kept token pairs: the last key block has nlast tokens)
+            const int jl = Nk - 1;
+            const bool lastA = (sm.kbits[gA][jl >> 5] >> (jl & 31)) & 1u;
+            const bool lastB = hasB && ((sm.kbits[gA + 1][jl >> 5] >> (jl & 31)) & 1u);
+            const unsigned long long tokA = (unsigned long long)nkA * kBlk - (lastA ? kBlk - nlast : 0);
+            const unsigned long long tokB = (unsigned long long)nkB * kBlk - (lastB ? kBlk - nlast : 0);
+            sm.st64[0] += (unsigned long long)(nkA + (hasB ? nkB : 0));
+            sm.st64[1] += (unsigned long long)Nk * (hasB ? 2 : 1);
+            sm.st64[2] += tokA * (unsigned long long)nA + (hasB ? tokB * (unsigned long long)nB : 0ull);
+            sm.st32[0] = min(sm.st32[0], hasB ? (unsigned)min(nkA, nkB) : (unsigned)nkA);
+            sm.st32[1] = max(sm.st32[1], hasB ? (unsigned)max(nkA, nkB) : (unsigned)nkA);
+          }
         }
-        const int ca = wave_sum_int(__popc(wa)), cb = wave_sum_int(__popc(wb));
-        if (lane == 63) sm.cnt[0][wid] = x;
-        if (lane == 0) {
-          sm.cnt[1][wid] = ca;
-          sm.cnt[2][wid] = cb;
-        }
-        __syncthreads();  // (also: every wave holds its Q operands; the stages are free)
-        int off = x - cu;
-        for (int w2 = 0; w2 < wid; ++w2) off += sm.cnt[0][w2];
-        for (uint32_t r = wu; r != 0u; r &= r - 1u) {
-          const int bit = __builtin_ctz(r);
-          ulist[off++] = (uint16_t)((32 * tid + bit) | (((wa >> bit) & 1u) << 14) | (((wb >> bit) & 1u) << 15));
-        }
-        nu = sm.cnt[0][0] + sm.cnt[0][1] + sm.cnt[0][2] + sm.cnt[0][3];
-        const int nkA = sm.cnt[1][0] + sm.cnt[1][1] + sm.cnt[1][2] + sm.cnt[1][3];
-        const int nkB = sm.cnt[2][0] + sm.cnt[2][1] + sm.cnt[2][2] + sm.cnt[2][3];
-        if (tid == 0) {
-          // this pair's stats (kept token pairs: the last key block has nlast tokens)
-          const int jl = Nk - 1;
-          const bool lastA = (sm.kbits[gA][jl >> 5] >> (jl & 31)) & 1u;
-          const bool lastB = hasB && ((sm.kbits[gA + 1][jl >> 5] >> (jl & 31)) & 1u);
-          const unsigned long long tokA = (unsigned long long)nkA * kBlk - (lastA ? kBlk - nlast : 0);
-          const unsigned long long tokB = (unsigned long long)nkB * kBlk - (lastB ? kBlk - nlast : 0);
-          sm.st64[0] += (unsigned long long)(nkA + (hasB ? nkB : 0));
-          sm.st64[1] += (unsigned long long)Nk * (hasB ? 2 : 1);
-          sm.st64[2] += tokA * (unsigned long long)nA + (hasB ? tokB * (unsigned long long)nB : 0ull);
-          sm.st32[0] = min(sm.st32[0], hasB ? (unsigned)min(nkA, nkB) : (unsigned)nkA);
-          sm.st32[1] = max(sm.st32[1], hasB ? (unsigned)max(nkA, nkB) : (unsigned)nkA);
-        }
-        __syncthreads();  // the list is complete
+        __syncthreads();  // every wave holds its Q operands: the stages are free
       }
 
       // ---- 3. exact attention over the union list (online softmax, base 2) ----
@@ -830,9 +854,9 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         const uint16_t* kh = p.k + hoff;
         const uint16_t* vh = p.v + hoff;
         const int ownbit = 1 << (14 + qb);
-        // K and V tiles of kept key block ulist[t] into one stage
-        auto dma = [&](unsigned char* stage, int t) {
-          const int j = ulist[t] & 0x3fff;
+        // K and V tiles of the union entry e (key block e & 0x3fff) into one stage
+        auto dma = [&](unsigned char* stage, int e) {
+          const int j = e & 0x3fff;
           const uint32_t bytes = (uint32_t)min(kBlk, N - j * kBlk) * D * 2;
           dma_tile<D>(stage, make_rsrc(kh + (size_t)j * kBlk * D, bytes), make_rsrc(vh + (size_t)j * kBlk * D, bytes),
                       wid, lane);
@@ -1012,24 +1036,54 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           }
         };
 
+        // The walk over the union: the next entry j | A << 14 | B << 15 (A, B:
+        // kept by the pair's first / second block), or -1 past the end.
+        // Every value here is the same in all lanes of all waves, so the
+        // barriers below stay matched.
+        uint32_t rem = 0u, bitsA = 0u, bitsB = 0u;
+        int wbase = 0;
+        auto next = [&]() -> int {
+          if (rem == 0u) {
+            // the next nonzero word: selects, not branches, between the two masks
+            const bool lo = nz0 != 0ull;
+            const uint64_t m = lo ? nz0 : nz1;
+            if (m == 0ull) return -1;
+            const int w = (lo ? 0 : 64) + (int)__builtin_ctzll(m);
+            const uint64_t m2 = m & (m - 1ull);
+            nz0 = lo ? m2 : 0ull;
+            nz1 = lo ? nz1 : m2;
+            bitsA = __builtin_amdgcn_readfirstlane(sm.kbits[gA][w]);
+            bitsB = hasB ? __builtin_amdgcn_readfirstlane(sm.kbits[gA + 1][w]) : 0u;
+            rem = bitsA | bitsB;
+            wbase = 32 * w;
+          }
+          const int bit = __builtin_ctz(rem);
+          rem &= rem - 1u;
+          return (wbase + bit) | (int)(((bitsA >> bit) & 1u) << 14) | (int)(((bitsB >> bit) & 1u) << 15);
+        };
+
         // Every barrier below is preceded by an explicit wait for all of this
         // wave's outstanding copies: the copy into one stage is issued in one
         // loop iteration and consumed in the next, a dependency the compiler's
         // own wait insertion does not carry across the loop back-edge.
-        if (nu > 0) dma(stA, 0);
-        if (nu > 1) dma(stB, 1);
+        int eA = next();
+        int eB = eA >= 0 ? next() : -1;
+        if (eA >= 0) dma(stA, eA);
+        if (eB >= 0) dma(stB, eB);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // tiles 0 and 1 are in LDS
-        for (int t = 0; t < nu; t += 2) {
-          compute(stA, ulist[t], std::false_type{});
+        __syncthreads();  // the first two tiles are in LDS
+        while (eA >= 0) {
+          compute(stA, eA, std::false_type{});
           __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();  // tile t+1 has landed in stB; nobody reads stA any more
-          if (t + 2 < nu) dma(stA, t + 2);
-          if (t + 1 < nu) {
-            compute(stB, ulist[t + 1], std::false_type{});
+          __syncthreads();  // stage B's tile has landed; nobody reads stage A any more
+          eA = eB >= 0 ? next() : -1;
+          if (eA >= 0) dma(stA, eA);
+          if (eB >= 0) {
+            compute(stB, eB, std::false_type{});
             __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();  // tile t+2 has landed in stA; nobody reads stB any more
-            if (t + 3 < nu) dma(stB, t + 3);
+            __syncthreads();  // stage A's tile has landed; nobody reads stage B any more
+            eB = eA >= 0 ? next() : -1;
+            if (eB >= 0) dma(stB, eB);
           }
         }
         if (RC) {
@@ -1149,24 +1203,20 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
 
 }  // namespace
 
-size_t forward_dynamic_lds(int Nk) { return ((size_t)Nk * 2 + 15) & ~(size_t)15; }
-
 int forward_items(int BH, int Nq, int G) { return BH * ((Nq + G - 1) / G); }
 
-int forward_max_group(int Nk) { return Nk <= kMaxKeyBlocksG8 ? 8 : 4; }
+int forward_max_group(int Nk) { return Nk <= kMaxKeyBlocksG8 ? 16 : 4; }
 
 template <int D, int G, bool RC, bool RO>
 static hipError_t launch_dg(const FwdParams& p, hipStream_t stream) {
-  // per-device CU count and occupancy (bucketed by dynamic LDS in 4 KiB steps)
+  // per-device CU count and occupancy
   static std::mutex mu;
   static int cus[64] = {0};
-  static int occ_cache[64][8] = {{0}};
+  static int occ_cache[64] = {0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  const size_t dyn = RO ? 0 : forward_dynamic_lds(p.Nk);
-  const int bucket = (int)std::min<size_t>(7, dyn / 4096);
   int grid_per_cu = 0, ncu = 0;
   {
     std::lock_guard<std::mutex> lock(mu);
@@ -1174,29 +1224,28 @@ static hipError_t launch_dg(const FwdParams& p, hipStream_t stream) {
       int n = 0;
       e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<D, G, RC, RO>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 32 * 1024);
-      if (e != hipSuccess) return e;
       cus[dev] = n;
     }
-    if (occ_cache[dev][bucket] == 0) {
+    if (occ_cache[dev] == 0) {
       int occ = 0;
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&fwd_kernel<D, G, RC, RO>),
-                                                       kThreads, (size_t)(bucket + 1) * 4096);
+                                                       kThreads, 0);
       if (e != hipSuccess) return e;
-      occ_cache[dev][bucket] = occ < 1 ? 1 : occ;
+      occ_cache[dev] = occ < 1 ? 1 : occ;
     }
     ncu = cus[dev];
-    grid_per_cu = occ_cache[dev][bucket];
+    grid_per_cu = occ_cache[dev];
   }
   const int grid = p.static_grid ? p.nitems : (int)std::min<long long>((long long)ncu * grid_per_cu, p.nitems);
-  hipLaunchKernelGGL((fwd_kernel<D, G, RC, RO>), dim3(grid), dim3(kThreads), dyn, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, G, RC, RO>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool RC>
 static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
   switch (p.group) {
+    case 16:  // (the routing-only kernel runs groups of at most four)
+      return p.route_only ? hipErrorInvalidValue : launch_dg<D, 16, RC, false>(p, stream);
     case 8: return p.route_only ? launch_dg<D, 8, false, true>(p, stream) : launch_dg<D, 8, RC, false>(p, stream);
     case 4: return p.route_only ? launch_dg<D, 4, false, true>(p, stream) : launch_dg<D, 4, RC, false>(p, stream);
     default: return p.route_only ? launch_dg<D, 2, false, true>(p, stream) : launch_dg<D, 2, RC, false>(p, stream);

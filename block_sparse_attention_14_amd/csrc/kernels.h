@@ -30,8 +30,8 @@ __host__ __device__ inline int queue_begin(int x, int nitems) {
   return (int)(((long long)x * nitems) / kQueues);
 }
 
-// Longest head (in key blocks) that a work item of eight query blocks
-// supports: its kept bits and kept list must fit the workgroup's LDS.
+// Longest head (in key blocks) that a work item of eight or sixteen query
+// blocks supports: its kept bits must fit the workgroup's LDS.
 constexpr int kMaxKeyBlocksG8 = 2048;
 
 struct FwdParams {
@@ -42,11 +42,12 @@ struct FwdParams {
   const float* kpool;    // fp32 [BH][Nk][d]
   const float* vmean;    // fp32 [BH][Nk][d]
   const unsigned* perm;  // nullable: rank -> item, within each queue's range
+  const unsigned* plan_items;  // with perm: the item count the order was made for
   unsigned* hdr;         // workspace header (kHdr*), clean on entry
   sol_attn_stats* stats; // nullable, written by the last workgroup
   uint32_t* bitmap;      // nullable, [BH][Nq][nwords]
   int N, Nq, Nk, nitems, nwords;  // nitems = forward_items(BH, Nq, group)
-  int group;             // query blocks per work item: 2, 4 or 8
+  int group;             // query blocks per work item: 2, 4, 8 or 16
   int ngroups;           // work items per head, ceil(Nq / group)
   int route_only;        // stop after routing (the kept-block bitmap is the only output)
   int static_grid;       // one workgroup per item, no queues, no header, no stats (route_only)
@@ -119,12 +120,14 @@ hipError_t launch_reset(unsigned* hdr, hipStream_t stream);
 // blocks, from sampled query means) and the order of each queue's range of
 // items of `group` query blocks (an item costs the sum over its pairs):
 // head-major, then its last third heaviest first.
-// perm[rank] = item, with rank and item in the same queue range.
-hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, int BH, int N, int Nq,
-                       int Nk, int d, float tau, float proxy_scale, int group, hipStream_t stream);
+// perm[rank] = item, with rank and item in the same queue range; *plan_items
+// = the number of items the order is for.
+hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, unsigned* plan_items,
+                       int BH, int N, int Nq, int Nk, int d, float tau, float proxy_scale, int group,
+                       hipStream_t stream);
 
 // perm[i] = i for every item (the order of a plan that does not sort).
-hipError_t launch_identity_order(unsigned* perm, int nitems, hipStream_t stream);
+hipError_t launch_identity_order(unsigned* perm, unsigned* plan_items, int nitems, hipStream_t stream);
 
 // The fused routing + exact + correction kernel (persistent grid).
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t stream);
@@ -136,9 +139,6 @@ hipError_t launch_proxy_map(const float* qpool, const float* kpool, float* map, 
 // Per-row sort of the map; mode 0 keeps the top `topk`, mode 1 the top-p prefix.
 hipError_t launch_sort_mask(const float* map, uint32_t* bitmap, int BH, int Nq, int Nk, int topk, float topp,
                             int mode, hipStream_t stream);
-
-// Dynamic LDS bytes the fused kernel needs for the kept list of Nk blocks.
-size_t forward_dynamic_lds(int Nk);
 
 // Number of work items (groups of `group` query blocks) of the fused kernel.
 int forward_items(int BH, int Nq, int group);

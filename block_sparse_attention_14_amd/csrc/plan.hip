@@ -235,7 +235,8 @@ __global__ __launch_bounds__(64 * kPlanWaves) void plan_kernel(const uint16_t* _
 // An item of G query blocks costs the sum over its G / 2 pairs, bucketed in
 // units of G / 2 so that the histogram keeps Nk + 1 buckets.
 __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict__ cost, unsigned* __restrict__ perm,
-                                                     int nitems, int Nk, int npairs, int group, int ngroups) {
+                                                     unsigned* __restrict__ plan_items, int nitems, int Nk, int npairs,
+                                                     int group, int ngroups) {
   extern __shared__ unsigned hist[];  // [Nk + 1] counts, then running offsets
   __shared__ unsigned part[1024];
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict_
     for (int t = 0; t < hp && p0 + t < npairs; ++t) c += cost[(size_t)bh * npairs + p0 + t];
     return min(c / (unsigned)hp, (unsigned)Nk);
   };
+  if (blockIdx.x == 0 && tid == 0) *plan_items = (unsigned)nitems;
   for (int i = lo + tid; i < t0; i += nt) perm[i] = (unsigned)i;
   for (int b = tid; b <= Nk; b += nt) hist[b] = 0u;
   __syncthreads();
@@ -282,20 +284,23 @@ __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict_
   for (int i = t0 + tid; i < hi; i += nt) perm[atomicAdd(&hist[bucket(i)], 1u)] = (unsigned)i;
 }
 
-__global__ __launch_bounds__(256) void iota_kernel(unsigned* __restrict__ perm, int nitems) {
+__global__ __launch_bounds__(256) void iota_kernel(unsigned* __restrict__ perm, unsigned* __restrict__ plan_items,
+                                                   int nitems) {
   const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) *plan_items = (unsigned)nitems;
   if (i < nitems) perm[i] = (unsigned)i;
 }
 
 }  // namespace
 
-hipError_t launch_identity_order(unsigned* perm, int nitems, hipStream_t stream) {
-  hipLaunchKernelGGL(iota_kernel, dim3((nitems + 255) / 256), dim3(256), 0, stream, perm, nitems);
+hipError_t launch_identity_order(unsigned* perm, unsigned* plan_items, int nitems, hipStream_t stream) {
+  hipLaunchKernelGGL(iota_kernel, dim3((nitems + 255) / 256), dim3(256), 0, stream, perm, plan_items, nitems);
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, int BH, int N, int Nq,
-                       int Nk, int d, float tau, float proxy_scale, int group, hipStream_t stream) {
+hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, unsigned* plan_items,
+                       int BH, int N, int Nq, int Nk, int d, float tau, float proxy_scale, int group,
+                       hipStream_t stream) {
   const dim3 grid((Nq + kPlanQ - 1) / kPlanQ, BH);
   if (d == 128)
     hipLaunchKernelGGL(plan_kernel<128>, grid, dim3(64 * kPlanWaves), 0, stream, q, kpool, cost, N, Nq, Nk, tau,
@@ -307,7 +312,7 @@ hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, un
   if (e != hipSuccess) return e;
   const int nitems = forward_items(BH, Nq, group);
   hipLaunchKernelGGL(order_kernel, dim3(kQueues), dim3(1024), (size_t)(Nk + 1) * sizeof(unsigned), stream, cost,
-                     perm, nitems, Nk, (Nq + 1) / 2, group, (Nq + group - 1) / group);
+                     perm, plan_items, nitems, Nk, (Nq + 1) / 2, group, (Nq + group - 1) / group);
   return hipGetLastError();
 }
 

@@ -74,9 +74,10 @@ enum {
    * ideally for these q, kpool and tau), possibly followed by other forwards
    * on it: launch only the fused kernel, taking the items in the planned
    * order. The order only schedules work, so a plan made for other inputs
-   * of the same shapes gives the same result, only scheduled worse. A
-   * workspace that was never planned must not be used with this flag.
-   * Requires SOL_F_POOLED. */
+   * of the same shapes gives the same result, only scheduled worse; a plan
+   * made for another number of work items (the automatic group size depends
+   * on tau) is ignored and the items go in sequence. A workspace that was
+   * never planned must not be used with this flag. Requires SOL_F_POOLED. */
   SOL_F_PLANNED = 1u << 2,
   /* Token-to-block correction (§3 "Unified execution": one score tile per
    * query row and key block; App. B analyses one query row): a skipped block
@@ -89,18 +90,22 @@ enum {
   /* `out` is bf16 [B][H][N][d] instead of fp32: the same fp32 result, rounded
    * to nearest even as it is stored (half the output bytes). */
   SOL_F_OUT_BF16 = 1u << 4,
-  /* Bits 5-6: query blocks per work item of the fused kernel; the group's
-   * routing pass reads the head's pooled keys and values once for all of
-   * them. 0 (the default): chosen by the library (8 when the call has at
-   * least 6 such items per CU and at most 2048 key blocks, else 4 under the
-   * same item rule, else 2). SOL_F_GROUP2 / 4 / 8 ask for a size; 8 needs
-   * ceil(N/64) <= 2048 (SOL_EUNSUPPORTED otherwise) and none combines with
-   * SOL_F_PLANNED (SOL_EINVAL). The size only schedules work: results agree
-   * within floating-point rounding (sums are taken in another order), and
-   * are bitwise reproducible for a given size. */
+  /* Bits 5-6 and bit 8: query blocks per work item of the fused kernel; the
+   * group's routing pass reads the head's pooled keys and values once for
+   * all of them. None set (the default): chosen by the library (16 for
+   * row-max routing with tau <= 4 when the call has at least 6 such items
+   * per CU and at most 2048 key blocks, else 8 under the same item and block
+   * rules, else 4 under the item rule, else 2).
+   * SOL_F_GROUP2 / 4 / 8 / 16 ask for a size; 8 and 16 need
+   * ceil(N/64) <= 2048 (SOL_EUNSUPPORTED otherwise); SOL_F_GROUP16 together
+   * with bits 5-6, or any size with SOL_F_PLANNED, is SOL_EINVAL. The size
+   * only schedules work: results agree within floating-point rounding (sums
+   * are taken in another order), and are bitwise reproducible for a given
+   * size. */
   SOL_F_GROUP2 = 1u << 5,
   SOL_F_GROUP4 = 2u << 5,
   SOL_F_GROUP8 = 3u << 5,
+  SOL_F_GROUP16 = 1u << 8,
   /* The workspace holds sol_attn_prepare() of these q, kpool and vmean (with
    * the same SOL_F_ROW_CORRECTION bit): skip the pre-pass. Requires
    * SOL_F_POOLED. With SOL_F_PLANNED only the fused kernel is launched. */
@@ -186,7 +191,9 @@ int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean,
  * third heaviest first. A scheduling aid only: the forward still routes every
  * block itself, in fp32, and nothing routing-related is written to device
  * memory beyond one count per item. For tau = +inf (and very large B*H*N)
- * the order is the identity. Resets the workspace's queue and stats words.
+ * the order is the identity. The items are those of the forward's automatic
+ * group size at this tau (their count is recorded with the order). Resets
+ * the workspace's queue and stats words.
  *   q         bf16 [B][H][N][d]
  *   kpool     fp32 [B][H][Nk][d], sol_attn_pool() of k
  *   workspace as for sol_attn_forward

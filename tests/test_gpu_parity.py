@@ -154,12 +154,13 @@ def test_video_dit_119k(video119k, tau, whole):
 
 
 def test_video_dit_119k_router_and_group_sizes(video119k):
-    """On the 119K layer: the threshold router (the fused kernel stopped after
-    routing) exports the forward's bitmap bit for bit; groups of two, four and
-    eight query blocks route alike away from the tie band (their scores are
-    summed in different orders), give outputs within the bar of each other
-    where they route alike, and match the oracle on their own routing where
-    they do not."""
+    """On the 119K layer: the library's own choice is sixteen query blocks per
+    item; the threshold router (the fused kernel stopped after routing, four
+    blocks per item) exports the bitmap of the forward with four blocks per
+    item bit for bit; groups of two, four, eight and sixteen query blocks
+    route alike away from the tie band (their scores are summed in different
+    orders), give outputs within the bar of each other where they route
+    alike, and match the oracle on their own routing where they do not."""
     from parity import BITMAP_TIE, oracle_route
 
     wl = get_workload("video_dit_119k")
@@ -167,23 +168,23 @@ def test_video_dit_119k_router_and_group_sizes(video119k):
     r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
     tau = 4.0
     outs, bms = {}, {}
-    for g in (0, 2, 4, 8):
+    for g in (0, 2, 4, 8, 16):
         bm = torch.zeros(sa.bitmap_shape(wl.B, wl.H, wl.N), dtype=torch.int32, device=q.device)
         outs[g] = r(q, k, v, tau, bitmap=bm, group=g).clone()
         bms[g] = bm
     torch.cuda.synchronize()
-    assert torch.equal(bms[0], bms[8]) and torch.equal(outs[0].view(torch.int32), outs[8].view(torch.int32))
+    assert torch.equal(bms[0], bms[16]) and torch.equal(outs[0].view(torch.int32), outs[16].view(torch.int32))
     mb = sa.MaskBuilder(wl.B, wl.H, wl.N, wl.d)
-    assert torch.equal(mb.threshold(q, r.kpool, tau=tau), bms[0])
-    keep8 = sa.unpack_bitmap(bms[8], wl.Nk)[0]
-    out8 = outs[8].cpu().numpy()[0]
-    for g in (2, 4):
+    assert torch.equal(mb.threshold(q, r.kpool, tau=tau), bms[4])
+    keep8 = sa.unpack_bitmap(bms[16], wl.Nk)[0]
+    out8 = outs[16].cpu().numpy()[0]
+    for g in (2, 4, 8):
         keep = sa.unpack_bitmap(bms[g], wl.Nk)[0]
         out = outs[g].cpu().numpy()[0]
         rows_differ = (keep != keep8).any(axis=-1)  # [H, Nq]
         same = np.repeat(~rows_differ, 64, axis=1)[:, :wl.N]
         err = np.abs(out - out8).max(axis=-1)[same].max()
-        print(f"[parity] video_dit_119k group {g} vs 8: {int(rows_differ.sum())} query blocks route differently, "
+        print(f"[parity] video_dit_119k group {g} vs 16: {int(rows_differ.sum())} query blocks route differently, "
               f"max abs diff elsewhere {err:.3e}", flush=True)
         assert err <= 2e-2
         for h, i in np.argwhere(rows_differ)[:8]:
@@ -197,17 +198,18 @@ def test_video_dit_119k_router_and_group_sizes(video119k):
                 assert np.abs(oo[sl] - ref[sl]).max() <= 2e-2
 
 
-@pytest.mark.parametrize("group", [2, 4, 8])
+@pytest.mark.parametrize("group", [2, 4, 8, 16])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [65, 1000, 4000])
 @pytest.mark.parametrize("tau", [0.0, 2.0, INF])
 def test_group_sizes(group, d, N, tau):
     """Every group size on ragged heads: 2, 16 and 63 query blocks, so that
-    groups of four and eight end partial (63 = 7 x 8 + 7), on every row."""
+    groups of four, eight and sixteen end partial (63 = 7 x 8 + 7 =
+    3 x 16 + 15), on every row."""
     _full_parity(_custom(N, d, H=2, seed=N + d + group), tau, group=group)
 
 
-@pytest.mark.parametrize("group", [4, 8])
+@pytest.mark.parametrize("group", [4, 8, 16])
 def test_group_sizes_gauss_sinks_and_row_correction(group):
     wl = _custom(4000, 128, H=2, seed=88)
     _full_parity(wl, 0.0, beta=1.0, group=group)
@@ -216,7 +218,8 @@ def test_group_sizes_gauss_sinks_and_row_correction(group):
     _full_parity(wl, 1.0, sinks=(60, 3), flags=sa.SOL_F_EXACT_ONLY, group=group)
 
 
-def test_group8_far_maximum_rechecks_early_candidates():
+@pytest.mark.parametrize("group", [8, 16])
+def test_group8_far_maximum_rechecks_early_candidates(group):
     """A long head (1500 key blocks, six routing chunks) whose best blocks are
     sink blocks at the start of the sequence: every group meets its maximum
     in a late chunk, so blocks kept against the running maximum of earlier
@@ -224,7 +227,7 @@ def test_group8_far_maximum_rechecks_early_candidates():
     wl = Workload(name="sink_far_N96000_d64", B=1, H=2, grid=(1, 1, 96000), d=64, dtype="bf16", taus=(), seed=515,
                   locality=(3.0, 3.0), sink_heads=(0, 1), sink_blocks=4)
     for tau in (2.0, 6.0):
-        _full_parity(wl, tau, group=8)
+        _full_parity(wl, tau, group=group)
 
 
 def test_row_correction_video_dit_119k(video119k):
@@ -458,6 +461,28 @@ def test_prepared_forwards_match_one_shot():
             assert r.read_stats() == ref_stats
     print(f"[prepared] image_dit_4k tau=8: prepared forwards identical to one-shot, kept {ref_stats['kept_blocks']}",
           flush=True)
+
+
+def test_plan_for_another_group_size_is_ignored(video119k):
+    """On the 119K layer the library routes sixteen query blocks per item at
+    tau <= 4 and eight above: a plan made at one tau and followed by a
+    planned forward at the other is for another item count, so the fused
+    kernel takes the items in sequence and the result equals the unplanned
+    forward bit for bit (and the matching plan is still followed)."""
+    wl = get_workload("video_dit_119k")
+    q, k, v = (to_device_bf16(video119k[n]) for n in "qkv")
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    sa.pool(k, v, kpool=r.kpool, vmean=r.vmean)
+    for plan_tau, tau in ((2.0, 8.0), (8.0, 2.0), (2.0, 2.0)):
+        ref = r(q, k, v, tau, flags=sa.SOL_F_POOLED).clone()
+        ref_stats = r.read_stats()
+        r.plan(q, plan_tau)
+        out = r(q, k, v, tau, flags=sa.SOL_F_POOLED | sa.SOL_F_PLANNED)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), (plan_tau, tau)
+        assert r.read_stats() == ref_stats
+        print(f"[plan] video_dit_119k plan at tau={plan_tau}, forward at tau={tau}: identical to unplanned",
+              flush=True)
 
 
 def test_garbage_workspace_is_reset():
