@@ -51,15 +51,22 @@
 //      sums merge under the row maximum; the group's bits are final;
 //   then for each PAIR of blocks of the group:
 //   1. both Q tiles through LDS into registers, the B operand of S^T = K Q^T
-//      (waves 0-1 own block A, waves 2-3 block B, 32 rows each);
-//   2. the union of the two kept lists, walked in ascending order straight
-//      from the kept bits (wave-uniform scalar state, no stored list);
+//      (wave w holds rows 16w .. 16w + 15 of both blocks: query tile 0 of the
+//      first block, query tile 1 of the second);
+//   2. the union of the two kept lists, walked straight from the kept bits
+//      (wave-uniform scalar state, no stored list) in three runs: the key
+//      blocks both blocks keep, then those only the first keeps, then those
+//      only the second keeps, each run in ascending order with its own copy
+//      of the step below (one owner pattern per loop keeps the registers of
+//      the three copies apart);
 //   3. for every union entry, the K and V tiles stream from HBM straight into
 //      LDS (buffer loads with an LDS destination, no registers involved),
 //      double-buffered in two stages, one barrier per tile. 16-byte chunks are
 //      XOR-swizzled per row through the per-lane source addresses, so both
-//      operand reads below are bank-conflict free. Each wave whose block keeps
-//      the entry computes its 64x32 S^T with 16x16x32 bf16 MFMAs, the online
+//      operand reads below are bank-conflict free. Every wave computes the
+//      64 x 16 S^T tile of each of its query tiles whose block keeps the
+//      entry (so all four waves work on every entry) with 16x16x32 bf16
+//      MFMAs, the online
 //      softmax in base 2 with a lazily raised maximum (one query row per lane:
 //      two permlane swaps reduce a row), the row sums as an MFMA against a
 //      ones operand, and O^T += V^T P^T with V^T operands read from the
@@ -243,8 +250,9 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g16 = lane >> 4, c16 = lane & 15;
-  const int qb = wid >> 1;           // which block of a pair this wave serves
-  const int qrow0 = 32 * (wid & 1);  // first of its 32 rows in that block
+  // wave w serves rows 16w .. 16w + 15 of both blocks of a pair: query tile
+  // 0 of the first block, query tile 1 of the second
+  const int qrow0 = 16 * wid;
   const int nlast = N - (Nk - 1) * kBlk;
   const float csc = p.scale_log2;
   const bool rowmax = p.rule == SOL_ROUTE_ROWMAX;
@@ -772,7 +780,6 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
       const bool lastpair = pr == G / 2 - 1 || qA + 2 >= Nq;
       const int nA = min(kBlk, N - qA * kBlk);
       const int nB = hasB ? min(kBlk, N - (qA + 1) * kBlk) : 0;
-      const int nmine = qb ? nB : nA;
 
       // ---- 1. Q tiles -> LDS -> Q^T operands ----
       bf16x8 qop[2][NDS];
@@ -794,19 +801,20 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           for (int u = 0; u < PER; ++u) *reinterpret_cast<uint4*>(qd + u * RSTEP * GM::QS) = qr[blk][u];
         }
         __syncthreads();
-        const uint16_t* qs = reinterpret_cast<const uint16_t*>(qb ? stB : stA) + (qrow0 + c16) * GM::QS + 8 * g16;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < 2; ++qt) {
+          const uint16_t* qs = reinterpret_cast<const uint16_t*>(qt ? stB : stA) + (qrow0 + c16) * GM::QS + 8 * g16;
 #pragma unroll
-          for (int ds = 0; ds < NDS; ++ds)
-            qop[qt][ds] = as_bf16x8(*reinterpret_cast<const uint4*>(&qs[16 * qt * GM::QS + 32 * ds]));
+          for (int ds = 0; ds < NDS; ++ds) qop[qt][ds] = as_bf16x8(*reinterpret_cast<const uint4*>(&qs[32 * ds]));
+        }
       }
 
-      // ---- 2. the union of the two kept lists, walked in ascending order ----
+      // ---- 2. the union of the two kept lists, walked from the kept bits ----
       // No list is stored: every wave holds a bit mask of the union's
       // nonzero kept-bit words (one ballot per 64 words) and walks the union
-      // with wave-uniform scalar state, reading a word's bits from LDS when
-      // the walk reaches it. Wave 0 counts the pair's kept blocks for the stats.
+      // (in three runs by owner, step 3) with wave-uniform scalar state,
+      // reading a word's bits from LDS when the walk reaches it. Wave 0
+      // counts the pair's kept blocks for the stats.
       uint64_t nz0, nz1 = 0ull;
       {
         const int nw = (Nk + 31) / 32;
@@ -853,7 +861,6 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         const bf16x8 ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
         const uint16_t* kh = p.k + hoff;
         const uint16_t* vh = p.v + hoff;
-        const int ownbit = 1 << (14 + qb);
         // K and V tiles of the union entry e (key block e & 0x3fff) into one stage
         auto dma = [&](unsigned char* stage, int e) {
           const int j = e & 0x3fff;
@@ -884,9 +891,12 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         for (int dt = 0; dt < NDT; ++dt)
           voffs[dt] = GM::TILE + vrow * GM::RB + 16 * vslot<D>(vrow, 2 * dt + (vcc >> 1)) + 8 * (vcc & 1);
 
-        auto compute = [&](const unsigned char* stage, int e, auto pooled) {
+        // QM: the query tiles that take part (bit 0: the first block's, bit
+        // 1: the second's), i.e. the blocks of the pair that keep the entry;
+        // a tile that does not take part costs nothing
+        auto compute = [&](const unsigned char* stage, int e, auto pooled, auto qmask) __attribute__((always_inline)) {
           constexpr bool kPooled = decltype(pooled)::value;
-          if (!kPooled && !(e & ownbit)) return;  // wave-uniform: this wave's block skips the entry
+          constexpr int QM = decltype(qmask)::value;
           const int j = e & 0x3fff;
           const int nj = kPooled ? kBlk : min(kBlk, N - j * kBlk);
           // S^T[kv][q]: 4 key tiles x 2 query tiles; each K operand serves both
@@ -914,8 +924,8 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
               const bf16x8 a = kop[i];
               if (i + KA < 4 * NDS) kop[i + KA] = kread(i + KA);
               __builtin_amdgcn_sched_barrier(0);
-              st[0][kt] = mfma16x16x32(a, qop[0][ds], st[0][kt]);
-              st[1][kt] = mfma16x16x32(a, qop[1][ds], st[1][kt]);
+              if (QM & 1) st[0][kt] = mfma16x16x32(a, qop[0][ds], st[0][kt]);
+              if (QM & 2) st[1][kt] = mfma16x16x32(a, qop[1][ds], st[1][kt]);
               __builtin_amdgcn_sched_barrier(0);
               if (kPooled) {  // the remainder part of the pooled keys, one tile further on
                 const bf16x8 b =
@@ -927,25 +937,27 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           }
           // lane holds S^T[16kt + 4g + i][row c16 of query tile qt]
           if (kPooled) {
-            // pooled key 64e + 16kt + 4g + i: masked when kept by this wave's
-            // block (it is in the exact branch) or past Nk; otherwise its
-            // weight n_j enters as log2(n_j) on the base-2 logit, added here in
-            // raw dot-product units (n_j = 64 but for the ragged last block)
-            const uint32_t* kb = sm.kbits[gA + qb];
+            // pooled key 64e + 16kt + 4g + i: masked for a query tile when
+            // kept by its block (it is in the exact branch) or past Nk;
+            // otherwise its weight n_j enters as log2(n_j) on the base-2 logit,
+            // added here in raw dot-product units (n_j = 64 but for the ragged
+            // last block)
             const int valid = Nk - e * kBlk;
-            uint64_t offb = (uint64_t)kb[2 * e] | ((uint64_t)kb[2 * e + 1] << 32);
-            if (valid < kBlk) offb |= ~0ull << valid;
-            offb >>= 4 * g16;
             const int last = Nk - 1 - e * kBlk - 4 * g16;  // lane position of the last block, if here
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int qt = 0; qt < 2; ++qt) {
+              const uint32_t* kb = sm.kbits[gA + qt];
+              uint64_t offb = (uint64_t)kb[2 * e] | ((uint64_t)kb[2 * e + 1] << 32);
+              if (valid < kBlk) offb |= ~0ull << valid;
+              offb >>= 4 * g16;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const bool masked = (offb >> (16 * kt + i)) & 1ull;
-                const float b = masked ? -INFINITY : 16 * kt + i == last ? pbias_last : pbias;
-                st[0][kt][i] += b;
-                st[1][kt][i] += b;
-              }
+              for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const bool masked = (offb >> (16 * kt + i)) & 1ull;
+                  st[qt][kt][i] += masked ? -INFINITY : 16 * kt + i == last ? pbias_last : pbias;
+                }
+            }
           } else if (nj < kBlk) {
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
@@ -960,6 +972,8 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           float mn[2];
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
+            mn[qt] = m[qt];
+            if (!((QM >> qt) & 1)) continue;
             // two chains of three-input maxima over the lane's 16 scores
             float b0 = fmaxf(fmaxf(st[qt][0][0], st[qt][0][1]), st[qt][0][2]);
             float b1 = fmaxf(fmaxf(st[qt][2][0], st[qt][2][1]), st[qt][2][2]);
@@ -976,6 +990,7 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           if (__ballot(raise)) {  // rare: a row's max rose by more than the lazy margin
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
+              if (!((QM >> qt) & 1)) continue;
               const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn[qt]);
               lsum[qt] *= alpha;
 #pragma unroll
@@ -987,6 +1002,7 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           bf16x8 pb[2][2];
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
+            if (!((QM >> qt) & 1)) continue;
             const float nm = -m[qt];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -1008,7 +1024,7 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           }
           // O^T[d][q] += V^T[d][kv] P^T[kv][q]; the transposing reads of rows
           // 32ks + 4g + e and 32ks + 16 + 4g + e give exactly the keys of the P^T
-          // slots; each V^T operand serves both query tiles
+          // slots; each V^T operand serves the query tiles that take part
           const unsigned char* vstage = kPooled ? stB : stage;
           // V^T operands of the next 16 rows of d read while this slice's MFMAs run
           auto vread = [&](int dt, uint2 (&o)[4]) {
@@ -1027,8 +1043,8 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
               const bf16x8 a = as_bf16x8(make_uint4(vc[2 * ks].x, vc[2 * ks].y, vc[2 * ks + 1].x, vc[2 * ks + 1].y));
-              accO[0][dt] = mfma16x16x32(a, pb[0][ks], accO[0][dt]);
-              accO[1][dt] = mfma16x16x32(a, pb[1][ks], accO[1][dt]);
+              if (QM & 1) accO[0][dt] = mfma16x16x32(a, pb[0][ks], accO[0][dt]);
+              if (QM & 2) accO[1][dt] = mfma16x16x32(a, pb[1][ks], accO[1][dt]);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1036,56 +1052,66 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           }
         };
 
-        // The walk over the union: the next entry j | A << 14 | B << 15 (A, B:
-        // kept by the pair's first / second block), or -1 past the end.
-        // Every value here is the same in all lanes of all waves, so the
-        // barriers below stay matched.
-        uint32_t rem = 0u, bitsA = 0u, bitsB = 0u;
-        int wbase = 0;
-        auto next = [&]() -> int {
-          if (rem == 0u) {
-            // the next nonzero word: selects, not branches, between the two masks
-            const bool lo = nz0 != 0ull;
-            const uint64_t m = lo ? nz0 : nz1;
-            if (m == 0ull) return -1;
-            const int w = (lo ? 0 : 64) + (int)__builtin_ctzll(m);
-            const uint64_t m2 = m & (m - 1ull);
-            nz0 = lo ? m2 : 0ull;
-            nz1 = lo ? nz1 : m2;
-            bitsA = __builtin_amdgcn_readfirstlane(sm.kbits[gA][w]);
-            bitsB = hasB ? __builtin_amdgcn_readfirstlane(sm.kbits[gA + 1][w]) : 0u;
-            rem = bitsA | bitsB;
-            wbase = 32 * w;
-          }
-          const int bit = __builtin_ctz(rem);
-          rem &= rem - 1u;
-          return (wbase + bit) | (int)(((bitsA >> bit) & 1u) << 14) | (int)(((bitsB >> bit) & 1u) << 15);
-        };
-
-        // Every barrier below is preceded by an explicit wait for all of this
-        // wave's outstanding copies: the copy into one stage is issued in one
-        // loop iteration and consumed in the next, a dependency the compiler's
-        // own wait insertion does not carry across the loop back-edge.
-        int eA = next();
-        int eB = eA >= 0 ? next() : -1;
-        if (eA >= 0) dma(stA, eA);
-        if (eB >= 0) dma(stB, eB);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // the first two tiles are in LDS
-        while (eA >= 0) {
-          compute(stA, eA, std::false_type{});
-          __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();  // stage B's tile has landed; nobody reads stage A any more
-          eA = eB >= 0 ? next() : -1;
+        // The union in three runs, one per owner pattern (kept by both
+        // blocks, by the first only, by the second only), each walked in
+        // ascending order with wave-uniform scalar state: the next entry
+        // j | A << 14 | B << 15, or -1 past the end. Every value here is the
+        // same in all lanes of all waves, so the barriers stay matched.
+        using kBoth = std::integral_constant<int, 3>;
+        using kFirst = std::integral_constant<int, 1>;
+        using kSecond = std::integral_constant<int, 2>;
+        auto run = [&](auto qmask) __attribute__((always_inline)) {
+          constexpr int QM = decltype(qmask)::value;
+          uint64_t m0 = nz0, m1 = nz1;
+          uint32_t rem = 0u;
+          int wbase = 0;
+          auto next = [&]() __attribute__((always_inline)) -> int {
+            while (rem == 0u) {
+              const bool lo = m0 != 0ull;
+              const uint64_t m = lo ? m0 : m1;
+              if (m == 0ull) return -1;
+              const int w = (lo ? 0 : 64) + (int)__builtin_ctzll(m);
+              const uint64_t m2 = m & (m - 1ull);
+              m0 = lo ? m2 : 0ull;
+              m1 = lo ? m1 : m2;
+              const uint32_t a = __builtin_amdgcn_readfirstlane(sm.kbits[gA][w]);
+              const uint32_t b = hasB ? __builtin_amdgcn_readfirstlane(sm.kbits[gA + 1][w]) : 0u;
+              rem = QM == 3 ? (a & b) : QM == 1 ? (a & ~b) : (b & ~a);
+              wbase = 32 * w;
+            }
+            const int bit = __builtin_ctz(rem);
+            rem &= rem - 1u;
+            return (wbase + bit) | (QM << 14);
+          };
+          // Every barrier below is preceded by an explicit wait for all of
+          // this wave's outstanding copies: the copy into one stage is issued
+          // in one loop iteration and consumed in the next, a dependency the
+          // compiler's own wait insertion does not carry across the loop
+          // back-edge.
+          int eA = next();
+          int eB = eA >= 0 ? next() : -1;
           if (eA >= 0) dma(stA, eA);
-          if (eB >= 0) {
-            compute(stB, eB, std::false_type{});
+          if (eB >= 0) dma(stB, eB);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();  // the first two tiles are in LDS
+          while (eA >= 0) {
+            compute(stA, eA, std::false_type{}, qmask);
             __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();  // stage A's tile has landed; nobody reads stage B any more
-            eB = eA >= 0 ? next() : -1;
-            if (eB >= 0) dma(stB, eB);
+            __syncthreads();  // stage B's tile has landed; nobody reads stage A any more
+            eA = eB >= 0 ? next() : -1;
+            if (eA >= 0) dma(stA, eA);
+            if (eB >= 0) {
+              compute(stB, eB, std::false_type{}, qmask);
+              __builtin_amdgcn_s_waitcnt(0);
+              __syncthreads();  // stage A's tile has landed; nobody reads stage B any more
+              eB = eA >= 0 ? next() : -1;
+              if (eB >= 0) dma(stB, eB);
+            }
           }
-        }
+        };
+        run(kBoth{});
+        run(kFirst{});
+        run(kSecond{});
         if (RC) {
           // pooled tiles, one at a time: each fills stage A and half of stage B
           const int npool = (Nk + kBlk - 1) / kBlk;
@@ -1102,7 +1128,7 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
             dma_pooled(c);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // pooled tile c is in LDS
-            compute(stA, c, std::true_type{});
+            compute(stA, c, std::true_type{}, kBoth{});
             __syncthreads();  // nobody reads the pooled tile any more
           }
         }
@@ -1117,16 +1143,15 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
 
       // ---- 4. fold exact and corrected terms, normalise, store ----
       {
-        const int gm = gA + qb;
-        const float M2 = sm.M[gm] * kLog2e;
-        const float cden = sm.cden[gm];
-        const int rbase = (qA + qb) * kBlk;
-        // with no correction mass (exact-only, the per-row mode, every block
-        // kept, or every skipped weight zero) the exact state alone is
-        // normalised: a common maximum with M2 could underflow it to zero
-        const bool cm = corr && cden > 0.f;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
+          const int gm = gA + qt;  // query tile qt holds rows of the pair's block qt
+          const float M2 = sm.M[gm] * kLog2e;
+          const float cden = sm.cden[gm];
+          // with no correction mass (exact-only, the per-row mode, every block
+          // kept, or every skipped weight zero) the exact state alone is
+          // normalised: a common maximum with M2 could underflow it to zero
+          const bool cm = corr && cden > 0.f;
           const float lt = lsum[qt][0];
           const float mf = cm ? fmaxf(m[qt], M2) : m[qt];
           const float fa = __builtin_amdgcn_exp2f(m[qt] - mf);
@@ -1146,9 +1171,9 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         if (lastpair && tid == 0) sm.item = p.static_grid ? -1 : item_of(take(next_ticket));
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-          const int row = qrow0 + 16 * qt + c16;
-          if (row < nmine) {
-            const size_t orow = hoff + (size_t)(rbase + row) * D;
+          const int row = qrow0 + c16;
+          if (row < (qt ? nB : nA)) {
+            const size_t orow = hoff + (size_t)((qA + qt) * kBlk + row) * D;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
               const int c = 16 * dt + 4 * g16;
