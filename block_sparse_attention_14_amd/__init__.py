@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     SOL_F_GROUP4,
     SOL_F_GROUP8,
     SOL_F_GROUP16,
+    SOL_F_GROUP6,
     SOL_F_OUT_BF16,
     SOL_F_PLANNED,
     SOL_F_POOLED,

@@ -23,6 +23,7 @@ SOL_F_GROUP2 = 1 << 5
 SOL_F_GROUP4 = 2 << 5
 SOL_F_GROUP8 = 3 << 5
 SOL_F_GROUP16 = 1 << 8
+SOL_F_GROUP6 = 1 << 9
 SOL_F_PREPARED = 1 << 7
 
 SOL_ROUTE_ROWMAX = 0

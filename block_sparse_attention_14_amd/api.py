@@ -14,18 +14,19 @@ from typing import Dict, Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import (SOL_F_EXACT_ONLY, SOL_F_GROUP2, SOL_F_GROUP4, SOL_F_GROUP8, SOL_F_GROUP16, SOL_F_OUT_BF16,  # noqa: F401
-                   SOL_F_PLANNED, SOL_F_POOLED, SOL_F_PREPARED, SOL_F_ROW_CORRECTION, check, lib)
+from ._lib import (SOL_F_EXACT_ONLY, SOL_F_GROUP2, SOL_F_GROUP4, SOL_F_GROUP6, SOL_F_GROUP8,  # noqa: F401
+                   SOL_F_GROUP16, SOL_F_OUT_BF16, SOL_F_PLANNED, SOL_F_POOLED, SOL_F_PREPARED,  # noqa: F401
+                   SOL_F_ROW_CORRECTION, check, lib)  # noqa: F401
 
 STATS_WORDS = 4  # sol_attn_stats is 32 bytes
 
 
 def group_flag(group: int) -> int:
-    """The SOL_F_GROUP* bits for 2, 4, 8 or 16 query blocks per work item (0: automatic)."""
+    """The SOL_F_GROUP* bits for 2, 4, 6, 8 or 16 query blocks per work item (0: automatic)."""
     try:
-        return {0: 0, 2: SOL_F_GROUP2, 4: SOL_F_GROUP4, 8: SOL_F_GROUP8, 16: SOL_F_GROUP16}[int(group)]
+        return {0: 0, 2: SOL_F_GROUP2, 4: SOL_F_GROUP4, 6: SOL_F_GROUP6, 8: SOL_F_GROUP8, 16: SOL_F_GROUP16}[int(group)]
     except KeyError:
-        raise ValueError("group must be 0, 2, 4, 8 or 16") from None
+        raise ValueError("group must be 0, 2, 4, 6, 8 or 16") from None
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -129,7 +130,7 @@ class SolAttention:
         diagonal estimator from the pooled-key statistics. ``sinks`` =
         (first, count) key blocks that are always kept. The output is fp32,
         or bf16 (SOL_F_OUT_BF16) when ``out`` or ``out_dtype`` is bfloat16.
-        ``group`` (2, 4, 8 or 16; 0 = the library's choice) sets the query
+        ``group`` (2, 4, 6, 8 or 16; 0 = the library's choice) sets the query
         blocks per work item (SOL_F_GROUP*)."""
         flags |= group_flag(group)
         shape = (self.B, self.H, self.N, self.d)

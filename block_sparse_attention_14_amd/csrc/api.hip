@@ -81,11 +81,14 @@ WsLayout ws_layout(int BH, int N, int d) {
 // tiles is a block), smaller ones give the persistent grid more items to
 // balance; a group is taken only while the call keeps at least 6 items per
 // CU (three per workgroup), and eight or sixteen blocks only up to 2048 key
-// blocks (their kept bits must fit the workgroup's LDS). Sixteen only where
-// the routing pass dominates the items: row-max routing with tau <= 4 (on the
-// 119K-token video layer: 12% faster at tau = 2, 3% at tau = 4, but 9%
-// slower at tau = 8, where larger items balance worse). A flag may ask for a
-// size; none there means this automatic choice.
+// blocks (their kept bits must fit the workgroup's LDS). Where the routing
+// pass dominates the items (row-max routing with tau <= 4) the largest of
+// 16, 8 and 6 that still gives 4 items per CU is taken: on the 119K-token
+// video layer sixteen are 12% faster than eight at tau = 2 and 3% at tau = 4,
+// but 9% slower at tau = 8, where larger items balance worse; on the
+// 32K-token layer six are 5% faster than four at tau = 2 to 4 (and 5%
+// slower on its variant with six diffuse heads, whose kept work dominates).
+// A flag may ask for a size; none there means this automatic choice.
 std::mutex cu_mu;
 int cu_count[64] = {0};
 
@@ -105,9 +108,13 @@ constexpr float kGroup16MaxTau = 4.f;
 
 int auto_group(int BH, int Nq, const sol_attn_route& r) {
   const long long target = 6ll * device_cus();
-  if (r.rule == SOL_ROUTE_ROWMAX && r.tau <= kGroup16MaxTau && Nq <= sol::kMaxKeyBlocksG8 &&
-      (long long)sol::forward_items(BH, Nq, 16) >= target)
-    return 16;
+  if (r.rule == SOL_ROUTE_ROWMAX && r.tau <= kGroup16MaxTau) {
+    // routing dominates: larger groups while there are 4 items per CU
+    const long long low = 4ll * device_cus();
+    if (Nq <= sol::kMaxKeyBlocksG8 && (long long)sol::forward_items(BH, Nq, 16) >= low) return 16;
+    if (Nq <= sol::kMaxKeyBlocksG8 && (long long)sol::forward_items(BH, Nq, 8) >= low) return 8;
+    if ((long long)sol::forward_items(BH, Nq, 6) >= low) return 6;
+  }
   if (Nq <= sol::kMaxKeyBlocksG8 && (long long)sol::forward_items(BH, Nq, 8) >= target) return 8;
   if ((long long)sol::forward_items(BH, Nq, 4) >= target) return 4;
   return 2;
@@ -116,6 +123,7 @@ int auto_group(int BH, int Nq, const sol_attn_route& r) {
 // The group size a flag field asks for (0: automatic), or 0 if unsupported.
 int group_of(unsigned flags, int BH, int Nq, const sol_attn_route& r) {
   if (flags & SOL_F_GROUP16) return Nq <= sol::kMaxKeyBlocksG8 ? 16 : 0;
+  if (flags & SOL_F_GROUP6) return 6;
   switch ((flags & SOL_F_GROUP_MASK) >> SOL_F_GROUP_SHIFT) {
     case 1: return 2;
     case 2: return 4;
@@ -219,11 +227,12 @@ int check_args(const void* q, const void* k, const void* v, const void* out, int
     return SOL_EINVAL;
   if (check_route(route, N, Bk) != SOL_OK) return SOL_EINVAL;
   if (flags & ~(unsigned)(SOL_F_POOLED | SOL_F_EXACT_ONLY | SOL_F_PLANNED | SOL_F_ROW_CORRECTION | SOL_F_OUT_BF16 |
-                          SOL_F_GROUP_MASK | SOL_F_GROUP16 | SOL_F_PREPARED))
+                          SOL_F_GROUP_MASK | SOL_F_GROUP16 | SOL_F_GROUP6 | SOL_F_PREPARED))
     return SOL_EINVAL;
   // one group size at most; a plan orders the items of the automatic size
-  if ((flags & SOL_F_GROUP16) && (flags & SOL_F_GROUP_MASK)) return SOL_EINVAL;
-  if ((flags & SOL_F_PLANNED) && (flags & (SOL_F_GROUP_MASK | SOL_F_GROUP16))) return SOL_EINVAL;
+  const int nsizes = ((flags & SOL_F_GROUP_MASK) != 0) + ((flags & SOL_F_GROUP16) != 0) + ((flags & SOL_F_GROUP6) != 0);
+  if (nsizes > 1) return SOL_EINVAL;
+  if ((flags & SOL_F_PLANNED) && nsizes > 0) return SOL_EINVAL;
   if ((flags & SOL_F_EXACT_ONLY) && (flags & SOL_F_ROW_CORRECTION)) return SOL_EINVAL;
   // exact-only under a Gaussian threshold: a query block whose threshold lies
   // above its best block would keep nothing, and its rows would have no terms

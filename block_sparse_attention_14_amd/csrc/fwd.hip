@@ -16,7 +16,7 @@
 //                                    exact and the corrected terms
 //
 // Work decomposition. A work item is a GROUP of G consecutive 64-row query
-// blocks of one head (G = 2, 4, 8 or 16, chosen by the host so that there are
+// blocks of one head (G = 2, 4, 6, 8 or 16, chosen by the host so that there are
 // enough items to balance the grid). A persistent grid of 256-thread
 // workgroups (two per CU) takes items from atomic ticket counters: per-block
 // budgets differ by two orders of magnitude, so a static split would idle CUs.
@@ -1272,6 +1272,8 @@ static hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     case 16:  // (the routing-only kernel runs groups of at most four)
       return p.route_only ? hipErrorInvalidValue : launch_dg<D, 16, RC, false>(p, stream);
     case 8: return p.route_only ? launch_dg<D, 8, false, true>(p, stream) : launch_dg<D, 8, RC, false>(p, stream);
+    case 6:  // (likewise)
+      return p.route_only ? hipErrorInvalidValue : launch_dg<D, 6, RC, false>(p, stream);
     case 4: return p.route_only ? launch_dg<D, 4, false, true>(p, stream) : launch_dg<D, 4, RC, false>(p, stream);
     default: return p.route_only ? launch_dg<D, 2, false, true>(p, stream) : launch_dg<D, 2, RC, false>(p, stream);
   }

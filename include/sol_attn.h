@@ -90,22 +90,23 @@ enum {
   /* `out` is bf16 [B][H][N][d] instead of fp32: the same fp32 result, rounded
    * to nearest even as it is stored (half the output bytes). */
   SOL_F_OUT_BF16 = 1u << 4,
-  /* Bits 5-6 and bit 8: query blocks per work item of the fused kernel; the
+  /* Bits 5-6, 8 and 9: query blocks per work item of the fused kernel; the
    * group's routing pass reads the head's pooled keys and values once for
-   * all of them. None set (the default): chosen by the library (16 for
-   * row-max routing with tau <= 4 when the call has at least 6 such items
-   * per CU and at most 2048 key blocks, else 8 under the same item and block
-   * rules, else 4 under the item rule, else 2).
-   * SOL_F_GROUP2 / 4 / 8 / 16 ask for a size; 8 and 16 need
-   * ceil(N/64) <= 2048 (SOL_EUNSUPPORTED otherwise); SOL_F_GROUP16 together
-   * with bits 5-6, or any size with SOL_F_PLANNED, is SOL_EINVAL. The size
-   * only schedules work: results agree within floating-point rounding (sums
-   * are taken in another order), and are bitwise reproducible for a given
-   * size. */
+   * all of them. None set (the default): chosen by the library. For
+   * row-max routing with tau <= 4 the largest of 16, 8 (both only up to
+   * 2048 key blocks) and 6 that gives the call at least 4 such items per
+   * CU; otherwise 8 when there are at least 6 items per CU and at most 2048
+   * key blocks, else 4 under the item rule, else 2. SOL_F_GROUP2 / 4 / 6 /
+   * 8 / 16 ask for a size; 8 and 16 need ceil(N/64) <= 2048
+   * (SOL_EUNSUPPORTED otherwise); two sizes at once, or any size with
+   * SOL_F_PLANNED, is SOL_EINVAL. The size only schedules work: results
+   * agree within floating-point rounding (sums are taken in another order),
+   * and are bitwise reproducible for a given size. */
   SOL_F_GROUP2 = 1u << 5,
   SOL_F_GROUP4 = 2u << 5,
   SOL_F_GROUP8 = 3u << 5,
   SOL_F_GROUP16 = 1u << 8,
+  SOL_F_GROUP6 = 1u << 9,
   /* The workspace holds sol_attn_prepare() of these q, kpool and vmean (with
    * the same SOL_F_ROW_CORRECTION bit): skip the pre-pass. Requires
    * SOL_F_POOLED. With SOL_F_PLANNED only the fused kernel is launched. */

@@ -295,6 +295,10 @@ def test_noalloc_scratch_limit():
     (dict(flags=sa.SOL_F_GROUP4), sa.SOL_EWORKSPACE),
     (dict(flags=sa.SOL_F_GROUP8), sa.SOL_EWORKSPACE),
     (dict(flags=sa.SOL_F_GROUP16), sa.SOL_EWORKSPACE),
+    (dict(flags=sa.SOL_F_GROUP6), sa.SOL_EWORKSPACE),
+    (dict(flags=sa.SOL_F_GROUP6, N=2048 * 64 + 1), sa.SOL_EWORKSPACE),
+    (dict(flags=sa.SOL_F_GROUP6 | sa.SOL_F_GROUP16), sa.SOL_EINVAL),
+    (dict(flags=sa.SOL_F_GROUP6 | sa.SOL_F_GROUP2), sa.SOL_EINVAL),
     # eight or sixteen query blocks per item only up to 2048 key blocks
     (dict(flags=sa.SOL_F_GROUP8, N=2048 * 64 + 1), sa.SOL_EUNSUPPORTED),
     (dict(flags=sa.SOL_F_GROUP16, N=2048 * 64 + 1), sa.SOL_EUNSUPPORTED),
@@ -305,7 +309,7 @@ def test_noalloc_scratch_limit():
     # a plan orders the items of the automatic group size
     (dict(flags=sa.SOL_F_GROUP2 | sa.SOL_F_POOLED | sa.SOL_F_PLANNED), sa.SOL_EINVAL),
     (dict(flags=sa.SOL_F_GROUP16 | sa.SOL_F_POOLED | sa.SOL_F_PLANNED), sa.SOL_EINVAL),
-    (dict(flags=1 << 9), sa.SOL_EINVAL),                     # unknown bit
+    (dict(flags=1 << 10), sa.SOL_EINVAL),                    # unknown bit
 ])
 def test_group_field_of_the_flags(over, code):
     assert fwd(**over) == code

@@ -198,18 +198,18 @@ def test_video_dit_119k_router_and_group_sizes(video119k):
                 assert np.abs(oo[sl] - ref[sl]).max() <= 2e-2
 
 
-@pytest.mark.parametrize("group", [2, 4, 8, 16])
+@pytest.mark.parametrize("group", [2, 4, 6, 8, 16])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [65, 1000, 4000])
 @pytest.mark.parametrize("tau", [0.0, 2.0, INF])
 def test_group_sizes(group, d, N, tau):
     """Every group size on ragged heads: 2, 16 and 63 query blocks, so that
-    groups of four, eight and sixteen end partial (63 = 7 x 8 + 7 =
-    3 x 16 + 15), on every row."""
+    groups of four, six, eight and sixteen end partial (63 = 10 x 6 + 3 =
+    7 x 8 + 7 = 3 x 16 + 15), on every row."""
     _full_parity(_custom(N, d, H=2, seed=N + d + group), tau, group=group)
 
 
-@pytest.mark.parametrize("group", [4, 8, 16])
+@pytest.mark.parametrize("group", [4, 6, 8, 16])
 def test_group_sizes_gauss_sinks_and_row_correction(group):
     wl = _custom(4000, 128, H=2, seed=88)
     _full_parity(wl, 0.0, beta=1.0, group=group)
