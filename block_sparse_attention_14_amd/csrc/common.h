@@ -10,7 +10,6 @@ namespace sol {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWave = 64;
 constexpr int kBlk = 64;  // Bq = Bk = 64 tokens per block
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -54,11 +53,8 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 
 // Cross-lane moves inside a row of 16 lanes (DPP, a VALU operand modifier;
 // no LDS round trip). Controls: quad_perm [1,0,3,2] swaps neighbours,
-// quad_perm [2,3,0,1] swaps pairs, row_half_mirror maps lane i of each
-// 8-lane half-row to lane 7 - i, row_ror:8 rotates a row by 8.
+// row_ror:8 rotates a row by 8.
 constexpr int kDppXor1 = 0xB1;
-constexpr int kDppXor2 = 0x4E;
-constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppRor8 = 0x128;  // row_ror:8, lane i of a row of 16 reads lane i ^ 8
 
 template <int CTRL>
@@ -69,16 +65,6 @@ __device__ __forceinline__ float dpp(float x) {
 template <int CTRL>
 __device__ __forceinline__ int dpp(int x) {
   return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
-}
-
-// Sum over each aligned group of 8 lanes; every lane of the group gets it.
-// After the two quad steps all four lanes of a quad hold the same value, so
-// the mirror step adds the other quad's sum.
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp<kDppXor1>(x);
-  x += dpp<kDppXor2>(x);
-  x += dpp<kDppHalfMirror>(x);
-  return x;
 }
 
 // Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle).
@@ -95,11 +81,6 @@ __device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
-// 8-byte load; bytes at or beyond the resource's size read as zero.
-__device__ __forceinline__ uint2 ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
-  return make_uint2(v[0], v[1]);
-}
 __device__ __forceinline__ float4 ld16f(rsrc_t r, uint32_t voff, uint32_t soff) {
   const uint4 u = ld16(r, voff, soff);
   return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
@@ -113,12 +94,6 @@ __device__ __forceinline__ float colsum_rows(float x) {
   if (CH == 8) x += dpp<kDppRor8>(x);
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Sum of a value over lanes l and l ^ 32 (every lane gets it).
-__device__ __forceinline__ float sum_half32(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }

@@ -1230,8 +1230,6 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
 
 int forward_items(int BH, int Nq, int G) { return BH * ((Nq + G - 1) / G); }
 
-int forward_max_group(int Nk) { return Nk <= kMaxKeyBlocksG8 ? 16 : 4; }
-
 template <int D, int G, bool RC, bool RO>
 static hipError_t launch_dg(const FwdParams& p, hipStream_t stream) {
   // per-device CU count and occupancy

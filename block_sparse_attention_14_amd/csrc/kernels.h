@@ -143,7 +143,4 @@ hipError_t launch_sort_mask(const float* map, uint32_t* bitmap, int BH, int Nq, 
 // Number of work items (groups of `group` query blocks) of the fused kernel.
 int forward_items(int BH, int Nq, int group);
 
-// Largest group size the fused kernel supports for Nk key blocks.
-int forward_max_group(int Nk);
-
 }  // namespace sol
