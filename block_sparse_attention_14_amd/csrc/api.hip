@@ -42,12 +42,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: [header words | the plan's item count | item costs | item order |
-// pooled-key copies and statistics of the optional modes]. The cost and order
-// slots are sized for items of two query blocks, the most items any group
-// size gives.
+// Workspace: [header words | the plan's item and unit counts | item costs |
+// item order | work units | pooled-key copies and statistics of the optional
+// modes]. The cost and order slots are sized for items of two query blocks,
+// the most items any group size gives; the units for every pair of every
+// item of any group size (at most ceil(Nq / 2) + 8 per head).
 struct WsLayout {
-  size_t plan, cost, perm, qpool, kh, km, kl, vt, vbar16, kstats, kmom, total;
+  size_t plan, cost, perm, units, qpool, kh, km, kl, vt, vbar16, kstats, kmom, total;
 };
 
 // Key blocks per head in the tiled operand planes: Nk rounded up to 64 (the
@@ -63,7 +64,8 @@ WsLayout ws_layout(int BH, int N, int d) {
   w.plan = round_up(sol::kHdrWords * 4, 256);
   w.cost = w.plan + 256;
   w.perm = round_up(w.cost + 4 * items, 256);
-  w.qpool = round_up(w.perm + 4 * items, 256);
+  w.units = round_up(w.perm + 4 * items, 256);
+  w.qpool = round_up(w.units + 4 * (size_t)BH * ((Nq + 1) / 2 + 8), 256);
   w.kh = round_up(w.qpool + (size_t)BH * Nq * (size_t)d * 4, 256);
   w.km = w.kh + tplane;
   w.kl = w.km + tplane;
@@ -105,6 +107,13 @@ int device_cus() {
 }
 
 constexpr float kGroup16MaxTau = 4.f;
+
+// A planned item whose estimated cost (the sizes of its pairs' unions, in
+// key blocks) reaches a quarter of the head's key blocks is handed out pair
+// by pair: its routing pass, a stream over all Nk pooled blocks, is then a
+// small part of each pair (at tau = 8 on the 32K-token layer typical items
+// cost about Nk / 8; items of heads that keep every block, 2 Nk).
+unsigned split_cost(int Nk) { return (unsigned)std::max(1, Nk / 4); }
 
 int auto_group(int BH, int Nq, const sol_attn_route& r) {
   const long long target = 6ll * device_cus();
@@ -193,14 +202,15 @@ hipError_t plan_impl(const uint16_t* q, const float* kpool, int BH, int N, int d
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   const int Nq = (N + 63) / 64, Nk = Nq;
   unsigned* perm = reinterpret_cast<unsigned*>(wsb + w.perm);
+  unsigned* units = reinterpret_cast<unsigned*>(wsb + w.units);
   unsigned* plan_items = reinterpret_cast<unsigned*>(wsb + w.plan);
   const int group = auto_group(BH, Nq, rowmax_route(tau));
   const int nitems = sol::forward_items(BH, Nq, group);
   *ordered = use_order(tau, nitems) && BH <= kMaxGridHeads;
   if (*ordered)
-    return sol::launch_plan(q, kpool, reinterpret_cast<unsigned*>(wsb + w.cost), perm, plan_items, BH, N, Nq, Nk,
-                            d, tau, (float)(1.0 / sqrt((double)d)), group, s);
-  return sol::launch_identity_order(perm, plan_items, nitems, s);
+    return sol::launch_plan(q, kpool, reinterpret_cast<unsigned*>(wsb + w.cost), perm, units, plan_items, BH, N, Nq,
+                            Nk, d, tau, (float)(1.0 / sqrt((double)d)), group, split_cost(Nk), s);
+  return sol::launch_identity_order(units, plan_items, nitems, group, s);
 }
 
 int check_route(const sol_attn_route& r, int N, int Bk) {
@@ -309,7 +319,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   const int group = group_of(flags, BH, Nq, route);
   const int nitems = sol::forward_items(BH, Nq, group);
 
-  const unsigned* perm = nullptr;
+  const unsigned* units = nullptr;
   hipError_t e = hipSuccess;
   // the pooling pre-pass (unless the workspace holds it already); the header
   // words are reset by it or, after sol_attn_prepare, by a reset kernel,
@@ -332,14 +342,14 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   if (e != hipSuccess) return SOL_EHIP;
   if (flags & SOL_F_PLANNED) {
     // the workspace holds a valid order from sol_attn_plan(), as a previous call left it
-    perm = reinterpret_cast<const unsigned*>(wsb + w.perm);
+    units = reinterpret_cast<const unsigned*>(wsb + w.units);
   } else {
     // plan the order of the work where that was measured to pay (elsewhere
     // the items go in sequence; the order never changes the result)
     if (e == hipSuccess && plan_by_default(route, BH, Nq, nitems, group)) {
       bool ordered = false;
       e = plan_impl(q16, kpool, BH, N, d, route.tau, ws, s, &ordered);
-      perm = reinterpret_cast<const unsigned*>(wsb + w.perm);
+      units = reinterpret_cast<const unsigned*>(wsb + w.units);
     }
   }
   if (e != hipSuccess) return SOL_EHIP;
@@ -361,7 +371,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   p.out = out;
   p.kpool = kpool;
   p.vmean = vmean;
-  p.perm = perm;
+  p.units = units;
   p.plan_items = reinterpret_cast<const unsigned*>(wsb + w.plan);
   p.hdr = static_cast<unsigned*>(ws);
   p.stats = stats;
@@ -375,6 +385,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   p.ngroups = (Nq + group - 1) / group;
   p.route_only = 0;
   p.static_grid = 0;
+  // without a plan, every block kept (tau = +inf): each queue's last items
+  // (one per workgroup of its XCD) go out pair by pair; the routing pass is
+  // then a small part of an item
+  p.split_n = route.rule == SOL_ROUTE_ROWMAX && isinf(route.tau) ? std::max(1, device_cus() / 4) : 0;
   p.kmom = kmom;
   p.rule = route.rule;
   p.tau = route.rule == SOL_ROUTE_ROWMAX ? route.tau : 0.f;

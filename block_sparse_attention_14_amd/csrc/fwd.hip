@@ -207,6 +207,7 @@ struct alignas(16) Small {
   unsigned long long st64[3];  // this workgroup's stats: kept blocks, total blocks, kept token pairs
   unsigned st32[2];            // fewest and most kept blocks of a query block
   int item;  // the item of the next iteration (-1: none left)
+  int pair;  // its one pair to process (-1: all of them)
   int last;  // this workgroup finished last
 };
 
@@ -272,12 +273,61 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
   const int home = (int)(blockIdx.x % kQueues);
   int qcur = 0;
   auto ticket = [&]() -> unsigned { return atomicAdd(p.hdr + kHdrQueue + 32 * ((home + qcur) & (kQueues - 1)), 1u); };
-  auto take = [&](unsigned t) -> int {
+  // Work units: an item (all its pairs) or one pair of an item, which is
+  // then routed once for each of its pairs taken so (so that the finish of
+  // the grid is set by pairs rather than by whole heavy items). With a plan
+  // made for this many items, queue x's tickets index its units; a plan made
+  // for another group size is ignored and the items go in sequence. A unit
+  // past the items, possible only with a workspace that was never planned,
+  // ends this workgroup's work instead of being followed. Without a plan,
+  // the last split_n items of each queue are handed out pair by pair.
+  constexpr int HP = G / 2;  // pairs per item
+  const unsigned* units = p.units != nullptr && *p.plan_items == (unsigned)p.nitems ? p.units : nullptr;
+  // the item of ticket t (or -1 when every queue is drained) and its pair
+  // (-1: all); a split-off pair that the head's last, partial group does not
+  // have is passed over
+  auto take = [&](unsigned t, int& pair) -> int {
     for (;;) {
       const int x = (home + qcur) & (kQueues - 1);
       const int lo = queue_begin(x, p.nitems), n = queue_begin(x + 1, p.nitems) - lo;
-      if (t < (unsigned)n) return lo + (int)t;
-      if (++qcur >= kQueues) return -1;
+      pair = -1;
+      int it = -1;
+      bool here = false;
+      if (units) {
+        if (t < p.plan_items[8 + x]) {
+          const unsigned u = units[(size_t)lo * HP + t];
+          const unsigned pb = HP >= 2 ? u >> 28 : 0u;
+          it = (int)(HP >= 2 ? u & 0x0fffffffu : u);
+          pair = (int)pb - 1;
+          here = true;
+        }
+      } else {
+        const int a = HP >= 2 && p.split_n > 0 ? max(0, n - p.split_n) : n;  // split ranks [a, n)
+        if (t < (unsigned)(a + HP * (n - a))) {
+          if (t < (unsigned)a) {
+            it = lo + (int)t;
+          } else {
+            it = lo + a + (int)(t - a) / HP;
+            pair = (int)(t - a) % HP;
+          }
+          here = true;
+        }
+      }
+      if (here) {
+        if (it < 0 || it >= p.nitems) {
+          pair = -1;
+          return -1;
+        }
+        if (pair >= 0 && G * (it % p.ngroups) + 2 * pair >= p.Nq) {
+          t = ticket();
+          continue;
+        }
+        return it;
+      }
+      if (++qcur >= kQueues) {
+        pair = -1;
+        return -1;
+      }
       t = ticket();
     }
   };
@@ -290,21 +340,16 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
     sm.st32[1] = 0u;
   }
 
-  // A planned order is followed only if it was made for this many items (a
-  // plan made for another group size is ignored: the items then go in
-  // sequence). An order entry out of range, possible only with a workspace
-  // that was never planned, ends this workgroup's work instead of being
-  // followed.
-  const unsigned* perm = p.perm != nullptr && *p.plan_items == (unsigned)p.nitems ? p.perm : nullptr;
-  auto item_of = [&](int rank) {
-    const unsigned it = rank < 0 ? ~0u : (perm ? perm[rank] : (unsigned)rank);
-    return it < (unsigned)p.nitems ? (int)it : -1;
-  };
-  if (tid == 0) sm.item = p.static_grid ? (int)blockIdx.x : item_of(take(ticket()));
+  if (tid == 0) {
+    int pr = -1;
+    sm.item = p.static_grid ? (int)blockIdx.x : take(ticket(), pr);
+    sm.pair = pr;
+  }
   __syncthreads();
   for (;;) {
     const int item = sm.item;
     if (item < 0) break;
+    const int ipair = sm.pair;  // (read before the next item's ticket overwrites it)
     const int bh = item / p.ngroups;  // head-major: neighbouring groups are consecutive tickets
     const int g0 = G * (item - bh * p.ngroups);
     const size_t hoff = (size_t)bh * N * D;
@@ -759,13 +804,18 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
     if constexpr (RO) {
       if (p.static_grid) break;
       __syncthreads();
-      if (tid == 0) sm.item = item_of(take(ticket()));
+      if (tid == 0) {
+        int pr = -1;
+        sm.item = take(ticket(), pr);
+        sm.pair = pr;
+      }
       __syncthreads();
       continue;
     } else {
 
     // ---- the pairs of the group: Q tiles, union list, kept loop, fold ----
-    for (int pr = 0; pr < G / 2; ++pr) {
+    const int pr_lo = ipair >= 0 ? ipair : 0, pr_hi = ipair >= 0 ? ipair + 1 : G / 2;
+    for (int pr = pr_lo; pr < pr_hi; ++pr) {
       // The lane indices pass through an empty asm statement, so that the
       // kept loop's per-lane offsets are formed here for every pair instead of
       // being hoisted out of the item loop and held in registers through the
@@ -777,7 +827,7 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
       if (qA >= Nq) break;
       const int gA = 2 * pr;
       const bool hasB = qA + 1 < Nq;
-      const bool lastpair = pr == G / 2 - 1 || qA + 2 >= Nq;
+      const bool lastpair = pr == pr_hi - 1 || qA + 2 >= Nq;
       const int nA = min(kBlk, N - qA * kBlk);
       const int nB = hasB ? min(kBlk, N - (qA + 1) * kBlk) : 0;
 
@@ -1168,7 +1218,11 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         }
         // the next item, resolved before this wave's stores, so that waiting
         // for the ticket never waits for them
-        if (lastpair && tid == 0) sm.item = p.static_grid ? -1 : item_of(take(next_ticket));
+        if (lastpair && tid == 0) {
+          int pr2 = -1;
+          sm.item = p.static_grid ? -1 : take(next_ticket, pr2);
+          sm.pair = pr2;
+        }
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           const int row = qrow0 + c16;

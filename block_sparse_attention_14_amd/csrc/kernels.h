@@ -41,13 +41,14 @@ struct FwdParams {
   void* out;             // [BH][N][d]: fp32, or bf16 when out_bf16
   const float* kpool;    // fp32 [BH][Nk][d]
   const float* vmean;    // fp32 [BH][Nk][d]
-  const unsigned* perm;  // nullable: rank -> item, within each queue's range
-  const unsigned* plan_items;  // with perm: the item count the order was made for
+  const unsigned* units;  // nullable: a plan's work units (launch_plan), queue x's at queue_begin(x) * group / 2
+  const unsigned* plan_items;  // with units: [0] the item count the plan was made for, [8 + x] queue x's units
   unsigned* hdr;         // workspace header (kHdr*), clean on entry
   sol_attn_stats* stats; // nullable, written by the last workgroup
   uint32_t* bitmap;      // nullable, [BH][Nq][nwords]
   int N, Nq, Nk, nitems, nwords;  // nitems = forward_items(BH, Nq, group)
-  int group;             // query blocks per work item: 2, 4, 8 or 16
+  int group;             // query blocks per work item: 2, 4, 6, 8 or 16
+  int split_n;           // items per queue handed out pair by pair (0: none)
   int ngroups;           // work items per head, ceil(Nq / group)
   int route_only;        // stop after routing (the kept-block bitmap is the only output)
   int static_grid;       // one workgroup per item, no queues, no header, no stats (route_only)
@@ -120,14 +121,18 @@ hipError_t launch_reset(unsigned* hdr, hipStream_t stream);
 // blocks, from sampled query means) and the order of each queue's range of
 // items of `group` query blocks (an item costs the sum over its pairs):
 // head-major, then its last third heaviest first.
-// perm[rank] = item, with rank and item in the same queue range; *plan_items
-// = the number of items the order is for.
-hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, unsigned* plan_items,
-                       int BH, int N, int Nq, int Nk, int d, float tau, float proxy_scale, int group,
-                       hipStream_t stream);
+// perm[rank] = item, with rank and item in the same queue range (scratch);
+// the queue's work units (an item, or one pair of an item whose estimated
+// cost reaches split_cost: item | (pair + 1) << 28) at units[queue_begin(x)
+// * group / 2 ...]; plan_items[0] = the number of items the order is for,
+// plan_items[8 + x] = the number of units of queue x.
+hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, unsigned* units,
+                       unsigned* plan_items, int BH, int N, int Nq, int Nk, int d, float tau, float proxy_scale,
+                       int group, unsigned split_cost, hipStream_t stream);
 
-// perm[i] = i for every item (the order of a plan that does not sort).
-hipError_t launch_identity_order(unsigned* perm, unsigned* plan_items, int nitems, hipStream_t stream);
+// One unit per item, each queue in sequence (the order of a plan that does
+// not sort), with the same plan_items words.
+hipError_t launch_identity_order(unsigned* units, unsigned* plan_items, int nitems, int group, hipStream_t stream);
 
 // The fused routing + exact + correction kernel (persistent grid).
 hipError_t launch_forward(const FwdParams& p, int d, hipStream_t stream);

@@ -234,22 +234,28 @@ __global__ __launch_bounds__(64 * kPlanWaves) void plan_kernel(const uint16_t* _
 // finish.
 // An item of G query blocks costs the sum over its G / 2 pairs, bucketed in
 // units of G / 2 so that the histogram keeps Nk + 1 buckets.
+// The queue is then written out as work units in this order: an item whose
+// estimated cost reaches split_cost (so that its routing pass is a small part
+// of it) becomes G / 2 units, one per pair, each routing the item again; any
+// other item one unit. Unit u = item | (pair + 1) << 28 (pair bits only for
+// G >= 4), at units[lo * G / 2 ...], their number in unit_counts[queue].
 __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict__ cost, unsigned* __restrict__ perm,
-                                                     unsigned* __restrict__ plan_items, int nitems, int Nk, int npairs,
-                                                     int group, int ngroups) {
+                                                     unsigned* __restrict__ units, unsigned* __restrict__ plan_items,
+                                                     int nitems, int Nk, int npairs, int group, int ngroups,
+                                                     unsigned split_cost) {
   extern __shared__ unsigned hist[];  // [Nk + 1] counts, then running offsets
   __shared__ unsigned part[1024];
   const int tid = threadIdx.x, nt = blockDim.x;
   const int lo = queue_begin(blockIdx.x, nitems), hi = queue_begin(blockIdx.x + 1, nitems);
   const int t0 = hi - (hi - lo) / 3;  // first item of the sorted tail
   const int hp = group / 2;           // pairs per item
-  auto bucket = [&](int i) {
+  auto item_cost = [&](int i) {
     const int bh = i / ngroups, p0 = hp * (i - bh * ngroups);
     unsigned c = 0;
     for (int t = 0; t < hp && p0 + t < npairs; ++t) c += cost[(size_t)bh * npairs + p0 + t];
-    return min(c / (unsigned)hp, (unsigned)Nk);
+    return c;
   };
-  if (blockIdx.x == 0 && tid == 0) *plan_items = (unsigned)nitems;
+  auto bucket = [&](int i) { return min(item_cost(i) / (unsigned)hp, (unsigned)Nk); };
   for (int i = lo + tid; i < t0; i += nt) perm[i] = (unsigned)i;
   for (int b = tid; b <= Nk; b += nt) hist[b] = 0u;
   __syncthreads();
@@ -282,25 +288,67 @@ __global__ __launch_bounds__(1024) void order_kernel(const unsigned* __restrict_
   }
   __syncthreads();
   for (int i = t0 + tid; i < hi; i += nt) perm[atomicAdd(&hist[bucket(i)], 1u)] = (unsigned)i;
+  __threadfence_block();
+  __syncthreads();  // the queue's order is complete
+
+  // work units in the order's sequence: an exclusive scan of the units per
+  // rank, 1024 ranks at a time
+  unsigned* out = units + (size_t)lo * hp;
+  unsigned base = 0;
+  for (int r0 = lo; r0 < hi; r0 += nt) {
+    const int r = r0 + tid;
+    unsigned it = 0, nu = 0;
+    if (r < hi) {
+      it = perm[r];
+      nu = hp >= 2 && item_cost((int)it) >= split_cost ? (unsigned)hp : 1u;
+    }
+    part[tid] = nu;
+    __syncthreads();
+    for (int off = 1; off < nt; off <<= 1) {  // inclusive scan
+      const unsigned v = tid >= off ? part[tid - off] : 0u;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
+    }
+    const unsigned at = base + part[tid] - nu;
+    if (nu == 1u)
+      out[at] = it;
+    else
+      for (unsigned k = 0; k < nu; ++k) out[at + k] = it | ((k + 1u) << 28);
+    base += part[nt - 1];
+    __syncthreads();  // part is rewritten by the next chunk
+  }
+  if (tid == 0) {
+    plan_items[8 + blockIdx.x] = base;
+    if (blockIdx.x == 0) *plan_items = (unsigned)nitems;
+  }
 }
 
-__global__ __launch_bounds__(256) void iota_kernel(unsigned* __restrict__ perm, unsigned* __restrict__ plan_items,
-                                                   int nitems) {
+// The identity order as work units: one per item, each queue in sequence.
+__global__ __launch_bounds__(256) void iota_kernel(unsigned* __restrict__ units, unsigned* __restrict__ plan_items,
+                                                   int nitems, int hp) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i == 0) *plan_items = (unsigned)nitems;
-  if (i < nitems) perm[i] = (unsigned)i;
+  if (i < kQueues) plan_items[8 + i] = (unsigned)(queue_begin(i + 1, nitems) - queue_begin(i, nitems));
+  if (i < nitems) {
+    int x = 0;
+    while (x + 1 < kQueues && queue_begin(x + 1, nitems) <= i) ++x;
+    const int lo = queue_begin(x, nitems);
+    units[(size_t)lo * hp + (i - lo)] = (unsigned)i;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_identity_order(unsigned* perm, unsigned* plan_items, int nitems, hipStream_t stream) {
-  hipLaunchKernelGGL(iota_kernel, dim3((nitems + 255) / 256), dim3(256), 0, stream, perm, plan_items, nitems);
+hipError_t launch_identity_order(unsigned* units, unsigned* plan_items, int nitems, int group, hipStream_t stream) {
+  hipLaunchKernelGGL(iota_kernel, dim3((nitems + 255) / 256), dim3(256), 0, stream, units, plan_items, nitems,
+                     group / 2);
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, unsigned* plan_items,
-                       int BH, int N, int Nq, int Nk, int d, float tau, float proxy_scale, int group,
-                       hipStream_t stream) {
+hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, unsigned* perm, unsigned* units,
+                       unsigned* plan_items, int BH, int N, int Nq, int Nk, int d, float tau, float proxy_scale,
+                       int group, unsigned split_cost, hipStream_t stream) {
   const dim3 grid((Nq + kPlanQ - 1) / kPlanQ, BH);
   if (d == 128)
     hipLaunchKernelGGL(plan_kernel<128>, grid, dim3(64 * kPlanWaves), 0, stream, q, kpool, cost, N, Nq, Nk, tau,
@@ -312,7 +360,7 @@ hipError_t launch_plan(const uint16_t* q, const float* kpool, unsigned* cost, un
   if (e != hipSuccess) return e;
   const int nitems = forward_items(BH, Nq, group);
   hipLaunchKernelGGL(order_kernel, dim3(kQueues), dim3(1024), (size_t)(Nk + 1) * sizeof(unsigned), stream, cost,
-                     perm, plan_items, nitems, Nk, (Nq + 1) / 2, group, (Nq + group - 1) / group);
+                     perm, units, plan_items, nitems, Nk, (Nq + 1) / 2, group, (Nq + group - 1) / group, split_cost);
   return hipGetLastError();
 }
 
