@@ -189,9 +189,12 @@ int sol_attn_pool(const void* k, const void* v, float* kpool, float* vmean,
  * products of query means sampled from every 4th row and the pooled keys)
  * and orders each work queue: its first two thirds in sequence (neighbouring
  * query blocks keep overlapping key blocks and share them in L2), its last
- * third heaviest first. A scheduling aid only: the forward still routes every
- * block itself, in fp32, and nothing routing-related is written to device
- * memory beyond one count per item. For tau = +inf (and very large B*H*N)
+ * third heaviest first; an item estimated at a quarter of the head's key
+ * blocks or more (its routing pass then a small part of it) is handed out
+ * one pair of query blocks at a time, each routing the item again. A
+ * scheduling aid only: the forward still routes every block itself, in
+ * fp32, and nothing routing-related is written to device memory beyond one
+ * count per item and the order. For tau = +inf (and very large B*H*N)
  * the order is the identity. The items are those of the forward's automatic
  * group size at this tau (their count is recorded with the order). Resets
  * the workspace's queue and stats words.
