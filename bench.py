@@ -502,12 +502,23 @@ def main():
 
 
 def cpu_model() -> str:
-    """The host CPU's model name, as lscpu reports it (else /proc/cpuinfo)."""
+    """The host CPU's model name, as lscpu reports it (else /proc/cpuinfo);
+    a name without a model number (some virtual machines report only the
+    brand) gets lscpu's CPU family, model and stepping appended."""
     try:
         r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20)
+        fields = {}
         for ln in r.stdout.splitlines():
-            if ln.strip().lower().startswith("model name"):
-                return ln.split(":", 1)[1].strip()
+            if ":" in ln:
+                key, val = ln.split(":", 1)
+                fields.setdefault(key.strip().lower(), val.strip())
+        name = fields.get("model name")
+        if name:
+            if not any(ch.isdigit() for ch in name):
+                ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if fields.get(k)]
+                if ids:
+                    name += " (" + ", ".join(ids) + ")"
+            return name
     except (OSError, subprocess.SubprocessError):
         pass
     try:
