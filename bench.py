@@ -437,7 +437,8 @@ def main():
     if not args.no_ablation and not args.profile_only:
         abl = {"reference": "this kernel at tau = +inf (dense attention)",
                "video_dit_32k": ablation("video_dit_32k", (2.0, 4.0, 8.0)),
-               "video_dit_32k_smoothv": ablation("video_dit_32k_smoothv", (2.0, 4.0, 8.0))}
+               "video_dit_32k_smoothv": ablation("video_dit_32k_smoothv", (2.0, 4.0, 8.0)),
+               "video_dit_32k_mild": ablation("video_dit_32k_mild", (1.0, 2.0, 4.0))}
         print(f"[bench] ablation {json.dumps(abl)}", file=sys.stderr, flush=True)
 
     per_wl = None

@@ -141,6 +141,48 @@ def test_video_dit_32k_imbalance(imbalance32k, heads):
 
 
 @pytest.fixture(scope="module")
+def mild32k():
+    return make_inputs(get_workload("video_dit_32k_mild"))
+
+
+@pytest.mark.parametrize("tau", [1.0, 2.0])
+def test_video_dit_32k_mild(mild32k, tau):
+    """The milder-locality layer with smooth values: every row of all 12
+    heads, block-level correction, and the per-row correction's stratified
+    sample with head 7 on every row."""
+    wl = get_workload("video_dit_32k_mild")
+    _full_parity(wl, tau, mild32k)
+    _full_parity(wl, tau, mild32k, flags=RC, stratified=True, whole_heads=(7,), seed=int(tau) + 40)
+
+
+def test_video_dit_32k_mild_tau4(mild32k):
+    """tau = 4 keeps about a third of the blocks here: the stratified sample and
+    head 2 on every row."""
+    _full_parity(get_workload("video_dit_32k_mild"), 4.0, mild32k, stratified=True, whole_heads=(2,), seed=44)
+
+
+@pytest.mark.parametrize("tau", [1.0, 2.0])
+def test_correction_ablation_on_the_gpu(mild32k, tau):
+    """§4 "Ablations" on the GPU: against this kernel's dense output (tau =
+    +inf) on the mild layer, per-row correction < block-level correction <
+    exact-only attention over the same kept blocks, in relative L2 error over
+    all 12 heads (the oracle pins the same order on a reduced layer)."""
+    wl = get_workload("video_dit_32k_mild")
+    q, k, v = (to_device_bf16(mild32k[n]) for n in "qkv")
+    r = sa.SolAttention(wl.B, wl.H, wl.N, wl.d)
+    dense = r(q, k, v, INF).double()
+
+    def err(flags):
+        o = r(q, k, v, tau, flags=flags).double()
+        return float((o - dense).norm() / dense.norm())
+
+    blk, row, exact = err(0), err(RC), err(sa.SOL_F_EXACT_ONLY)
+    print(f"[ablation] video_dit_32k_mild tau={tau}: row {row:.4f} block {blk:.4f} exact-only {exact:.4f}", flush=True)
+    assert row < blk < exact, (row, blk, exact)
+    assert blk < 0.85 * exact, (blk, exact)
+
+
+@pytest.fixture(scope="module")
 def video119k():
     return make_inputs(get_workload("video_dit_119k"))
 

@@ -425,6 +425,35 @@ def test_correction_beats_exact_only_on_a_smooth_layer():
         assert err_c < err_e, (tau, err_c, err_e)
 
 
+def test_correction_order_on_a_mild_layer():
+    """§4 "Ablations" and App. B: on a layer built like video_dit_32k_mild
+    (milder locality, half-scale per-token draws of q and k, smooth values),
+    reduced to a 4x16x32 grid at d = 128, the skipped blocks hold a visible
+    share of the attention mass, and the outputs order as the pages describe:
+    token-to-block correction closer to dense attention than block-level
+    correction, which is closer than exact-only attention on the same blocks."""
+    from workloads.gen import pos_code
+
+    grid, d = (4, 16, 32), 128
+    N = grid[0] * grid[1] * grid[2]
+    P = pos_code(grid, d).astype(np.float64)
+    rng = np.random.default_rng(11)
+    q = 0.5 * rng.standard_normal((N, d)) + 1.5 * P
+    k = 0.5 * rng.standard_normal((N, d)) + 1.5 * P
+    v = rng.standard_normal((N, d)) + 3 * P
+    dense = sdpa64(q, k, v)
+
+    def err(o):
+        return np.linalg.norm(o - dense) / np.linalg.norm(dense)
+
+    for tau in (1.0, 2.0):
+        row = err(attend_head(q, k, v, 64, 64, tau, row_correction=True)["out"])
+        blk = err(attend_head(q, k, v, 64, 64, tau)["out"])
+        exact = err(attend_head(q, k, v, 64, 64, tau, correction=False)["out"])
+        assert row < blk < exact, (tau, row, blk, exact)
+        assert blk < 0.8 * exact, (tau, blk, exact)
+
+
 # ---------------------------------------------------------------------------
 # Top-k and top-p masks, the routing baselines of §2 "Block-Sparse Attention"
 # ---------------------------------------------------------------------------

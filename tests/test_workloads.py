@@ -23,6 +23,7 @@ def test_workload_shapes():
         "video_dit_32k": (1, 12, 32760, 128, 512),
         "video_dit_32k_imbalance": (1, 12, 32760, 128, 512),
         "video_dit_32k_smoothv": (1, 12, 32760, 128, 512),
+        "video_dit_32k_mild": (1, 12, 32760, 128, 512),
         "video_dit_119k": (1, 24, 118800, 128, 1857),
     }
     for name, (B, H, N, d, Nq) in expect.items():
@@ -86,7 +87,8 @@ def test_imbalance_construction():
 
 def test_all_workloads_registered():
     assert set(WORKLOADS) == {"tiny_fp32", "image_dit_4k", "video_dit_32k",
-                              "video_dit_32k_imbalance", "video_dit_32k_smoothv", "video_dit_119k"}
+                              "video_dit_32k_imbalance", "video_dit_32k_smoothv", "video_dit_32k_mild",
+                              "video_dit_119k"}
 
 
 def test_smooth_values_share_the_position_code():
@@ -98,3 +100,21 @@ def test_smooth_values_share_the_position_code():
     # v = noise + 3 P: its projection on P is about 3 |P|^2 per token
     c = float((v.astype(np.float64) * P).sum() / (P * P).sum())
     assert abs(c - 3.0) < 0.05
+
+
+def test_mild_layer_scales_the_draws():
+    """video_dit_32k_mild: q and k are 0.5 N(0, 1) + 1.5 P(pos), v is N(0, 1) + 3 P(pos);
+    the other layers keep unit draws (their generated bits are unchanged)."""
+    from workloads.gen import _pos32, make_head
+
+    w = get_workload("video_dit_32k_mild")
+    q, k, v = make_head(w, 0, 3)
+    P = _pos32(w.grid, w.d)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 0, 3])))
+    zq = rng.standard_normal((w.N, w.d), dtype=np.float32)
+    zk = rng.standard_normal((w.N, w.d), dtype=np.float32)
+    zv = rng.standard_normal((w.N, w.d), dtype=np.float32)
+    np.testing.assert_array_equal(q, np.float32(0.5) * zq + np.float32(1.5) * P)
+    np.testing.assert_array_equal(k, np.float32(0.5) * zk + np.float32(1.5) * P)
+    np.testing.assert_array_equal(v, zv + np.float32(3.0) * P)
+    assert get_workload("video_dit_32k").qk_noise == 1.0

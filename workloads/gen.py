@@ -47,6 +47,8 @@ class Workload:
     sink_blocks: int = 0
     # scale of the position code added to v (0: values independent per token)
     value_locality: float = 0.0
+    # scale of the per-token N(0, 1) draws of q and k (1: unit noise)
+    qk_noise: float = 1.0
     description: str = ""
 
     @property
@@ -112,6 +114,14 @@ WORKLOADS: Dict[str, Workload] = {
             taus=(2.0, 4.0, 8.0), seed=1005, value_locality=3.0,
             description=("video-DiT layer, N=32760, values sharing the position code "
                          "(spatially smooth), for the correction ablation"),
+        ),
+        _wl(
+            name="video_dit_32k_mild",
+            B=1, H=12, grid=(21, 30, 52), d=128, dtype="bf16",
+            taus=(1.0, 2.0, 4.0), seed=1006, locality=(1.5,) * 12, qk_noise=0.5, value_locality=3.0,
+            description=("video-DiT layer, N=32760, milder locality (1.5 P(pos) on q and k, per-token "
+                         "draws of q and k at half scale) and smooth values: skipped blocks hold a "
+                         "share of the attention mass that the correction can recover"),
         ),
         _wl(
             name="video_dit_119k",
@@ -205,6 +215,9 @@ def make_head(wl: Workload, b: int, h: int) -> Tuple[np.ndarray, np.ndarray, np.
     q = rng.standard_normal((N, d), dtype=np.float32)
     k = rng.standard_normal((N, d), dtype=np.float32)
     v = rng.standard_normal((N, d), dtype=np.float32)
+    if wl.qk_noise != 1.0:
+        q *= np.float32(wl.qk_noise)
+        k *= np.float32(wl.qk_noise)
     alpha = wl.head_locality(h)
     if alpha != 0.0:
         P = _pos32(wl.grid, d)
