@@ -907,6 +907,7 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         for (int dt = 0; dt < NDT; ++dt) accO[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       float m[2] = {-INFINITY, -INFINITY};
+      float mlim[2] = {-INFINITY, -INFINITY};  // m + kLazyRescale
       {
         const bf16x8 ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
         const uint16_t* kh = p.k + hoff;
@@ -1018,11 +1019,15 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
                   st[1][kt][i] = -INFINITY;
                 }
           }
+          // The lazily raised maximum: each lane compares the maximum of its own
+          // 16 scores with its row's limit m + kLazyRescale (a row's maximum
+          // passes the limit iff one of its four lanes' does); the rows' maxima
+          // are formed, and the state rescaled, only when some row of the wave
+          // passes its limit.
           bool raise = false;
-          float mn[2];
+          float lm[2];
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
-            mn[qt] = m[qt];
             if (!((QM >> qt) & 1)) continue;
             // two chains of three-input maxima over the lane's 16 scores
             float b0 = fmaxf(fmaxf(st[qt][0][0], st[qt][0][1]), st[qt][0][2]);
@@ -1033,19 +1038,21 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
             b1 = fmaxf(fmaxf(b1, st[qt][3][1]), st[qt][3][2]);
             b0 = fmaxf(b0, st[qt][1][3]);
             b1 = fmaxf(b1, st[qt][3][3]);
-            const float bm = rowmax4(fmaxf(b0, b1)) * csc;
-            mn[qt] = bm > m[qt] + kLazyRescale ? bm : m[qt];
-            raise = raise || (mn[qt] != m[qt]);
+            lm[qt] = fmaxf(b0, b1);
+            raise = raise || (lm[qt] * csc > mlim[qt]);
           }
           if (__ballot(raise)) {  // rare: a row's max rose by more than the lazy margin
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
               if (!((QM >> qt) & 1)) continue;
-              const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn[qt]);
+              const float bm = rowmax4(lm[qt]) * csc;
+              const float mn = bm > mlim[qt] ? bm : m[qt];
+              const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
               lsum[qt] *= alpha;
 #pragma unroll
               for (int dt = 0; dt < NDT; ++dt) accO[qt][dt] *= alpha;
-              m[qt] = mn[qt];
+              m[qt] = mn;
+              mlim[qt] = mn + kLazyRescale;
             }
           }
           // P^T operand slots 0-3 = keys 32ks+4g+i, slots 4-7 = keys 32ks+16+4g+i
