@@ -1083,29 +1083,28 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           // 32ks + 4g + e and 32ks + 16 + 4g + e give exactly the keys of the P^T
           // slots; each V^T operand serves the query tiles that take part
           const unsigned char* vstage = kPooled ? stB : stage;
-          // V^T operands of the next 16 rows of d read while this slice's MFMAs run
-          auto vread = [&](int dt, uint2 (&o)[4]) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              o[2 * ks] = ld_tr(vstage + voffs[dt] + 32 * ks * GM::RB);
-              o[2 * ks + 1] = ld_tr(vstage + voffs[dt] + (32 * ks + 16) * GM::RB);
-            }
+          // the O^T products in 16 slices t = 16 rows of d (dt = t % NDT) x 32 keys
+          // (ks = t / NDT), each accumulator taking its two key steps in order;
+          // the V^T operands of slice t + VA are read while slice t's MFMAs run
+          auto vread = [&](int t, uint2 (&o)[2]) {
+            const int dt = t % NDT, ks = t / NDT;
+            o[0] = ld_tr(vstage + voffs[dt] + 32 * ks * GM::RB);
+            o[1] = ld_tr(vstage + voffs[dt] + (32 * ks + 16) * GM::RB);
           };
-          uint2 vc[4], vn[4];
-          vread(0, vc);
+          constexpr int VA = 3;
+          constexpr int NT = 2 * NDT;
+          uint2 vo[NT][2];
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            if (dt + 1 < NDT) vread(dt + 1, vn);
+          for (int t = 0; t < VA; ++t) vread(t, vo[t]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            if (t + VA < NT) vread(t + VA, vo[t + VA]);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              const bf16x8 a = as_bf16x8(make_uint4(vc[2 * ks].x, vc[2 * ks].y, vc[2 * ks + 1].x, vc[2 * ks + 1].y));
-              if (QM & 1) accO[0][dt] = mfma16x16x32(a, pb[0][ks], accO[0][dt]);
-              if (QM & 2) accO[1][dt] = mfma16x16x32(a, pb[1][ks], accO[1][dt]);
-            }
+            const int dt = t % NDT, ks = t / NDT;
+            const bf16x8 a = as_bf16x8(make_uint4(vo[t][0].x, vo[t][0].y, vo[t][1].x, vo[t][1].y));
+            if (QM & 1) accO[0][dt] = mfma16x16x32(a, pb[0][ks], accO[0][dt]);
+            if (QM & 2) accO[1][dt] = mfma16x16x32(a, pb[1][ks], accO[1][dt]);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) vc[e2] = vn[e2];
           }
         };
 
