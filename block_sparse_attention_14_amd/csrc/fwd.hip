@@ -105,6 +105,11 @@ constexpr int kThreads = 256;
 // this (base-2 units); until then probabilities may reach 2^8, which fp32 and
 // bf16 carry as exactly (relatively) as values below 1.
 constexpr float kLazyRescale = 8.0f;
+// Union runs longer than this wait for each stage-B copy before the stage-A
+// step (see the kept loop).
+constexpr int kLongRun = 64;
+// s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kVmcnt0 = 0x0F70;
 // max over the four lanes l, l^16, l^32, l^48 that share one query row
 __device__ __forceinline__ float rowmax4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -866,6 +871,7 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
       // reading a word's bits from LDS when the walk reaches it. Wave 0
       // counts the pair's kept blocks for the stats.
       uint64_t nz0, nz1 = 0ull;
+      int run_len[3];  // union entries kept by both blocks, by the first only, by the second only
       {
         const int nw = (Nk + 31) / 32;
         auto uword = [&](int w) -> uint32_t {
@@ -873,6 +879,20 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         };
         nz0 = __ballot(uword(lane) != 0u);
         if constexpr (KW > 64) nz1 = __ballot(uword(64 + lane) != 0u);
+        // the lengths of the three runs (every wave; they pick the copy
+        // schedule of each run, step 3)
+        {
+          int cboth = 0, cfirst = 0, csecond = 0;
+          for (int w = lane; w < nw; w += 64) {
+            const uint32_t a = sm.kbits[gA][w], b = hasB ? sm.kbits[gA + 1][w] : 0u;
+            cboth += __popc(a & b);
+            cfirst += __popc(a & ~b);
+            csecond += __popc(b & ~a);
+          }
+          run_len[0] = __builtin_amdgcn_readfirstlane(wave_sum_int(cboth));
+          run_len[1] = __builtin_amdgcn_readfirstlane(wave_sum_int(cfirst));
+          run_len[2] = __builtin_amdgcn_readfirstlane(wave_sum_int(csecond));
+        }
         if (wid == 0) {
           int ca = 0, cb = 0;
           for (int w = lane; w < nw; w += 64) {
@@ -913,9 +933,11 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         const uint16_t* kh = p.k + hoff;
         const uint16_t* vh = p.v + hoff;
         // K and V tiles of the union entry e (key block e & 0x3fff) into one stage
+        // (e < 0, past the end of a run: an empty copy, every load out of range,
+        // so that a copy can be issued without a branch around it)
         auto dma = [&](unsigned char* stage, int e) {
-          const int j = e & 0x3fff;
-          const uint32_t bytes = (uint32_t)min(kBlk, N - j * kBlk) * D * 2;
+          const int j = e < 0 ? 0 : e & 0x3fff;
+          const uint32_t bytes = e < 0 ? 0u : (uint32_t)min(kBlk, N - j * kBlk) * D * 2;
           dma_tile<D>(stage, make_rsrc(kh + (size_t)j * kBlk * D, bytes), make_rsrc(vh + (size_t)j * kBlk * D, bytes),
                       wid, lane);
         };
@@ -1141,28 +1163,37 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           };
           // Every barrier below is preceded by an explicit wait for all of
           // this wave's outstanding copies: the copy into one stage is issued
-          // in one loop iteration and consumed in the next, a dependency the
-          // compiler's own wait insertion does not carry across the loop
-          // back-edge.
+          // before the other stage's step and consumed after it. The loop is
+          // rotated so that no copy is in flight across its back-edge and each
+          // copy sits in the same block as the step after it (the copy past a
+          // run's end is an empty one): the compiler's own wait insertion then
+          // sees that the step's reads of one stage do not touch the other
+          // (with a copy in flight at the loop head it waited for that copy
+          // before every step on stage A). Runs longer than kLongRun entries
+          // (dense-like pairs) still wait for the stage-B copy before the
+          // stage-A step: overlapping every copy there measured 6% slower on
+          // dense calls and 3% slower on a layer with diffuse heads, while it
+          // pays on the short runs of sparse pairs.
+          const bool waitb = run_len[QM == 3 ? 0 : QM == 1 ? 1 : 2] > kLongRun;
           int eA = next();
           int eB = eA >= 0 ? next() : -1;
           if (eA >= 0) dma(stA, eA);
-          if (eB >= 0) dma(stB, eB);
           __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();  // the first two tiles are in LDS
+          __syncthreads();  // the first tile is in LDS
           while (eA >= 0) {
+            // stage A holds entry eA; nothing in flight
+            dma(stB, eB);
+            if (waitb) __builtin_amdgcn_s_waitcnt(kVmcnt0);
             compute(stA, eA, std::false_type{}, qmask);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // stage B's tile has landed; nobody reads stage A any more
-            eA = eB >= 0 ? next() : -1;
-            if (eA >= 0) dma(stA, eA);
-            if (eB >= 0) {
-              compute(stB, eB, std::false_type{}, qmask);
-              __builtin_amdgcn_s_waitcnt(0);
-              __syncthreads();  // stage A's tile has landed; nobody reads stage B any more
-              eB = eA >= 0 ? next() : -1;
-              if (eB >= 0) dma(stB, eB);
-            }
+            if (eB < 0) break;
+            eA = next();
+            dma(stA, eA);
+            compute(stB, eB, std::false_type{}, qmask);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();  // stage A's tile has landed; nobody reads stage B any more
+            eB = eA >= 0 ? next() : -1;
           }
         };
         run(kBoth{});
