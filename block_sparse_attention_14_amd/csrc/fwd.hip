@@ -943,13 +943,23 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         };
         // pooled tile c (per-row correction): the two bf16 parts of the pooled
         // keys fill stage A (both as K rows), the pooled values stage B's V half
-        auto dma_pooled = [&](int c) {
-          // (the tiled key planes hold zeros past Nk; the row-major values are bounded)
-          const size_t toff = ((size_t)bh * p.Nkp + (size_t)c * kBlk) * D;
-          dma_one<D, true, true>(stA, make_rsrc(p.khi16 + toff, GM::TILE), wid, lane);
-          dma_one<D, true, true>(stA + GM::TILE, make_rsrc(p.klo16 + toff, GM::TILE), wid, lane);
-          const uint32_t bytes = (uint32_t)min(kBlk, Nk - c * kBlk) * D * 2;
-          const size_t off = ((size_t)bh * Nk + (size_t)c * kBlk) * D;
+        // pooled tile c (per-row correction): the two bf16 parts of the pooled
+        // keys into stage A (both as K rows), the pooled values into stage B's
+        // V half. c = npool: empty copies (every load out of range), so that
+        // no branch separates a copy from the reads after it.
+        const int npool = (Nk + kBlk - 1) / kBlk;
+        auto dma_pooled_keys = [&](int c) {
+          // (the tiled key planes hold zeros past Nk)
+          const bool on = c < npool;
+          const size_t toff = ((size_t)bh * p.Nkp + (size_t)(on ? c : 0) * kBlk) * D;
+          dma_one<D, true, true>(stA, make_rsrc(p.khi16 + toff, on ? GM::TILE : 0u), wid, lane);
+          dma_one<D, true, true>(stA + GM::TILE, make_rsrc(p.klo16 + toff, on ? GM::TILE : 0u), wid, lane);
+        };
+        auto dma_pooled_vals = [&](int c) {
+          // (the row-major values are bounded)
+          const bool on = c < npool;
+          const uint32_t bytes = on ? (uint32_t)min(kBlk, Nk - c * kBlk) * D * 2 : 0u;
+          const size_t off = ((size_t)bh * Nk + (size_t)(on ? c : 0) * kBlk) * D;
           dma_one<D, false>(stB + GM::TILE, make_rsrc(p.vbar16 + off, bytes), wid, lane);
         };
         // per-lane byte offsets of the swizzled operand reads (independent of the key tile kt)
@@ -967,7 +977,9 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         // QM: the query tiles that take part (bit 0: the first block's, bit
         // 1: the second's), i.e. the blocks of the pair that keep the entry;
         // a tile that does not take part costs nothing
-        auto compute = [&](const unsigned char* stage, int e, auto pooled, auto qmask) __attribute__((always_inline)) {
+        // mid(): called between the probabilities and the O^T products (the
+        // pooled tiles' copy schedule; nothing for the exact tiles)
+        auto compute = [&](const unsigned char* stage, int e, auto pooled, auto qmask, auto mid) __attribute__((always_inline)) {
           constexpr bool kPooled = decltype(pooled)::value;
           constexpr int QM = decltype(qmask)::value;
           const int j = e & 0x3fff;
@@ -1105,6 +1117,7 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
           // 32ks + 4g + e and 32ks + 16 + 4g + e give exactly the keys of the P^T
           // slots; each V^T operand serves the query tiles that take part
           const unsigned char* vstage = kPooled ? stB : stage;
+          mid();
           // the O^T products in 16 slices t = 16 rows of d (dt = t % NDT) x 32 keys
           // (ks = t / NDT), each accumulator taking its two key steps in order;
           // the V^T operands of slice t + VA are read while slice t's MFMAs run
@@ -1184,13 +1197,13 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
             // stage A holds entry eA; nothing in flight
             dma(stB, eB);
             if (waitb) __builtin_amdgcn_s_waitcnt(kVmcnt0);
-            compute(stA, eA, std::false_type{}, qmask);
+            compute(stA, eA, std::false_type{}, qmask, [] {});
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // stage B's tile has landed; nobody reads stage A any more
             if (eB < 0) break;
             eA = next();
             dma(stA, eA);
-            compute(stB, eB, std::false_type{}, qmask);
+            compute(stB, eB, std::false_type{}, qmask, [] {});
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // stage A's tile has landed; nobody reads stage B any more
             eB = eA >= 0 ? next() : -1;
@@ -1200,24 +1213,50 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         run(kFirst{});
         run(kSecond{});
         if (RC) {
-          // pooled tiles, one at a time: each fills stage A and half of stage B
-          const int npool = (Nk + kBlk - 1) / kBlk;
-          for (int c = 0; c < npool; ++c) {
-            // a tile whose key blocks both rows keep holds only masked pooled
-            // keys (all of them, at tau = +inf): skipped, the same decision in
-            // every thread (kept bits in LDS), so the barriers stay matched
+          // Pooled tiles in turn. A tile whose key blocks both rows keep holds
+          // only masked pooled keys (all of them, at tau = +inf) and is passed
+          // over, the same decision in every thread (kept bits in LDS), so the
+          // barriers stay matched. The next tile's key parts are copied once
+          // every wave is past this tile's score products (they land during
+          // its O^T products), its values once every wave is past this tile's
+          // O^T products (they land during the next score products).
+          auto needed = [&](int c) -> bool {
             const int nv = min(kBlk, Nk - c * kBlk);
             const uint64_t valid = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
             const uint64_t ka = (uint64_t)sm.kbits[gA][2 * c] | ((uint64_t)sm.kbits[gA][2 * c + 1] << 32);
             const uint64_t kb = hasB ? ((uint64_t)sm.kbits[gA + 1][2 * c] | ((uint64_t)sm.kbits[gA + 1][2 * c + 1] << 32))
                                      : valid;
-            if ((valid & ~ka) == 0 && (valid & ~kb) == 0) continue;
-            dma_pooled(c);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();  // pooled tile c is in LDS
-            compute(stA, c, std::true_type{}, kBoth{});
-            __syncthreads();  // nobody reads the pooled tile any more
+            return (valid & ~ka) != 0 || (valid & ~kb) != 0;
+          };
+          auto next_tile = [&](int c) {
+            while (c < npool && !needed(c)) ++c;
+            return c;
+          };
+          // s_waitcnt operand: all but the last value copy's loads (this
+          // wave's loads complete in issue order)
+          constexpr int kWaitKeys = kVmcnt0 | (GM::NCH / 4);
+          int c = next_tile(0);
+          dma_pooled_keys(c);
+          dma_pooled_vals(c);
+          // (the barriers below wait for LDS work only: each wave first waits
+          // explicitly for the copies the next step reads)
+          // (the next tile is looked up where no copy is in flight: the
+          // compiler would otherwise wait for the copies before its LDS reads)
+          while (c < npool) {
+            __builtin_amdgcn_s_waitcnt(kWaitKeys);
+            lds_barrier();  // tile c's key parts are in LDS
+            int cn = npool;
+            compute(stA, c, std::true_type{}, kBoth{}, [&] {
+              __builtin_amdgcn_s_waitcnt(0);
+              lds_barrier();  // tile c's values are in LDS; nobody reads its key parts any more
+              cn = next_tile(c + 1);
+              dma_pooled_keys(cn);
+            });
+            lds_barrier();  // nobody reads tile c's values any more
+            dma_pooled_vals(cn);
+            c = cn;
           }
+          __builtin_amdgcn_s_waitcnt(0);  // the empty copies past the last tile
         }
       }
 
