@@ -61,16 +61,22 @@
 //      the three copies apart);
 //   3. for every union entry, the K and V tiles stream from HBM straight into
 //      LDS (buffer loads with an LDS destination, no registers involved),
-//      double-buffered in two stages, one barrier per tile. 16-byte chunks are
+//      double-buffered in two stages, one barrier per tile: the copy into one
+//      stage runs during the other stage's step (runs of more than 64 entries,
+//      dense-like pairs, wait for it before the stage-A step). 16-byte chunks are
 //      XOR-swizzled per row through the per-lane source addresses, so both
 //      operand reads below are bank-conflict free. Every wave computes the
 //      64 x 16 S^T tile of each of its query tiles whose block keeps the
 //      entry (so all four waves work on every entry) with 16x16x32 bf16
 //      MFMAs, the online
-//      softmax in base 2 with a lazily raised maximum (one query row per lane:
-//      two permlane swaps reduce a row), the row sums as an MFMA against a
+//      softmax in base 2 with a lazily raised maximum (one query row per lane;
+//      each lane tests its own scores against the row's limit, and two
+//      permlane swaps reduce a row when one passes it), the row sums as an MFMA against a
 //      ones operand, and O^T += V^T P^T with V^T operands read from the
 //      row-major V tile by transposing LDS reads (ds_read_b64_tr_b16);
+//      With the per-row (token-to-block) correction, the pooled tiles follow
+//      through the same step: the next tile's key parts are copied during
+//      this tile's O^T products, its values during the next score products;
 //   4. exact state and correction merge under a common maximum; rows are
 //      normalised and stored in fp32 (or rounded to bf16 on request). After
 //      the last pair the next item's ticket is resolved before the stores and
