@@ -80,7 +80,8 @@ def parse(argv=None):
     ap.add_argument("--taus", default="2,4,8,inf", help="taus reported alongside the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle baseline")
-    ap.add_argument("--profile-only", action="store_true", help="headline tau only, for profilers")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="headline tau only, the fused kernel only in default calls and split stages (for profilers)")
     ap.add_argument("--no-ablation", action="store_true", help="skip the correction ablation report")
     ap.add_argument("--no-routing-cost", action="store_true", help="skip the router comparison")
     ap.add_argument("--no-rules", action="store_true", help="skip the Gaussian-rule and sink timings")
@@ -214,17 +215,24 @@ def main():
         t_wall = time.perf_counter()
         r = {"call": timed_calls(lambda: runner(q, k, v, tau, out=out), steps)}
         wall = time.perf_counter() - t_wall
-        # the same calls with L2 and the MALL flushed first
-        ev = events(steps)
-        for i, (a, b) in enumerate(ev):
-            scratch.fill_(float(i))
-            a.record(stream)
-            runner(q, k, v, tau, out=out)
-            b.record(stream)
-        torch.cuda.synchronize()
-        r["call_flushed"] = elapsed(ev)
+        # (with --profile-only the fused kernel runs only as the default call and
+        # the split stages time it: a kernel trace's average is then the figure
+        # the roofline uses)
+        extras = not args.profile_only
+        if extras:
+            # the same calls with L2 and the MALL flushed first
+            ev = events(steps)
+            for i, (a, b) in enumerate(ev):
+                scratch.fill_(float(i))
+                a.record(stream)
+                runner(q, k, v, tau, out=out)
+                b.record(stream)
+            torch.cuda.synchronize()
+            r["call_flushed"] = elapsed(ev)
         r["pool"], r["prepare"], r["plan"], r["fwd"] = split_calls(runner, q, k, v, out, tau, steps)
         stats = runner.read_stats()
+        if not extras:
+            return r, wall, stats
         n = max(3, steps // 2)
         # the fused kernel with its items in sequence (the identity order)
         runner.plan(q, math.inf)
@@ -249,18 +257,22 @@ def main():
         kv_tokens, _ = kv_unique_tokens(runner, q, k, v, out, tau, wl)
         rl = fwd_roofline(B, H, N, d, wl.Nk, stats, kv_tokens, ms_fwd)
         kept_pct = 100.0 * stats["kept_blocks"] / stats["total_blocks"]
+
+        def med(key):
+            return round(float(np.median(r[key])), 4) if key in r else None
+
         rec = {
             "ms_per_call": round(ms_call, 4),
             "call_ms": pct(r["call"]),
-            "call_ms_l2_mall_flushed": pct(r["call_flushed"]),
+            "call_ms_l2_mall_flushed": pct(r["call_flushed"]) if "call_flushed" in r else None,
             "ms_pool": round(ms_pool, 4),
             "ms_prepare": round(ms_prep, 4),
             "ms_fwd": round(ms_fwd, 4),
             "fwd_ms": pct(r["fwd"]),
             "ms_plan": round(ms_plan, 4),
-            "fwd_ms_items_in_sequence": round(float(np.median(r["fwd_sequence_order"])), 4),
-            "row_correction_ms_per_call": round(float(np.median(r["call_row_correction"])), 4),
-            "bf16_out_ms_per_call": round(float(np.median(r["call_bf16_out"])), 4),
+            "fwd_ms_items_in_sequence": med("fwd_sequence_order"),
+            "row_correction_ms_per_call": med("call_row_correction"),
+            "bf16_out_ms_per_call": med("call_bf16_out"),
             "dense_equiv_tflops": round(dense / (ms_call * 1e-3) / 1e12, 1),
             "kept_block_pct": round(kept_pct, 3),
             "kept_token_pct": round(100.0 * stats["kept_pairs"] / (B * H * N * N), 3),
