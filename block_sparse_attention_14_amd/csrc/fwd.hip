@@ -871,20 +871,14 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
       }
 
       // ---- 2. the union of the two kept lists, walked from the kept bits ----
-      // No list is stored: every wave holds a bit mask of the union's
-      // nonzero kept-bit words (one ballot per 64 words) and walks the union
-      // (in three runs by owner, step 3) with wave-uniform scalar state,
-      // reading a word's bits from LDS when the walk reaches it. Wave 0
+      // No list is stored: the union is walked in three runs by owner (step
+      // 3); at the start of a run every wave holds the run's kept-bit words
+      // in its lanes (one word per lane) and a mask of the words that hold
+      // entries, and walks them with wave-uniform scalar state. Wave 0
       // counts the pair's kept blocks for the stats.
-      uint64_t nz0, nz1 = 0ull;
       int run_len[3];  // union entries kept by both blocks, by the first only, by the second only
       {
         const int nw = (Nk + 31) / 32;
-        auto uword = [&](int w) -> uint32_t {
-          return w < nw ? sm.kbits[gA][w] | (hasB ? sm.kbits[gA + 1][w] : 0u) : 0u;
-        };
-        nz0 = __ballot(uword(lane) != 0u);
-        if constexpr (KW > 64) nz1 = __ballot(uword(64 + lane) != 0u);
         // the lengths of the three runs (every wave; they pick the copy
         // schedule of each run, step 3)
         {
@@ -1159,22 +1153,31 @@ __global__ __launch_bounds__(kThreads, RO ? 4 : 2) void fwd_kernel(FwdParams p) 
         using kSecond = std::integral_constant<int, 2>;
         auto run = [&](auto qmask) __attribute__((always_inline)) {
           constexpr int QM = decltype(qmask)::value;
-          uint64_t m0 = nz0, m1 = nz1;
+          // this run's kept-bit words: lane l holds word l (and word 64 + l in
+          // the second register), so the walk takes a word with one lane read
+          // and visits only the words that hold entries of this run
+          const int nw = (Nk + 31) / 32;
+          auto run_word = [&](int w) -> uint32_t {
+            if (w >= nw) return 0u;
+            const uint32_t a = sm.kbits[gA][w], b = hasB ? sm.kbits[gA + 1][w] : 0u;
+            return QM == 3 ? (a & b) : QM == 1 ? (a & ~b) : (b & ~a);
+          };
+          const uint32_t rw0 = run_word(lane);
+          const uint32_t rw1 = KW > 64 ? run_word(64 + lane) : 0u;
+          uint64_t m0 = __ballot(rw0 != 0u), m1 = KW > 64 ? __ballot(rw1 != 0u) : 0ull;
           uint32_t rem = 0u;
           int wbase = 0;
           auto next = [&]() __attribute__((always_inline)) -> int {
-            while (rem == 0u) {
+            if (rem == 0u) {
               const bool lo = m0 != 0ull;
               const uint64_t m = lo ? m0 : m1;
               if (m == 0ull) return -1;
-              const int w = (lo ? 0 : 64) + (int)__builtin_ctzll(m);
+              const int l = (int)__builtin_ctzll(m);
               const uint64_t m2 = m & (m - 1ull);
               m0 = lo ? m2 : 0ull;
               m1 = lo ? m1 : m2;
-              const uint32_t a = __builtin_amdgcn_readfirstlane(sm.kbits[gA][w]);
-              const uint32_t b = hasB ? __builtin_amdgcn_readfirstlane(sm.kbits[gA + 1][w]) : 0u;
-              rem = QM == 3 ? (a & b) : QM == 1 ? (a & ~b) : (b & ~a);
-              wbase = 32 * w;
+              rem = (uint32_t)__builtin_amdgcn_readlane((int)(lo ? rw0 : rw1), l);
+              wbase = 32 * ((lo ? 0 : 64) + l);
             }
             const int bit = __builtin_ctz(rem);
             rem &= rem - 1u;
